@@ -1,0 +1,184 @@
+"""Block-scaled FP8 grouped quantize / wgrad / fprop for MoE expert layers on MI355X (gfx950).
+
+Thin ctypes binding of ``libbsfp8.so``.  It only marshals arguments: tensor data pointers,
+sizes and torch's current HIP stream go to the C ABI declared in ``include/bsfp8.h``; every
+step of the computation runs in the library's kernels.  PyTorch supplies device memory and the
+stream.  If the library has not been built, importing works but every call raises.
+
+Functions keep the C names without the ``bsfp8_`` prefix:
+  grouped_quantize, grouped_gemm_wgrad, grouped_gemm_fprop, the size queries, strerror.
+``alloc_quantized`` and ``alloc_*`` helpers size output tensors with the library's own size
+queries.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsfp8.so")
+
+RECIPE_MX = 1  # BSFP8_RECIPE_MX_1X32_E8M0
+RECIPE_PC = 2  # BSFP8_RECIPE_PER_CHANNEL_128_F32
+ROWWISE = 1
+COLWISE = 2
+OUT_F32 = 0
+OUT_BF16 = 1
+STATUS_NEGATIVE_SPLIT = 1
+STATUS_EXCEEDS_CAPACITY = 2
+MAX_GROUPS = 1024
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+_lib = None
+
+
+class BSFP8Error(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded libbsfp8.so; raises when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise BSFP8Error(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                             "(or python -m block_scaled_fp8_grouped_amd._build)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.bsfp8_colwise_rows_bound.restype = _i64
+        L.bsfp8_colwise_rows_bound.argtypes = [_i64, _i32]
+        L.bsfp8_colwise_data_bytes.restype = _sz
+        L.bsfp8_colwise_data_bytes.argtypes = [_i64, _i64, _i32]
+        L.bsfp8_colwise_scale_bytes.restype = _sz
+        L.bsfp8_colwise_scale_bytes.argtypes = [_i64, _i64, _i32, ctypes.c_int]
+        L.bsfp8_rowwise_data_bytes.restype = _sz
+        L.bsfp8_rowwise_data_bytes.argtypes = [_i64, _i64]
+        L.bsfp8_rowwise_scale_bytes.restype = _sz
+        L.bsfp8_rowwise_scale_bytes.argtypes = [_i64, _i64]
+        L.bsfp8_grouped_quantize.restype = ctypes.c_int
+        L.bsfp8_grouped_quantize.argtypes = [_vp, _i64, _i64, _vp, _i32, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.bsfp8_grouped_gemm_wgrad.restype = ctypes.c_int
+        L.bsfp8_grouped_gemm_wgrad.argtypes = [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i64, ctypes.c_int,
+                                               _vp, ctypes.c_int, _vp, _vp]
+        L.bsfp8_grouped_gemm_fprop.restype = ctypes.c_int
+        L.bsfp8_grouped_gemm_fprop.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i32, _vp,
+                                               ctypes.c_int, _vp, _vp]
+        L.bsfp8_strerror.restype = ctypes.c_char_p
+        L.bsfp8_strerror.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def strerror(code):
+    return lib().bsfp8_strerror(int(code)).decode()
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise BSFP8Error(f"{what}: {strerror(rc)} ({rc})")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        return int(t)  # a raw address
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# ------------------------------------------------------------------------------------------
+# size queries
+# ------------------------------------------------------------------------------------------
+
+def colwise_rows_bound(capacity_rows, num_groups):
+    return int(lib().bsfp8_colwise_rows_bound(capacity_rows, num_groups))
+
+
+def colwise_data_bytes(capacity_rows, cols, num_groups):
+    return int(lib().bsfp8_colwise_data_bytes(capacity_rows, cols, num_groups))
+
+
+def colwise_scale_bytes(capacity_rows, cols, num_groups, recipe):
+    return int(lib().bsfp8_colwise_scale_bytes(capacity_rows, cols, num_groups, recipe))
+
+
+def rowwise_data_bytes(rows, cols):
+    return int(lib().bsfp8_rowwise_data_bytes(rows, cols))
+
+
+def rowwise_scale_bytes(rows, cols):
+    return int(lib().bsfp8_rowwise_scale_bytes(rows, cols))
+
+
+def alloc_quantized(capacity_rows, cols, num_groups, recipe, which, device="cuda"):
+    """Output tensors for grouped_quantize, sized by the library's size queries.
+
+    Returns a dict with row_q uint8 [R, C], row_s uint8 [C/32, R], col_q uint8 [bytes],
+    col_s uint8 [bytes] (MX) or float32 [bytes/4] (per-channel), for the requested layouts."""
+    out = {}
+    if which & ROWWISE:
+        out["row_q"] = torch.empty((capacity_rows, cols), dtype=torch.uint8, device=device)
+        out["row_s"] = torch.empty((cols // 32, capacity_rows), dtype=torch.uint8, device=device)
+    if which & COLWISE:
+        out["col_q"] = torch.empty(colwise_data_bytes(capacity_rows, cols, num_groups), dtype=torch.uint8,
+                                   device=device)
+        nb = colwise_scale_bytes(capacity_rows, cols, num_groups, recipe)
+        if recipe == RECIPE_MX:
+            out["col_s"] = torch.empty(nb, dtype=torch.uint8, device=device)
+        else:
+            out["col_s"] = torch.empty(nb // 4, dtype=torch.float32, device=device)
+    return out
+
+
+# ------------------------------------------------------------------------------------------
+# entry points
+# ------------------------------------------------------------------------------------------
+
+def grouped_quantize(x, split_sizes, recipe, which, out, zero_amax_scale=1e-30, status=None, stream=None,
+                     capacity_rows=None, cols=None):
+    """bsfp8_grouped_quantize on a bf16 [R, C] tensor; ``out`` holds the output tensors
+    (see alloc_quantized).  split_sizes: int32 device tensor, or None (rowwise, all rows live)."""
+    if isinstance(x, torch.Tensor):
+        R, C = x.shape if capacity_rows is None else (capacity_rows, cols)
+    else:
+        R, C = capacity_rows, cols
+    E = 0 if split_sizes is None else int(split_sizes.numel())
+    rc = lib().bsfp8_grouped_quantize(_ptr(x), R, C, _ptr(split_sizes), E, recipe, which, float(zero_amax_scale),
+                                      _ptr(out.get("row_q")), _ptr(out.get("row_s")), _ptr(out.get("col_q")),
+                                      _ptr(out.get("col_s")), _ptr(status), _stream(stream))
+    _check(rc, "grouped_quantize")
+    return out
+
+
+def grouped_gemm_wgrad(dy_q, n, x_q, h, split_sizes, capacity_rows, recipe, out, accumulate=False, status=None,
+                       stream=None):
+    """bsfp8_grouped_gemm_wgrad: dy_q / x_q are the colwise dicts of grouped_quantize; out is
+    fp32 [E, n, h] (overwritten, or accumulated into with ``accumulate``)."""
+    E = int(split_sizes.numel())
+    rc = lib().bsfp8_grouped_gemm_wgrad(_ptr(dy_q["col_q"]), _ptr(dy_q["col_s"]), n, _ptr(x_q["col_q"]),
+                                        _ptr(x_q["col_s"]), h, _ptr(split_sizes), E, capacity_rows, recipe,
+                                        _ptr(out), 1 if accumulate else 0, _ptr(status), _stream(stream))
+    _check(rc, "grouped_gemm_wgrad")
+    return out
+
+
+def grouped_gemm_fprop(x_q, k, w_q, n, split_sizes, capacity_rows, out, out_dtype=OUT_F32, status=None,
+                       stream=None):
+    """bsfp8_grouped_gemm_fprop: x_q is the rowwise dict of x [R, k], w_q the rowwise dict of the
+    weight [E*n, k]; out is [R, n] fp32 or bf16 (rows past sum(split_sizes) untouched)."""
+    E = int(split_sizes.numel())
+    rc = lib().bsfp8_grouped_gemm_fprop(_ptr(x_q["row_q"]), _ptr(x_q["row_s"]), capacity_rows, k,
+                                        _ptr(w_q["row_q"]), _ptr(w_q["row_s"]), n, _ptr(split_sizes), E,
+                                        _ptr(out), out_dtype, _ptr(status), _stream(stream))
+    _check(rc, "grouped_gemm_fprop")
+    return out

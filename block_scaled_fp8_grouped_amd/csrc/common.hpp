@@ -1,0 +1,217 @@
+// Shared device helpers of the block-scaled FP8 grouped kernels (gfx950 / CDNA4).
+//
+//  * group_scan: every workgroup reads the device-resident split sizes and computes, in LDS,
+//    the prefix sums that place its tile (group offsets off_e, padded offsets P_e and tile
+//    prefixes), plus the validation of the sizes.  No host copy of the sizes is ever needed
+//    (TE PR #3224 review: split sizes stay on the device), and nothing depends on the buffer's
+//    capacity beyond the bound check, so one group, empty groups and 128-token groups take
+//    the same code (TE #3484, bug description).
+//  * e4m3 / E8M0 helpers: the hardware fp8 conversion rounds to nearest even on the OCP
+//    E4M3FN grid; the E8M0 exponent is read off the fp32 bit pattern of the block amax.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bsfp8.h"
+
+namespace bsfp8 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxGroups = BSFP8_MAX_GROUPS;
+
+// ---------------------------------------------------------------------------------------------
+// Scale rules
+// ---------------------------------------------------------------------------------------------
+
+// MXFP8 block exponent: smallest e with amax <= 448 * 2^e, clamped to [-127, 127].
+// amax = 1.m * 2^u (u unbiased); 448 = 1.75 * 2^8, so e = u - 8 when 1.m <= 1.75, else u - 7.
+// fp32 subnormals (and 0) are below 448 * 2^-127 and give -127.  For any finite amax the
+// result is at most 120, so 2^-e is always a normal fp32.
+__device__ __forceinline__ int e8m0_exponent(float amax) {
+  const uint32_t bits = __float_as_uint(amax);
+  const int ef = (int)((bits >> 23) & 0xffu);
+  if (ef == 0) return -127;
+  const int u = ef - 127;
+  int e = u - 8 + ((bits & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// 2^-e as an fp32 (exact; e in [-127, 120]).
+__device__ __forceinline__ float exp2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
+// Two fp32 -> two e4m3 codes in the low 16 bits (round to nearest even, sign kept).
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+// Four fp32 -> four e4m3 codes packed little-endian in a dword.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// bf16 halves of a dword -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite sums).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Group scan
+// ---------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ int64_t wave_inclusive_scan(int64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// Where a workgroup's tile sits: its group and the group's row extents.
+struct GroupInfo {
+  int64_t k;    // live rows of the group
+  int64_t off;  // first row of the group in the token buffer
+  int64_t kp;   // rows rounded up to 128
+  int64_t p;    // sum of kp over earlier groups (colwise packed offset, in rows)
+  int64_t tile; // first linear tile index of the group (tile_rows > 0 only)
+  int32_t e;    // group index, or -1 when the workgroup has no tile
+};
+
+template <int NT>
+struct GroupScanSmem {
+  int64_t wave_tot[NT / 64][3];
+  int32_t tile_prefix[kMaxGroups + 1];
+  int64_t info[4];
+  uint32_t flags;
+};
+
+// Scans split_sizes[0..E) across the workgroup.  tile_rows > 0 makes each group own
+// ceil(k_e / tile_rows) tiles, and the workgroup's linear tile `tile_index` is mapped to its
+// group (binary search over the tile prefix).  tile_rows == 0 selects group `group_index`.
+// Returns the validation bits (BSFP8_STATUS_*); GroupInfo.e is -1 when the tile is beyond the
+// last group's tiles or when the sizes are invalid.
+template <int NT>
+__device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_t capacity,
+                               int tile_rows, int64_t tile_index, int group_index,
+                               GroupScanSmem<NT>& sm, GroupInfo& gi) {
+  constexpr int kItems = (kMaxGroups + NT - 1) / NT;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  int64_t k[kItems], kp[kItems], tl[kItems];
+  int64_t sk = 0, skp = 0, stl = 0;
+  uint32_t bad = 0;
+#pragma unroll
+  for (int i = 0; i < kItems; ++i) {
+    const int e = tid * kItems + i;
+    const int64_t v = e < E ? (int64_t)splits[e] : 0;
+    if (v < 0) bad |= BSFP8_STATUS_NEGATIVE_SPLIT;
+    k[i] = v < 0 ? 0 : v;
+    kp[i] = ((k[i] + 127) >> 7) << 7;
+    tl[i] = tile_rows > 0 ? (k[i] + tile_rows - 1) / tile_rows : 0;
+    sk += k[i];
+    skp += kp[i];
+    stl += tl[i];
+  }
+  // exclusive prefix of the per-thread sums across the workgroup
+  const int64_t ik = wave_inclusive_scan(sk), ikp = wave_inclusive_scan(skp), itl = wave_inclusive_scan(stl);
+  if (tid == 0) sm.flags = 0;
+  if (lane == 63) {
+    sm.wave_tot[wave][0] = ik;
+    sm.wave_tot[wave][1] = ikp;
+    sm.wave_tot[wave][2] = itl;
+  }
+  __syncthreads();
+  if (bad) atomicOr(&sm.flags, bad);
+  int64_t bk = ik - sk, bkp = ikp - skp, btl = itl - stl, tot = 0, tot_tl = 0;
+  for (int w = 0; w < NT / 64; ++w) {
+    if (w < wave) {
+      bk += sm.wave_tot[w][0];
+      bkp += sm.wave_tot[w][1];
+      btl += sm.wave_tot[w][2];
+    }
+    tot += sm.wave_tot[w][0];
+    tot_tl += sm.wave_tot[w][2];
+  }
+  if (tid == 0 && tile_rows > 0) sm.tile_prefix[E] = (int32_t)tot_tl;
+  // per-entry exclusive prefixes; publish the tile prefix and the selected group's extents
+  int64_t ok = bk, okp = bkp, otl = btl;
+#pragma unroll
+  for (int i = 0; i < kItems; ++i) {
+    const int e = tid * kItems + i;
+    if (e < E && tile_rows > 0) sm.tile_prefix[e] = (int32_t)otl;
+    if (tile_rows == 0 && e == group_index && e < E) {
+      sm.info[0] = k[i];
+      sm.info[1] = ok;
+      sm.info[2] = kp[i];
+      sm.info[3] = okp;
+    }
+    ok += k[i];
+    okp += kp[i];
+    otl += tl[i];
+  }
+  __syncthreads();
+  uint32_t flags = sm.flags;
+  if (tot > capacity) flags |= BSFP8_STATUS_EXCEEDS_CAPACITY;
+  gi.e = -1;
+  if (flags) return flags;
+  if (tile_rows > 0) {
+    const int64_t total = sm.tile_prefix[E];
+    if (tile_index >= total) return 0;
+    int lo = 0, hi = E;  // tile_prefix[lo] <= tile_index < tile_prefix[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sm.tile_prefix[mid] <= tile_index) lo = mid; else hi = mid;
+    }
+    // this workgroup's group is lo; its owner thread publishes the extents
+    __syncthreads();
+    {
+      int64_t ok2 = bk, okp2 = bkp;
+#pragma unroll
+      for (int i = 0; i < kItems; ++i) {
+        const int e = tid * kItems + i;
+        if (e == lo) {
+          sm.info[0] = k[i];
+          sm.info[1] = ok2;
+          sm.info[2] = kp[i];
+          sm.info[3] = okp2;
+        }
+        ok2 += k[i];
+        okp2 += kp[i];
+      }
+    }
+    __syncthreads();
+    gi.e = lo;
+    gi.tile = sm.tile_prefix[lo];
+  } else {
+    gi.e = group_index;
+    gi.tile = 0;
+  }
+  gi.k = sm.info[0];
+  gi.off = sm.info[1];
+  gi.kp = sm.info[2];
+  gi.p = sm.info[3];
+  return 0;
+}
+
+// OR the validation bits into the caller's status word (one thread of workgroup 0 only).
+__device__ __forceinline__ void report_status(uint32_t* status, uint32_t flags) {
+  if (status != nullptr && flags != 0 && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+    atomicOr(status, flags);
+}
+
+}  // namespace bsfp8

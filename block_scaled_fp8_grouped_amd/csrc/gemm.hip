@@ -1,0 +1,483 @@
+// Grouped block-scaled FP8 GEMMs on gfx950.
+//
+//  wgrad (k-grouped; DeepGEMM #365, k_grouped_fp8_gemm_nt_contiguous; TE #3484, the weight
+//         gradient contracts over the token axis):  dW[e] (=|+=) dy_e^T x_e over the group's
+//         k_e live tokens.  Both operands are the colwise (K-major per group) buffers; K is the
+//         group's padded extent Kp_e, a multiple of 128 whose pad lanes hold zeros.
+//  fprop (m-grouped; TE PR #3224, grouped GEMM over a single grouped weight; the token axis is
+//         a free dimension): out[off_e + t] = x[off_e + t] W_e^T for t < k_e.
+//
+// Arithmetic.  The operands stay e4m3 (one byte) in HBM and LDS.  In registers every e4m3 value
+// is widened to bf16 with its block scale folded in (exact: e4m3 has 4 significant bits and a
+// power-of-two scale only moves the exponent), and the products are accumulated by the bf16
+// MFMA (v_mfma_f32_32x32x16_bf16) in fp32.  The scaled FP8 MFMA is not used: measured on
+// gfx950 it sums each group of 8 products in a ~14-bit window under the group's largest product
+// (smaller products are truncated), which leaves about 1.5e-5 relative error on Gaussian data
+// and cannot meet a 1e-5 bound; the bf16 MFMA on the same values is within fp32 rounding.
+// Per-channel recipe (fp32 scales per 128 rows): unit-scale widening, one partial sum p per
+// 128-row K step, folded as acc = fma(p, sa_i * sb_j, acc) in K order.
+//
+// Tiling.  Workgroup tile BM x BN (256 x 256 for MX, 128 x 128 for the per-channel recipe),
+// K step 128, 4 waves each owning a WM x WN block of 32 x 32 fragments.  Per K step the A and
+// B tiles (rows of 128 bytes) and their scales are moved straight from HBM into LDS by
+// global_load_lds (16 bytes per lane, no staging registers), double-buffered; the 16-byte
+// chunks of each row are XOR-swizzled so that the fragment reads of consecutive rows spread
+// over all banks.  A lane of a 32 x 32 fragment owns row (lane % 32) and reads, for the K half
+// s of the step, chunks 4s + h and 4s + 2 + h (h = lane / 32): the first lies in 32-block 2s,
+// the second in 2s + 1, so each half-fragment has a single block scale.  The next step's loads
+// are issued only after this step's fragments have been read into registers, so they overlap
+// the step's MFMAs.
+//
+// Determinism: one workgroup per output tile, fixed instruction order, no atomics, no split-K.
+// Rows past a group's live rows are clamped to its last live row on load (never read beyond
+// it) and their results are not stored.
+#include "common.hpp"
+#include "tile_addr.hpp"
+
+namespace bsfp8 {
+
+enum { kModeWgrad = 0, kModeFprop = 1 };
+
+struct GemmArgs {
+  const uint8_t* a_q;  // wgrad: dy colwise   fprop: x rowwise
+  const void* a_s;
+  const uint8_t* b_q;  // wgrad: x colwise    fprop: W rowwise
+  const void* b_s;
+  int64_t M;           // wgrad: n (dy channels)   fprop: unused (group rows)
+  int64_t N;           // wgrad: h (x channels)    fprop: n (weight rows per expert)
+  int64_t K;           // fprop: reduction length
+  int64_t R;           // capacity rows
+  const int32_t* splits;
+  int E;
+  int tiles_m, tiles_n;  // wgrad: per-group tile grid; fprop: tiles_n only
+  void* out;
+  uint32_t* status;
+};
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// fp32 value 2^(byte - 127) of an E8M0 scale byte (byte 0 is the fp32 subnormal 2^-127).
+__device__ __forceinline__ float e8m0_value(uint32_t byte) {
+  return byte ? __uint_as_float(byte << 23) : __uint_as_float(0x00400000u);
+}
+
+// Eight e4m3 codes (two dwords) -> eight bf16 values times `scale`.
+__device__ __forceinline__ v8bf widen8(int d0, int d1, float scale) {
+  const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d0, scale, false);
+  const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d0, scale, true);
+  const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d1, scale, false);
+  const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d1, scale, true);
+  return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+template <int MODE, bool PC, int BM, int BN, int WM, int WN>
+struct GemmShape {
+  static constexpr int BK = 128;
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int NW = WAVES_M * WAVES_N, NT = NW * 64;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  // LDS stage: A rows, B rows, then scales (MX: [4 blocks][rows] bytes; PC: one fp32 per row)
+  static constexpr int A_OFF = 0, B_OFF = BM * BK, SA_OFF = (BM + BN) * BK, SB_OFF = SA_OFF + BM * 4;
+  static constexpr int STAGE = SB_OFF + BN * 4;
+  static constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;  // 1 KB DMA instructions per wave
+  static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
+  static_assert(A_INS * 8 * NW == BM && B_INS * 8 * NW == BN, "DMA loader shape");
+  static_assert(2 * STAGE + (int)sizeof(GroupScanSmem<NT>) <= 160 * 1024, "LDS budget");
+};
+
+template <int MODE, bool PC, int BM, int BN, int WM, int WN, bool ACCUM, int OUT>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kernel(GemmArgs args) {
+  using S = GemmShape<MODE, PC, BM, BN, WM, WN>;
+  constexpr int NT = S::NT, NW = S::NW, BK = S::BK, FM = S::FM, FN = S::FN;
+  __shared__ GroupScanSmem<NT> gsm;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int wm = wave % S::WAVES_M, wn = wave / S::WAVES_M;
+
+  // ---------------- tile placement (device scheduler) ----------------
+  GroupInfo gi;
+  int e, tm, tn;
+  if constexpr (MODE == kModeWgrad) {
+    const int per = args.tiles_m * args.tiles_n;
+    e = (int)(blockIdx.x / per);
+    const int rem = (int)(blockIdx.x % per);
+    tm = rem / args.tiles_n;
+    tn = rem % args.tiles_n;
+    const uint32_t flags = group_scan<NT>(args.splits, args.E, args.R, 0, 0, e, gsm, gi);
+    report_status(args.status, flags);
+    if (gi.e < 0) return;
+  } else {
+    const uint32_t flags = group_scan<NT>(args.splits, args.E, args.R, BM, blockIdx.x, 0, gsm, gi);
+    report_status(args.status, flags);
+    if (gi.e < 0) return;
+    e = gi.e;
+    tm = (int)(blockIdx.x - gi.tile);
+    tn = blockIdx.y;
+  }
+
+  // ---------------- operand descriptors ----------------
+  const uint8_t *a_data, *b_data, *a_sc, *b_sc;
+  int64_t lda, ldb, a_sld, b_sld, a_valid, b_valid, kext;
+  const int64_t a_row0 = (int64_t)tm * BM, b_row0 = (int64_t)tn * BN;
+  if constexpr (MODE == kModeWgrad) {
+    if (gi.k == 0) {
+      if constexpr (!ACCUM) {  // an empty group's gradient is zero
+        float* o = (float*)args.out + ((int64_t)e * args.M + a_row0) * args.N + b_row0;
+        for (int idx = tid; idx < BM * BN / 4; idx += NT) {
+          const int r = idx / (BN / 4), c = (idx % (BN / 4)) * 4;
+          if (a_row0 + r < args.M && b_row0 + c < args.N) *(float4*)(o + (int64_t)r * args.N + c) = float4{0, 0, 0, 0};
+        }
+      }
+      return;
+    }
+    lda = ldb = gi.kp;
+    kext = gi.kp;
+    a_data = args.a_q + args.M * gi.p;
+    b_data = args.b_q + args.N * gi.p;
+    a_valid = args.M;
+    b_valid = args.N;
+    if constexpr (PC) {
+      a_sc = (const uint8_t*)((const float*)args.a_s + args.M * gi.p / 128);
+      b_sc = (const uint8_t*)((const float*)args.b_s + args.N * gi.p / 128);
+    } else {
+      a_sc = (const uint8_t*)args.a_s + args.M * gi.p / 32;
+      b_sc = (const uint8_t*)args.b_s + args.N * gi.p / 32;
+    }
+    a_sld = args.M;
+    b_sld = args.N;
+  } else {
+    lda = ldb = args.K;
+    kext = args.K;
+    a_data = args.a_q + gi.off * args.K;
+    b_data = args.b_q + (int64_t)e * args.N * args.K;
+    a_sc = (const uint8_t*)args.a_s + gi.off;
+    b_sc = (const uint8_t*)args.b_s + (int64_t)e * args.N;
+    a_sld = args.R;
+    b_sld = (int64_t)args.E * args.N;
+    a_valid = gi.k;
+    b_valid = args.N;
+  }
+  const int nk = (int)((kext + BK - 1) / BK);
+
+  // ---------------- loads of one K step, straight into LDS ----------------
+  // One DMA instruction moves 64 lanes x 16 bytes = 8 rows x 128 bytes; lane l fills LDS slot
+  // l of the region, i.e. row 8g + l/8, swizzled chunk l%8, which holds K chunk (l%8) ^ swz(row).
+  // Rows past the valid ones are clamped to the last valid row.  K chunks at or past kext
+  // (fprop tail only) are fetched from the row start and zeroed in LDS after the wait, so no
+  // byte past a row is ever read.  The row part of a lane's offset is 32-bit from a uniform
+  // tile base (the host bounds 256 * ld below 2^32).
+  const int a_last = (int)(a_valid - 1 - a_row0), b_last = (int)(b_valid - 1 - b_row0);  // >= 0
+  const uint8_t* a_tile = a_data + a_row0 * lda;
+  const uint8_t* b_tile = b_data + b_row0 * ldb;
+  auto dma16 = [&](const void* g, uint8_t* l) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+  };
+  auto dma4 = [&](const void* g, uint8_t* l) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+  };
+  uint32_t fa_sc = 0;  // fprop: the 4 A-scale bytes this thread stages through registers
+  auto issue = [&](int kk, uint8_t* __restrict__ base) {
+    const int64_t k0 = (int64_t)kk * BK;
+    // wgrad K extents are multiples of 128: no tail, so the K part is never redirected
+    const int64_t ktail = MODE == kModeFprop ? kext : INT64_MAX;
+#pragma unroll
+    for (int u = 0; u < S::A_INS; ++u) {
+      const int g = wave * S::A_INS + u;
+      dma16(a_tile + tile_dma_offset(g, lane, a_last, lda, k0, ktail), base + S::A_OFF + g * 1024);
+    }
+#pragma unroll
+    for (int u = 0; u < S::B_INS; ++u) {
+      const int g = wave * S::B_INS + u;
+      dma16(b_tile + tile_dma_offset(g, lane, b_last, ldb, k0, ktail), base + S::B_OFF + g * 1024);
+    }
+    if constexpr (PC) {
+      // one fp32 per row: BM + BN dwords, 64 per instruction
+      constexpr int S_INS = (BM + BN) / 64;
+      static_assert(S_INS % NW == 0, "PC scale loader shape");
+#pragma unroll
+      for (int u = 0; u < S_INS / NW; ++u) {
+        const int v = wave * (S_INS / NW) + u;
+        const int row = v * 64 + lane;
+        if (v * 64 < BM) {
+          dma4((const float*)a_sc + (int64_t)kk * a_sld + a_row0 + min(row, a_last), base + S::SA_OFF + v * 256);
+        } else {
+          dma4((const float*)b_sc + (int64_t)kk * b_sld + b_row0 + min(row - BM, b_last), base + S::SA_OFF + v * 256);
+        }
+      }
+    } else {
+      // E8M0 block rows [blk][row]: 4 rows of 4 bytes per lane, 256 bytes per instruction
+      constexpr int SA_INS = 4 * BM / 256, SB_INS = 4 * BN / 256;
+      static_assert((SA_INS + SB_INS) % NW == 0, "MX scale loader shape");
+#pragma unroll
+      for (int u = 0; u < (SA_INS + SB_INS) / NW; ++u) {
+        const int v = wave * ((SA_INS + SB_INS) / NW) + u;
+        const bool is_a = v < SA_INS;
+        const int vv = is_a ? v : v - SA_INS;
+        const int per = (is_a ? BM : BN) / 256;
+        const int blk = vv / per, part = vv % per;
+        const int64_t kb = (int64_t)kk * 4 + blk;
+        uint8_t* dst = base + (is_a ? S::SA_OFF + blk * BM : S::SB_OFF + blk * BN) + part * 256;
+        if (MODE == kModeFprop && is_a) {
+          // rows of a group start anywhere: four single-byte loads per thread instead (below)
+        } else if (MODE == kModeFprop && kb * 32 >= kext) {
+          *(uint32_t*)(dst + 4 * lane) = 0x7f7f7f7fu;  // past K: unit scales over zero data
+        } else {
+          // valid rows are a multiple of 32 here, so a group of 4 is all valid or all past
+          const int r4 = scale_dma_row(part, lane, is_a ? a_last : b_last);
+          dma4((is_a ? a_sc + a_row0 : b_sc + b_row0) + kb * (is_a ? a_sld : b_sld) + r4, dst);
+        }
+      }
+      if constexpr (MODE == kModeFprop) {
+        // A scales: thread t -> block t / 64 of this K step, rows 4 * (t % 64) .. + 4
+        static_assert(BM == 256 && NT == 256, "fprop A-scale staging shape");
+        const int blk = tid >> 6;
+        const int64_t kb = (int64_t)kk * 4 + blk;
+        uint32_t w = 0x7f7f7f7fu;
+        if (kb * 32 < kext) {
+          w = 0;
+          const uint8_t* src = a_sc + kb * a_sld + a_row0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w |= (uint32_t)src[min(4 * lane + i, a_last)] << (8 * i);
+        }
+        fa_sc = w;
+      }
+    }
+  };
+  // after the DMA has landed: zero K chunks past kext (fprop tail) and place register-staged bytes
+  auto settle = [&](int kk, uint8_t* base) {
+    if constexpr (MODE == kModeFprop) {
+      if ((int64_t)(kk + 1) * BK > kext) {
+#pragma unroll
+        for (int u = 0; u < S::A_INS; ++u) {
+          const int g = wave * S::A_INS + u;
+          if (tile_dma_is_tail(g, lane, (int64_t)kk * BK, kext)) *(v4i*)(base + S::A_OFF + g * 1024 + 16 * lane) = v4i{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < S::B_INS; ++u) {
+          const int g = wave * S::B_INS + u;
+          if (tile_dma_is_tail(g, lane, (int64_t)kk * BK, kext)) *(v4i*)(base + S::B_OFF + g * 1024 + 16 * lane) = v4i{0, 0, 0, 0};
+        }
+      }
+      *(uint32_t*)(base + S::SA_OFF + (tid >> 6) * BM + 4 * lane) = fa_sc;
+    }
+  };
+  auto wait_dma = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  v16f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // One K step.  `cur` (read) and `nxt` (DMA target) are distinct LDS stages; passing them as
+  // restrict pointers lets the compiler see that the fragment reads of `cur` need not wait for
+  // the DMA into `nxt`, so the loads overlap this step's MFMAs.
+  auto step = [&](int kk, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+    v16f part[FM][FN];
+    if constexpr (PC) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      // this K half's fp8 fragments and block scales -> registers
+      v8i af[FM], bf[FN];
+      float as[FM][2], bs[FN][2];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wm * WM + i * 32 + l32;
+        const v4i lo = *(const v4i*)(cur + S::A_OFF + row * BK + (((4 * s + h) ^ swz(row)) << 4));
+        const v4i hi = *(const v4i*)(cur + S::A_OFF + row * BK + (((4 * s + 2 + h) ^ swz(row)) << 4));
+        af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (!PC) {
+          as[i][0] = e8m0_value(cur[S::SA_OFF + (2 * s) * BM + row]);
+          as[i][1] = e8m0_value(cur[S::SA_OFF + (2 * s + 1) * BM + row]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int row = wn * WN + j * 32 + l32;
+        const v4i lo = *(const v4i*)(cur + S::B_OFF + row * BK + (((4 * s + h) ^ swz(row)) << 4));
+        const v4i hi = *(const v4i*)(cur + S::B_OFF + row * BK + (((4 * s + 2 + h) ^ swz(row)) << 4));
+        bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (!PC) {
+          bs[j][0] = e8m0_value(cur[S::SB_OFF + (2 * s) * BN + row]);
+          bs[j][1] = e8m0_value(cur[S::SB_OFF + (2 * s + 1) * BN + row]);
+        }
+      }
+      if (s == 0 && kk + 1 < nk) issue(kk + 1, nxt);
+      // widen and multiply: 4 bf16 MFMAs (K = 16 each) per fragment pair
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v8bf aw[FM], bw[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) aw[i] = widen8(af[i][2 * t], af[i][2 * t + 1], PC ? 1.0f : as[i][t >> 1]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bw[j] = widen8(bf[j][2 * t], bf[j][2 * t + 1], PC ? 1.0f : bs[j][t >> 1]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            if constexpr (PC) part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[i], bw[j], part[i][j], 0, 0, 0);
+            else acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[i], bw[j], acc[i][j], 0, 0, 0);
+          }
+      }
+    }
+    if constexpr (PC) {
+      // fold this 128-row block: acc = fma(p, sa_i * sb_j, acc)
+      const float* fsa = (const float*)(cur + S::SA_OFF);
+      const float* fsb = fsa + BM;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const float bsc = fsb[wn * WN + j * 32 + l32];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = wm * WM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            acc[i][j][r] = __builtin_fmaf(part[i][j][r], fsa[row] * bsc, acc[i][j][r]);
+          }
+        }
+    }
+  };
+
+  issue(0, smem);
+  wait_dma();
+  settle(0, smem);
+  __syncthreads();
+  for (int kk = 0; kk < nk; ++kk) {
+    uint8_t* cur = smem + (kk & 1) * S::STAGE;
+    uint8_t* nxt = smem + ((kk & 1) ^ 1) * S::STAGE;
+    step(kk, cur, nxt);
+    if (kk + 1 < nk) {
+      wait_dma();
+      settle(kk + 1, nxt);
+    }
+    __syncthreads();
+  }
+
+  // ---------------- epilogue ----------------
+  // fragment element r of lane (h, l32): row 8 (r / 4) + 4 h + r % 4, column l32
+  if constexpr (MODE == kModeWgrad) {
+    float* o = (float*)args.out + ((int64_t)e * args.M + a_row0) * args.N + b_row0;
+    const bool full = a_row0 + BM <= args.M && b_row0 + BN <= args.N;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = wn * WN + j * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * WM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (full || (a_row0 + row < args.M && b_row0 + col < args.N)) {
+            float* p = o + (int64_t)row * args.N + col;
+            if constexpr (ACCUM) *p = *p + acc[i][j][r];
+            else *p = acc[i][j][r];
+          }
+        }
+      }
+  } else {
+    const int64_t rows_left = gi.k - a_row0;
+    const bool full = rows_left >= BM && b_row0 + BN <= args.N;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = wn * WN + j * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * WM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (full || (row < rows_left && b_row0 + col < args.N)) {
+            const int64_t idx = (gi.off + a_row0 + row) * args.N + b_row0 + col;
+            if constexpr (OUT == BSFP8_OUT_F32) ((float*)args.out)[idx] = acc[i][j][r];
+            else ((uint16_t*)args.out)[idx] = f32_to_bf16_rne(acc[i][j][r]);
+          }
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Launchers
+// ------------------------------------------------------------------------------------------
+
+template <int MODE, bool PC, int BM, int BN, int WM, int WN, bool ACCUM, int OUT>
+static int launch(const GemmArgs& a, dim3 grid, hipStream_t stream) {
+  using S = GemmShape<MODE, PC, BM, BN, WM, WN>;
+  hipLaunchKernelGGL((grouped_gemm_kernel<MODE, PC, BM, BN, WM, WN, ACCUM, OUT>), grid, dim3(S::NT), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? BSFP8_OK : BSFP8_ERR_LAUNCH;
+}
+
+int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, const uint8_t* x_q, const void* x_s,
+                              int64_t h, const int32_t* splits, int E, int64_t R, int recipe, float* out,
+                              int accumulate, uint32_t* status, hipStream_t stream) {
+  GemmArgs a{};
+  a.a_q = dy_q;
+  a.a_s = dy_s;
+  a.b_q = x_q;
+  a.b_s = x_s;
+  a.M = n;
+  a.N = h;
+  a.R = R;
+  a.splits = splits;
+  a.E = E;
+  a.out = out;
+  a.status = status;
+  if (recipe == BSFP8_RECIPE_MX_1X32_E8M0) {
+    constexpr int BM = 256, BN = 256;
+    a.tiles_m = (int)((n + BM - 1) / BM);
+    a.tiles_n = (int)((h + BN - 1) / BN);
+    const int64_t blocks = (int64_t)E * a.tiles_m * a.tiles_n;
+    if (blocks > 0x7fffffff) return BSFP8_ERR_SHAPE;
+    dim3 grid((unsigned)blocks);
+    return accumulate ? launch<kModeWgrad, false, BM, BN, 128, 128, true, 0>(a, grid, stream)
+                      : launch<kModeWgrad, false, BM, BN, 128, 128, false, 0>(a, grid, stream);
+  }
+  constexpr int BM = 128, BN = 128;
+  a.tiles_m = (int)((n + BM - 1) / BM);
+  a.tiles_n = (int)((h + BN - 1) / BN);
+  const int64_t blocks = (int64_t)E * a.tiles_m * a.tiles_n;
+  if (blocks > 0x7fffffff) return BSFP8_ERR_SHAPE;
+  dim3 grid((unsigned)blocks);
+  return accumulate ? launch<kModeWgrad, true, BM, BN, 64, 64, true, 0>(a, grid, stream)
+                    : launch<kModeWgrad, true, BM, BN, 64, 64, false, 0>(a, grid, stream);
+}
+
+int launch_grouped_gemm_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R, int64_t K, const uint8_t* w_q,
+                              const uint8_t* w_s, int64_t N, const int32_t* splits, int E, void* out, int out_dtype,
+                              uint32_t* status, hipStream_t stream) {
+  constexpr int BM = 256, BN = 256;
+  GemmArgs a{};
+  a.a_q = x_q;
+  a.a_s = x_s;
+  a.b_q = w_q;
+  a.b_s = w_s;
+  a.N = N;
+  a.K = K;
+  a.R = R;
+  a.splits = splits;
+  a.E = E;
+  a.out = out;
+  a.status = status;
+  a.tiles_n = (int)((N + BN - 1) / BN);
+  // upper bound of sum ceil(k_e / BM) over valid sizes
+  const int64_t mt = (R + (int64_t)(BM - 1) * E) / BM;
+  if (mt <= 0) return BSFP8_OK;
+  if (mt > 0x7fffffff || a.tiles_n > 65535) return BSFP8_ERR_SHAPE;
+  dim3 grid((unsigned)mt, (unsigned)a.tiles_n);
+  return out_dtype == BSFP8_OUT_F32
+             ? launch<kModeFprop, false, BM, BN, 128, 128, false, BSFP8_OUT_F32>(a, grid, stream)
+             : launch<kModeFprop, false, BM, BN, 128, 128, false, BSFP8_OUT_BF16>(a, grid, stream);
+}
+
+}  // namespace bsfp8

@@ -1,0 +1,197 @@
+// Grouped quantize: bf16 -> e4m3 with MXFP8 1x32 E8M0 scales or per-channel 128-row fp32
+// scales (DeepGEMM #365 reproducer: per-channel cast and K-major pack; TE #3484: MXFP8 block
+// scaling over a padded token buffer; TE PR #3224: columnwise scales strided per group member).
+//
+// One workgroup (4 waves) owns a tile of 128 rows of one group x 128 channels.  The tile is
+// read once from HBM (16-byte loads, 256 contiguous bytes per row) into LDS; then
+//   colwise: wave w takes tokens [32w, 32w + 32) of the tile and lane l the channel pair
+//            (2l, 2l+1): one LDS dword per token, conflict-free, the block amax, the scale and
+//            32 codes per channel, written as 32 contiguous bytes of the channel's K-major run;
+//   rowwise: 4 lanes per 32-channel block of a row, amax by two lane exchanges, 8 codes per
+//            lane; the tile's row scales are staged in LDS and written 128 rows at a time.
+// Rows past the group's live rows are never read: they enter LDS as zeros, which leaves every
+// block amax unchanged and makes the packed pad lanes 0x00.  Tiles are placed by the
+// in-kernel scan of the split sizes (the grid is an upper bound; spare workgroups exit).
+#include "common.hpp"
+
+namespace bsfp8 {
+
+constexpr int kQThreads = 256;
+constexpr int kQRows = 128;
+constexpr int kQCols = 128;
+
+template <int RECIPE, bool ROW, bool COL>
+__global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
+    const uint16_t* __restrict__ in, int64_t R, int64_t C, const int32_t* __restrict__ splits, int E,
+    float zero_amax_scale, uint8_t* __restrict__ row_q, uint8_t* __restrict__ row_s,
+    uint8_t* __restrict__ col_q, void* __restrict__ col_s, uint32_t* status) {
+  __shared__ GroupScanSmem<kQThreads> gsm;
+  __shared__ __attribute__((aligned(16))) uint32_t tile[kQRows][kQCols / 2];  // bf16 pairs
+  __shared__ float pc_amax[4][kQCols];
+  __shared__ uint8_t rs_tile[kQCols / 32][kQRows];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+
+  int64_t row0, P = 0, kp = 0, jblk = 0;
+  int nlive;
+  if (splits != nullptr) {
+    GroupInfo gi;
+    const uint32_t flags = group_scan<kQThreads>(splits, E, R, kQRows, blockIdx.x, 0, gsm, gi);
+    report_status(status, flags);
+    if (gi.e < 0) return;
+    jblk = (int64_t)blockIdx.x - gi.tile;  // 128-row block index inside the group
+    row0 = gi.off + kQRows * jblk;
+    const int64_t left = gi.k - kQRows * jblk;
+    nlive = (int)(left < kQRows ? left : kQRows);
+    P = gi.p;
+    kp = gi.kp;
+  } else {
+    row0 = (int64_t)blockIdx.x * kQRows;
+    if (row0 >= R) return;
+    const int64_t left = R - row0;
+    nlive = (int)(left < kQRows ? left : kQRows);
+  }
+  const int64_t c0 = (int64_t)blockIdx.y * kQCols;
+  const int ncols = (int)((C - c0) < kQCols ? (C - c0) : kQCols);  // a multiple of 32
+
+  // ---- load the tile: 16 lanes per row, 8 channels (16 bytes) each ----
+#pragma unroll
+  for (int pass = 0; pass < kQRows / 16; ++pass) {
+    const int r = pass * 16 + (tid >> 4);
+    const int ch = tid & 15;
+    v4i v = {0, 0, 0, 0};
+    if (r < nlive && ch * 8 < ncols) v = *(const v4i*)(in + (row0 + r) * C + c0 + ch * 8);
+    *(v4i*)&tile[r][ch * 4] = v;
+  }
+  __syncthreads();
+
+  if constexpr (COL) {
+    // ---- colwise: wave -> 32 tokens, lane -> channel pair ----
+    const int c = 2 * lane;
+    uint32_t w[32];
+    uint32_t m0 = 0, m1 = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      w[i] = tile[wave * 32 + i][lane];
+      m0 = max(m0, w[i] & 0x7fffu);
+      m1 = max(m1, (w[i] >> 16) & 0x7fffu);
+    }
+    float s0, s1;
+    uint32_t sbits = 0;
+    if constexpr (RECIPE == BSFP8_RECIPE_MX_1X32_E8M0) {
+      const int e0 = e8m0_exponent(__uint_as_float(m0 << 16));
+      const int e1 = e8m0_exponent(__uint_as_float(m1 << 16));
+      s0 = exp2_neg(e0);
+      s1 = exp2_neg(e1);
+      sbits = (uint32_t)(e0 + 127) | ((uint32_t)(e1 + 127) << 8);
+    } else {
+      pc_amax[wave][c] = __uint_as_float(m0 << 16);
+      pc_amax[wave][c + 1] = __uint_as_float(m1 << 16);
+      __syncthreads();
+      float a0 = pc_amax[0][c], a1 = pc_amax[0][c + 1];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) {
+        a0 = fmaxf(a0, pc_amax[q][c]);
+        a1 = fmaxf(a1, pc_amax[q][c + 1]);
+      }
+      float sf0 = a0 / 448.0f, sf1 = a1 / 448.0f;
+      if (sf0 == 0.0f) sf0 = zero_amax_scale;
+      if (sf1 == 0.0f) sf1 = zero_amax_scale;
+      if (sf0 < 1e-30f) sf0 = 1e-30f;
+      if (sf1 < 1e-30f) sf1 = 1e-30f;
+      s0 = 1.0f / sf0;
+      s1 = 1.0f / sf1;
+      if (wave == 0 && c0 + c < C) {
+        float2 sv;
+        sv.x = sf0;
+        sv.y = sf1;
+        *(float2*)((float*)col_s + C * P / 128 + jblk * C + c0 + c) = sv;
+      }
+    }
+    v4i q0[2], q1[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t lo = e4m3x4(bf16_lo(w[4 * i]) * s0, bf16_lo(w[4 * i + 1]) * s0, bf16_lo(w[4 * i + 2]) * s0,
+                                 bf16_lo(w[4 * i + 3]) * s0);
+      const uint32_t hi = e4m3x4(bf16_hi(w[4 * i]) * s1, bf16_hi(w[4 * i + 1]) * s1, bf16_hi(w[4 * i + 2]) * s1,
+                                 bf16_hi(w[4 * i + 3]) * s1);
+      q0[i >> 2][i & 3] = (int)lo;
+      q1[i >> 2][i & 3] = (int)hi;
+    }
+    if (c0 + c < C) {
+      uint8_t* dst = col_q + C * P + (c0 + c) * kp + kQRows * jblk + 32 * wave;
+      *(v4i*)dst = q0[0];
+      *(v4i*)(dst + 16) = q0[1];
+      *(v4i*)(dst + kp) = q1[0];
+      *(v4i*)(dst + kp + 16) = q1[1];
+      if constexpr (RECIPE == BSFP8_RECIPE_MX_1X32_E8M0) {
+        *(uint16_t*)((uint8_t*)col_s + C * P / 32 + (4 * jblk + wave) * C + c0 + c) = (uint16_t)sbits;
+      }
+    }
+  }
+
+  if constexpr (ROW) {
+    // ---- rowwise: 16 lanes per row (8 channels each), 4 lanes per 32-channel block ----
+#pragma unroll
+    for (int pass = 0; pass < kQRows / 16; ++pass) {
+      const int r = pass * 16 + (tid >> 4);
+      const int ch = tid & 15;
+      const v4i v = *(const v4i*)&tile[r][ch * 4];
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = max(m, max((uint32_t)v[i] & 0x7fffu, ((uint32_t)v[i] >> 16) & 0x7fffu));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+      const int e = e8m0_exponent(__uint_as_float(m << 16));
+      const float s = exp2_neg(e);
+      v2i q;
+      q[0] = (int)e4m3x4(bf16_lo(v[0]) * s, bf16_hi(v[0]) * s, bf16_lo(v[1]) * s, bf16_hi(v[1]) * s);
+      q[1] = (int)e4m3x4(bf16_lo(v[2]) * s, bf16_hi(v[2]) * s, bf16_lo(v[3]) * s, bf16_hi(v[3]) * s);
+      if (r < nlive && ch * 8 < ncols) *(v2i*)(row_q + (row0 + r) * C + c0 + ch * 8) = q;
+      if ((ch & 3) == 0) rs_tile[ch >> 2][r] = (uint8_t)(e + 127);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < (kQCols / 32) * kQRows / kQThreads; ++i) {
+      const int idx = tid + i * kQThreads;
+      const int b = idx / kQRows, r = idx % kQRows;
+      if (r < nlive && b * 32 < ncols) row_s[(c0 / 32 + b) * R + row0 + r] = rs_tile[b][r];
+    }
+  }
+}
+
+// Upper bound of the number of 128-row tiles over all groups: sum ceil(k_e / 128) <=
+// floor((R + 127 E) / 128) for any valid sizes.
+static inline int64_t quantize_row_tiles(int64_t R, int E, bool grouped) {
+  return grouped ? (R + 127 * (int64_t)E) / kQRows : (R + kQRows - 1) / kQRows;
+}
+
+int launch_grouped_quantize(const void* in, int64_t R, int64_t C, const int32_t* splits, int E, int recipe,
+                            int which, float zas, uint8_t* row_q, uint8_t* row_s, uint8_t* col_q, void* col_s,
+                            uint32_t* status, hipStream_t stream) {
+  const int64_t gx = quantize_row_tiles(R, E, splits != nullptr);
+  const int64_t gy = (C + kQCols - 1) / kQCols;
+  if (gx <= 0 || gy <= 0) return BSFP8_OK;
+  if (gx > 0x7fffffff || gy > 65535) return BSFP8_ERR_SHAPE;
+  dim3 grid((unsigned)gx, (unsigned)gy), block(kQThreads);
+  const uint16_t* x = (const uint16_t*)in;
+  const bool row = (which & BSFP8_ROWWISE) != 0, col = (which & BSFP8_COLWISE) != 0;
+  if (recipe == BSFP8_RECIPE_MX_1X32_E8M0) {
+    if (row && col)
+      hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MX_1X32_E8M0, true, true>), grid, block, 0, stream, x,
+                         R, C, splits, E, zas, row_q, row_s, col_q, col_s, status);
+    else if (row)
+      hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MX_1X32_E8M0, true, false>), grid, block, 0, stream,
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, status);
+    else
+      hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MX_1X32_E8M0, false, true>), grid, block, 0, stream,
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, status);
+  } else {
+    hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_PER_CHANNEL_128_F32, false, true>), grid, block, 0,
+                       stream, x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, status);
+  }
+  return hipGetLastError() == hipSuccess ? BSFP8_OK : BSFP8_ERR_LAUNCH;
+}
+
+}  // namespace bsfp8

@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: every function declared in include/bsfp8.h is exported by
+libbsfp8.so, the size queries follow their documented formulas, and every host-checkable error
+is returned before the library touches a pointer or makes a HIP call (the fake pointers used
+below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp8_grouped_amd as bs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "bsfp8.h")
+
+P = 1 << 20  # a fake, 16-byte-aligned device address; never dereferenced by these calls
+MX, PC = bs.RECIPE_MX, bs.RECIPE_PC
+
+
+def _declared():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsfp8_\w+)\s*\(", text)))
+
+
+def _hdr_consts():
+    text = open(HDR).read()
+    return {k: int(v.strip("()")) for k, v in re.findall(r"#define\s+(BSFP8_\w+)\s+(\(?-?\d+\)?)u?\b", text)}
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 9
+    L = bs.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_binding_constants_match_header():
+    c = _hdr_consts()
+    assert c["BSFP8_RECIPE_MX_1X32_E8M0"] == bs.RECIPE_MX and c["BSFP8_RECIPE_PER_CHANNEL_128_F32"] == bs.RECIPE_PC
+    assert c["BSFP8_ROWWISE"] == bs.ROWWISE and c["BSFP8_COLWISE"] == bs.COLWISE
+    assert c["BSFP8_OUT_F32"] == bs.OUT_F32 and c["BSFP8_OUT_BF16"] == bs.OUT_BF16
+    assert c["BSFP8_MAX_GROUPS"] == bs.MAX_GROUPS
+
+
+def test_size_queries():
+    for R, E in [(1024, 4), (768, 4), (0, 1), (65664, 32), (1048576, 128), (5, 1024)]:
+        rb = 128 * ((R + 127 * E) // 128)
+        assert bs.colwise_rows_bound(R, E) == rb
+        assert bs.colwise_data_bytes(R, 256, E) == rb * 256
+        assert bs.colwise_scale_bytes(R, 256, E, MX) == rb // 32 * 256
+        assert bs.colwise_scale_bytes(R, 256, E, PC) == rb // 128 * 256 * 4
+    # the bound covers the worst case of any valid split
+    for R, E in [(1000, 7), (129, 2), (1, 1)]:
+        worst = sum(128 * ((k + 127) // 128) for k in [R - (E - 1)] + [1] * (E - 1))
+        assert worst <= bs.colwise_rows_bound(R, E)
+    assert bs.rowwise_data_bytes(10, 64) == 640 and bs.rowwise_scale_bytes(10, 64) == 20
+    assert bs.colwise_data_bytes(10, 33, 1) == 0 and bs.colwise_rows_bound(10, 0) == 0
+    assert bs.colwise_scale_bytes(10, 64, 1, 7) == 0
+
+
+def _q(**kw):
+    a = dict(inp=P, R=1024, C=256, splits=P, E=4, recipe=MX, which=bs.COLWISE, zas=1e-30, row_q=P, row_s=P,
+             col_q=P, col_s=P, status=P, stream=None)
+    a.update(kw)
+    return bs.lib().bsfp8_grouped_quantize(a["inp"], a["R"], a["C"], a["splits"], a["E"], a["recipe"], a["which"],
+                                           a["zas"], a["row_q"], a["row_s"], a["col_q"], a["col_s"], a["status"],
+                                           a["stream"])
+
+
+def _w(**kw):
+    a = dict(dyq=P, dys=P, n=256, xq=P, xs=P, h=256, splits=P, E=4, R=1024, recipe=MX, out=P, acc=0, status=P)
+    a.update(kw)
+    return bs.lib().bsfp8_grouped_gemm_wgrad(a["dyq"], a["dys"], a["n"], a["xq"], a["xs"], a["h"], a["splits"],
+                                             a["E"], a["R"], a["recipe"], a["out"], a["acc"], a["status"], None)
+
+
+def _f(**kw):
+    a = dict(xq=P, xs=P, R=1024, k=256, wq=P, ws=P, n=256, splits=P, E=4, out=P, dtype=bs.OUT_F32, status=P)
+    a.update(kw)
+    return bs.lib().bsfp8_grouped_gemm_fprop(a["xq"], a["xs"], a["R"], a["k"], a["wq"], a["ws"], a["n"],
+                                             a["splits"], a["E"], a["out"], a["dtype"], a["status"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(recipe=0), -3), (dict(recipe=3), -3),
+    (dict(which=0), -7), (dict(which=4), -7),
+    (dict(which=bs.ROWWISE, recipe=PC), -6),
+    (dict(C=33), -4), (dict(C=0), -4), (dict(R=-1), -4),
+    (dict(recipe=PC, zas=float("nan")), -7), (dict(recipe=PC, zas=-1.0), -7), (dict(recipe=PC, zas=float("inf")), -7),
+    (dict(splits=None), -1),
+    (dict(E=0), -2), (dict(E=1025), -2),
+    (dict(inp=None), -1), (dict(col_q=None), -1), (dict(col_s=None), -1),
+    (dict(which=bs.ROWWISE | bs.COLWISE, row_q=None), -1),
+    (dict(inp=P + 8), -5), (dict(col_q=P + 4), -5), (dict(splits=P + 2), -5), (dict(status=P + 1), -5),
+])
+def test_quantize_rejects_before_launch(kw, code):
+    assert _q(**kw) == code
+
+
+def test_quantize_zero_rows_returns_without_touching_pointers():
+    assert _q(R=0, inp=None, col_q=None, col_s=None) == 0
+    assert _q(R=0, which=bs.ROWWISE, splits=None, inp=None, row_q=None, row_s=None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(recipe=5), -3), (dict(E=0), -2), (dict(E=2000), -2),
+    (dict(n=100), -4), (dict(h=0), -4), (dict(R=-5), -4),
+    (dict(acc=2), -7), (dict(R=(1 << 24)), -4),
+    (dict(splits=None), -1), (dict(out=None), -1), (dict(dyq=None), -1), (dict(xs=None), -1),
+    (dict(out=P + 4), -5), (dict(dys=P + 1), -5), (dict(splits=P + 2), -5),
+])
+def test_wgrad_rejects_before_launch(kw, code):
+    assert _w(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(E=0), -2), (dict(k=48), -4), (dict(n=-32), -4), (dict(dtype=2), -7), (dict(k=1 << 24), -4),
+    (dict(xq=None), -1), (dict(ws=None), -1), (dict(splits=None), -1), (dict(out=None), -1),
+    (dict(out=P + 2), -5), (dict(wq=P + 8), -5),
+])
+def test_fprop_rejects_before_launch(kw, code):
+    assert _f(**kw) == code
+
+
+def test_fprop_zero_rows_early_return():
+    """TE PR #3224: a zero-row batch returns before any data pointer is used."""
+    assert _f(R=0, xq=None, xs=None, wq=None, ws=None, splits=None, out=None) == 0
+
+
+def test_strerror_covers_codes():
+    for c in range(-8, 1):
+        assert bs.strerror(c) != "unknown error code"
+    assert bs.strerror(-99) == "unknown error code"
