@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP8 grouped path on one MI355X.
+
+Workload: the MoE expert layer with 128 experts, 131,072 tokens x top-8 = 1,048,576 expert rows
+(6 empty experts, multinomial counts over the rest), hidden 7168, ffn 2048, bf16 inputs drawn
+as randn * 0.5, MXFP8 1x32 E8M0 recipe.  Inputs are seeded and generated on the GPU before the
+timed region.
+
+One step is one pass of the whole path:
+  1. grouped quantize of x  [T, 7168]: rowwise (for fprop) and colwise (for wgrad) in one pass
+  2. grouped quantize of dy [T, 2048]: colwise
+  3. quantize of the weight W [128 * 2048, 7168]: rowwise
+  4. k-grouped wgrad, accumulated into the fp32 main_grad [128, 2048, 7168]
+  5. m-grouped fprop, bf16 output [T, 2048]
+
+Reported (one JSON line on stdout):
+  value       useful wgrad TFLOP/s of the whole step: 2 * ffn * hidden * T per step / step time
+              (quantize and fprop time included, so this is a lower bound of the wgrad kernel's
+              own rate, which the roofline object reports).
+  roofline    the wgrad kernel: achieved = useful FLOP / its mean duration (HIP events on the
+              launch stream inside the timed region), against the bf16 MFMA peak the kernel
+              runs on; `traffic` is the HBM bytes per launch measured with rocprofv3 counters
+              when the committed measurement matches the current kernel source, else null.
+  legs        mean duration and rate of every kernel of the step.
+  cpu_baseline the CPU oracle (quantize + fp64 wgrad) on one expert and a slice of the dy
+              channels, in the same unit, with the number of threads it used.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "grouped FP8 wgrad TFLOP/s (useful FLOPs) and % of FP8 MFMA peak, 1 GPU"
+PEAK_BF16_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (the instruction the GEMMs run on)
+PEAK_FP8_MFMA_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wgrad_moe128_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.hpp", "tile_addr.hpp"):
+        with open(os.path.join(ROOT, "block_scaled_fp8_grouped_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per wgrad launch from the committed counter measurement, when it was taken on
+    the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, experts, channels):
+    """The oracle (as it stands) on a bounded sample of the workload: `experts` experts of
+    median size, all their rows, `channels` dy channels x all x channels each.  Returns the
+    useful wgrad FLOP rate in TFLOP/s, the threads used and a description of the sample."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    splits = case["splits"]
+    n, h = case["n"], case["h"]
+    channels = min(channels, n)
+    live = sorted((k, e) for e, k in enumerate(splits) if k > 0)
+    mid = len(live) // 2
+    picked = live[mid:mid + experts]
+    rows = np.arange(channels, dtype=np.int32)
+    offs = np.concatenate([[0], np.cumsum(splits)])
+    flops, dt = 0.0, 0.0
+    for k, e in picked:
+        off = int(offs[e])
+        dy = W.bf16_bits(case["dy"][off:off + k])
+        x = W.bf16_bits(case["x"][off:off + k])
+        t0 = time.perf_counter()
+        oq_dy = oracle.grouped_quantize(dy, [k], oracle.RECIPE_MX, oracle.COLWISE)
+        oq_x = oracle.grouped_quantize(x, [k], oracle.RECIPE_MX, oracle.COLWISE)
+        oracle.grouped_wgrad(oq_dy["col_q"], oq_dy["col_s"], n, oq_x["col_q"], oq_x["col_s"], h, [k], k,
+                             oracle.RECIPE_MX, rows_sel=rows)
+        dt += time.perf_counter() - t0
+        flops += 2.0 * channels * h * k
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"experts {[e for _, e in picked]} ({[k for k, _ in picked]} rows): colwise quantize of their "
+                  f"dy and x rows, then fp64 wgrad of {channels} of {n} dy channels x all {h} x channels "
+                  f"({flops / 1e9:.0f} GFLOP useful) in {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--cpu-experts", type=int, default=2,
+                    help="experts in the CPU-baseline sample (0 skips it)")
+    ap.add_argument("--cpu-channels", type=int, default=2048, help="dy channels per sampled expert")
+    ap.add_argument("--calibrate-copy-gb", type=float, default=0.0,
+                    help="after the timed region, run one device copy of this many GB (for counter "
+                         "calibration against a kernel of known traffic)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_scaled_fp8_grouped_amd as bs
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating the 128-expert workload on the GPU")
+    case = W.moe128_top8(dev)
+    splits, R, T = case["splits"], case["R"], case["T"]
+    n, h, K, N = case["n"], case["h"], case["K"], case["N"]
+    E = len(splits)
+    st = W.splits_tensor(splits, dev)
+    w2 = case["W"].view(E * N, K)
+    mg = case["main_grad"]
+    xq = bs.alloc_quantized(R, h, E, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, dev)
+    dq = bs.alloc_quantized(R, n, E, bs.RECIPE_MX, bs.COLWISE, dev)
+    wq = bs.alloc_quantized(E * N, K, 1, bs.RECIPE_MX, bs.ROWWISE, dev)
+    fout = torch.empty(R, N, dtype=torch.bfloat16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    legs = ["quantize_x", "quantize_dy", "quantize_w", "wgrad", "fprop"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        bs.grouped_quantize(case["x"], st, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, xq, status=status)
+        mark(1)
+        bs.grouped_quantize(case["dy"], st, bs.RECIPE_MX, bs.COLWISE, dq, status=status)
+        mark(2)
+        bs.grouped_quantize(w2, None, bs.RECIPE_MX, bs.ROWWISE, wq)
+        mark(3)
+        bs.grouped_gemm_wgrad(dq, n, xq, h, st, R, bs.RECIPE_MX, mg, accumulate=True, status=status)
+        mark(4)
+        bs.grouped_gemm_fprop(xq, K, wq, N, st, R, fout, bs.OUT_BF16, status=status)
+        mark(5)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    leg_ms = {name: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps for i, name in enumerate(legs)}
+
+    wgrad_flop = 2.0 * n * h * T
+    fprop_flop = 2.0 * T * K * N
+    # algorithmic HBM bytes: bf16 read once, e4m3 + E8M0 written once per requested layout
+    kp_rows = sum(128 * ((k + 127) // 128) for k in splits)
+    bytes_x = T * h * 2 + T * h * (1 + 1 / 32) + kp_rows * h * (1 + 1 / 32)
+    bytes_dy = T * n * 2 + kp_rows * n * (1 + 1 / 32)
+    bytes_w = E * N * K * (2 + 1 + 1 / 32)
+    wgrad_bytes = (n + h) * kp_rows * (1 + 1 / 32) + 2 * 4.0 * n * h * sum(1 for k in splits if k)
+    fprop_bytes = T * K * (1 + 1 / 32) + E * N * K * (1 + 1 / 32) + T * N * 2
+
+    wg_s = leg_ms["wgrad"] / 1e3
+    achieved = wgrad_flop / wg_s / 1e12
+    traffic = measured_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(wgrad_flop / (ms_per_step / 1e3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "operand_storage": "e4m3 + E8M0 (MXFP8 1x32)",
+        "data": "synthetic",
+        "config": {
+            "workload": "moe128_top8: 128 experts, 1,048,576 expert rows (6 empty), hidden 7168, ffn 2048, "
+                        "MXFP8 1x32 E8M0, wgrad into fp32 main_grad, fprop bf16",
+            "experts": E, "expert_rows": T, "hidden": h, "ffn": n,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_BF16_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_MFMA_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "grouped_gemm_kernel<wgrad, MX, 256x256, accumulate>",
+            "frac_of_fp8_peak": round(achieved / PEAK_FP8_MFMA_TFLOPS, 4),
+        },
+        "legs": {
+            "quantize_x": {"ms": round(leg_ms["quantize_x"], 3),
+                           "GB/s": round(bytes_x / (leg_ms["quantize_x"] / 1e3) / 1e9, 1)},
+            "quantize_dy": {"ms": round(leg_ms["quantize_dy"], 3),
+                            "GB/s": round(bytes_dy / (leg_ms["quantize_dy"] / 1e3) / 1e9, 1)},
+            "quantize_w": {"ms": round(leg_ms["quantize_w"], 3),
+                           "GB/s": round(bytes_w / (leg_ms["quantize_w"] / 1e3) / 1e9, 1)},
+            "wgrad": {"ms": round(leg_ms["wgrad"], 3), "TFLOP/s": round(achieved, 1),
+                      "algorithmic_GB": round(wgrad_bytes / 1e9, 2)},
+            "fprop": {"ms": round(leg_ms["fprop"], 3),
+                      "TFLOP/s": round(fprop_flop / (leg_ms["fprop"] / 1e3) / 1e12, 1),
+                      "algorithmic_GB": round(fprop_bytes / 1e9, 2)},
+        },
+    }
+    if args.calibrate_copy_gb > 0:
+        nbytes = int(args.calibrate_copy_gb * 1e9) // 16 * 16
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calibration_copy_bytes"] = nbytes
+        del src, dst
+    if args.cpu_experts > 0:
+        log("CPU baseline (oracle on a sample)")
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_experts, args.cpu_channels)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,6 +33,7 @@
 // it) and their results are not stored.
 #include "common.hpp"
 #include "tile_addr.hpp"
+#include "tile_sched.hpp"
 
 namespace bsfp8 {
 
@@ -50,6 +51,8 @@ struct GemmArgs {
   const int32_t* splits;
   int E;
   int tiles_m, tiles_n;  // wgrad: per-group tile grid; fprop: tiles_n only
+  int64_t tiles;         // logical tiles (fprop: an upper bound; spare ones exit)
+  int64_t per_xcd;       // launch = 8 * per_xcd workgroups, see xcd_logical()
   void* out;
   uint32_t* status;
 };
@@ -101,22 +104,23 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   // ---------------- tile placement (device scheduler) ----------------
   GroupInfo gi;
   int e, tm, tn;
+  // workgroup -> logical tile in the XCD-aware order; workgroup 0 always has tile 0 and is
+  // the one that reports the status bits
+  const int64_t L = xcd_logical(blockIdx.x, args.per_xcd);
+  if (L >= args.tiles) return;
   if constexpr (MODE == kModeWgrad) {
-    const int per = args.tiles_m * args.tiles_n;
-    e = (int)(blockIdx.x / per);
-    const int rem = (int)(blockIdx.x % per);
-    tm = rem / args.tiles_n;
-    tn = rem % args.tiles_n;
+    wgrad_tile(L, args.tiles_m, args.tiles_n, &e, &tm, &tn);
     const uint32_t flags = group_scan<NT>(args.splits, args.E, args.R, 0, 0, e, gsm, gi);
     report_status(args.status, flags);
     if (gi.e < 0) return;
   } else {
-    const uint32_t flags = group_scan<NT>(args.splits, args.E, args.R, BM, blockIdx.x, 0, gsm, gi);
+    int64_t mt;
+    fprop_tile(L, args.tiles_n, &mt, &tn);
+    const uint32_t flags = group_scan<NT>(args.splits, args.E, args.R, BM, mt, 0, gsm, gi);
     report_status(args.status, flags);
     if (gi.e < 0) return;
     e = gi.e;
-    tm = (int)(blockIdx.x - gi.tile);
-    tn = blockIdx.y;
+    tm = (int)(mt - gi.tile);
   }
 
   // ---------------- operand descriptors ----------------
@@ -367,43 +371,94 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   }
 
   // ---------------- epilogue ----------------
-  // fragment element r of lane (h, l32): row 8 (r / 4) + 4 h + r % 4, column l32
-  if constexpr (MODE == kModeWgrad) {
-    float* o = (float*)args.out + ((int64_t)e * args.M + a_row0) * args.N + b_row0;
-    const bool full = a_row0 + BM <= args.M && b_row0 + BN <= args.N;
+  // The accumulators leave through LDS, half a tile (BM / WAVES_M rows) at a time: the waves
+  // owning those rows write their fragments into a row-major fp32 block (row pitch padded so the
+  // two 32-lane halves of a fragment write land in different banks), then every thread moves
+  // 16-byte runs of full rows to HBM -- 64 threads cover one 1 KB row segment -- issuing all of
+  // its loads of main_grad before the first add.  Fragment element r of lane (h, l32) sits at
+  // row 8 (r / 4) + 4 h + r % 4, column l32 of its 32 x 32 fragment.
+  {
+    constexpr int HR = WM;                 // rows per pass (one wave row)
+    constexpr int PITCH = BN + 8;          // fp32 words per LDS row
+    constexpr int V4_PER_ROW = BN / 4;
+    constexpr int ROWS_PER_IT = NT / V4_PER_ROW;
+    constexpr int ITS = HR / ROWS_PER_IT;  // float4 per thread per pass
+    static_assert(HR * PITCH * 4 <= 2 * S::STAGE, "epilogue LDS block");
+    static_assert(NT % V4_PER_ROW == 0 && HR % ROWS_PER_IT == 0, "epilogue thread map");
+    float* blk = (float*)smem;
+    const int c4 = tid % V4_PER_ROW, r_in = tid / V4_PER_ROW;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int pass = 0; pass < S::WAVES_M; ++pass) {
+      if (wm == pass) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = wn * WN + j * 32 + l32;
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * WM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (full || (a_row0 + row < args.M && b_row0 + col < args.N)) {
-            float* p = o + (int64_t)row * args.N + col;
-            if constexpr (ACCUM) *p = *p + acc[i][j][r];
-            else *p = acc[i][j][r];
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+              blk[row * PITCH + wn * WN + j * 32 + l32] = acc[i][j][r];
+            }
+      }
+      __syncthreads();
+      const int64_t prow0 = a_row0 + (int64_t)pass * HR;  // first row of this pass in the group
+      const bool col_ok = b_row0 + 4 * c4 < args.N;
+      constexpr int BATCH = ITS < 16 ? ITS : 16;  // rows in flight per thread
+#pragma unroll
+      for (int b0 = 0; b0 < ITS; b0 += BATCH) {
+        float4 v[BATCH];
+#pragma unroll
+        for (int it = 0; it < BATCH; ++it)
+          v[it] = *(const float4*)(blk + (r_in + (b0 + it) * ROWS_PER_IT) * PITCH + 4 * c4);
+        if constexpr (MODE == kModeWgrad) {
+          float* o = (float*)args.out + ((int64_t)e * args.M + prow0) * args.N + b_row0 + 4 * c4;
+          if constexpr (ACCUM) {
+            float4 m[BATCH];
+#pragma unroll
+            for (int it = 0; it < BATCH; ++it) {
+              const int row = r_in + (b0 + it) * ROWS_PER_IT;
+              if (col_ok && prow0 + row < args.M) m[it] = *(const float4*)(o + (int64_t)row * args.N);
+            }
+#pragma unroll
+            for (int it = 0; it < BATCH; ++it) {
+              const int row = r_in + (b0 + it) * ROWS_PER_IT;
+              if (col_ok && prow0 + row < args.M) {
+                float4 w;
+                w.x = m[it].x + v[it].x;
+                w.y = m[it].y + v[it].y;
+                w.z = m[it].z + v[it].z;
+                w.w = m[it].w + v[it].w;
+                *(float4*)(o + (int64_t)row * args.N) = w;
+              }
+            }
+          } else {
+#pragma unroll
+            for (int it = 0; it < BATCH; ++it) {
+              const int row = r_in + (b0 + it) * ROWS_PER_IT;
+              if (col_ok && prow0 + row < args.M) *(float4*)(o + (int64_t)row * args.N) = v[it];
+            }
+          }
+        } else {
+          const int64_t rows_left = gi.k - prow0;
+#pragma unroll
+          for (int it = 0; it < BATCH; ++it) {
+            const int row = r_in + (b0 + it) * ROWS_PER_IT;
+            if (col_ok && row < rows_left) {
+              const int64_t idx = (gi.off + prow0 + row) * args.N + b_row0 + 4 * c4;
+              if constexpr (OUT == BSFP8_OUT_F32) {
+                *(float4*)((float*)args.out + idx) = v[it];
+              } else {
+                uint2 w;
+                w.x = (uint32_t)f32_to_bf16_rne(v[it].x) | ((uint32_t)f32_to_bf16_rne(v[it].y) << 16);
+                w.y = (uint32_t)f32_to_bf16_rne(v[it].z) | ((uint32_t)f32_to_bf16_rne(v[it].w) << 16);
+                *(uint2*)((uint16_t*)args.out + idx) = w;
+              }
+            }
           }
         }
       }
-  } else {
-    const int64_t rows_left = gi.k - a_row0;
-    const bool full = rows_left >= BM && b_row0 + BN <= args.N;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = wn * WN + j * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * WM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (full || (row < rows_left && b_row0 + col < args.N)) {
-            const int64_t idx = (gi.off + a_row0 + row) * args.N + b_row0 + col;
-            if constexpr (OUT == BSFP8_OUT_F32) ((float*)args.out)[idx] = acc[i][j][r];
-            else ((uint16_t*)args.out)[idx] = f32_to_bf16_rne(acc[i][j][r]);
-          }
-        }
-      }
+      __syncthreads();
+    }
   }
 }
 
@@ -437,18 +492,20 @@ int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, 
     constexpr int BM = 256, BN = 256;
     a.tiles_m = (int)((n + BM - 1) / BM);
     a.tiles_n = (int)((h + BN - 1) / BN);
-    const int64_t blocks = (int64_t)E * a.tiles_m * a.tiles_n;
-    if (blocks > 0x7fffffff) return BSFP8_ERR_SHAPE;
-    dim3 grid((unsigned)blocks);
+    a.tiles = (int64_t)E * a.tiles_m * a.tiles_n;
+    a.per_xcd = (a.tiles + kXcds - 1) / kXcds;
+    if (a.per_xcd * kXcds > 0x7fffffff) return BSFP8_ERR_SHAPE;
+    dim3 grid((unsigned)(a.per_xcd * kXcds));
     return accumulate ? launch<kModeWgrad, false, BM, BN, 128, 128, true, 0>(a, grid, stream)
                       : launch<kModeWgrad, false, BM, BN, 128, 128, false, 0>(a, grid, stream);
   }
   constexpr int BM = 128, BN = 128;
   a.tiles_m = (int)((n + BM - 1) / BM);
   a.tiles_n = (int)((h + BN - 1) / BN);
-  const int64_t blocks = (int64_t)E * a.tiles_m * a.tiles_n;
-  if (blocks > 0x7fffffff) return BSFP8_ERR_SHAPE;
-  dim3 grid((unsigned)blocks);
+  a.tiles = (int64_t)E * a.tiles_m * a.tiles_n;
+  a.per_xcd = (a.tiles + kXcds - 1) / kXcds;
+  if (a.per_xcd * kXcds > 0x7fffffff) return BSFP8_ERR_SHAPE;
+  dim3 grid((unsigned)(a.per_xcd * kXcds));
   return accumulate ? launch<kModeWgrad, true, BM, BN, 64, 64, true, 0>(a, grid, stream)
                     : launch<kModeWgrad, true, BM, BN, 64, 64, false, 0>(a, grid, stream);
 }
@@ -470,11 +527,14 @@ int launch_grouped_gemm_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R,
   a.out = out;
   a.status = status;
   a.tiles_n = (int)((N + BN - 1) / BN);
-  // upper bound of sum ceil(k_e / BM) over valid sizes
+  // upper bound of sum ceil(k_e / BM) over valid sizes, rounded up to whole runs of m-tiles
+  const int64_t gm = fprop_run_mtiles(a.tiles_n);
   const int64_t mt = (R + (int64_t)(BM - 1) * E) / BM;
   if (mt <= 0) return BSFP8_OK;
-  if (mt > 0x7fffffff || a.tiles_n > 65535) return BSFP8_ERR_SHAPE;
-  dim3 grid((unsigned)mt, (unsigned)a.tiles_n);
+  a.tiles = (mt + gm - 1) / gm * gm * a.tiles_n;
+  a.per_xcd = (a.tiles + kXcds - 1) / kXcds;
+  if (a.per_xcd * kXcds > 0x7fffffff) return BSFP8_ERR_SHAPE;
+  dim3 grid((unsigned)(a.per_xcd * kXcds));
   return out_dtype == BSFP8_OUT_F32
              ? launch<kModeFprop, false, BM, BN, 128, 128, false, BSFP8_OUT_F32>(a, grid, stream)
              : launch<kModeFprop, false, BM, BN, 128, 128, false, BSFP8_OUT_BF16>(a, grid, stream);

@@ -1,0 +1,60 @@
+// Tile order of the grouped GEMMs on MI355X: 8 XCDs of 32 CUs, each XCD with its own L2.
+//
+// The hardware hands workgroup b to XCD b % 8, and each XCD takes its workgroups in increasing
+// b.  xcd_logical() renumbers the launch so that XCD x walks the contiguous logical range
+// [x * per, (x + 1) * per); the logical order then packs tiles that share operand panels into
+// runs of 32 (one per CU of an XCD), so the 32 workgroups running together on one XCD read the
+// same few A and B panels at the same K positions through that XCD's L2.
+//   wgrad: per group, blocks of `gn` tile columns; inside a block, tile rows then columns
+//          (TM x gn tiles with gn = 32 / TM share all A panels and gn B panels).
+//   fprop: runs of `gm` m-tiles (rows of one group's tokens) times all TN weight tiles.
+// Plain C++ for the host-side bijection test and for gfx950.
+#pragma once
+
+#include <stdint.h>
+
+#include "tile_addr.hpp"  // BSFP8_HD
+
+namespace bsfp8 {
+
+constexpr int kXcds = 8;
+constexpr int kCusPerXcd = 32;
+
+// Logical tile of workgroup b in a launch of 8 * per workgroups.
+BSFP8_HD int64_t xcd_logical(int64_t b, int64_t per) { return (b % kXcds) * per + b / kXcds; }
+
+// Columns per block of the wgrad order for a TM-row tile grid.
+BSFP8_HD int wgrad_block_cols(int tm_count) {
+  const int g = kCusPerXcd / tm_count;
+  return g > 0 ? g : 1;
+}
+
+// wgrad: logical tile L < E * TM * TN -> (group e, tile row tm, tile column tn).
+BSFP8_HD void wgrad_tile(int64_t L, int TM, int TN, int* e, int* tm, int* tn) {
+  const int64_t per_group = (int64_t)TM * TN;
+  *e = (int)(L / per_group);
+  const int r = (int)(L % per_group);
+  const int gn = wgrad_block_cols(TM);
+  const int j = r / (TM * gn);                 // column block
+  const int q = r - j * TM * gn;
+  const int w = TN - j * gn < gn ? TN - j * gn : gn;  // width of this block
+  *tm = q / w;
+  *tn = j * gn + q % w;
+}
+
+// fprop: m-tiles per run for TN weight tiles.
+BSFP8_HD int fprop_run_mtiles(int tn_count) {
+  const int g = kCusPerXcd / tn_count;
+  return g > 0 ? g : 1;
+}
+
+// fprop: logical tile L -> (global m-tile index mt, weight tile tn).
+BSFP8_HD void fprop_tile(int64_t L, int TN, int64_t* mt, int* tn) {
+  const int gm = fprop_run_mtiles(TN);
+  const int64_t run = L / ((int64_t)gm * TN);
+  const int w = (int)(L % ((int64_t)gm * TN));
+  *mt = run * gm + w / TN;
+  *tn = w % TN;
+}
+
+}  // namespace bsfp8

@@ -63,10 +63,17 @@ def lib():
                                            _vp, _i32, ctypes.c_int, _vp, _vp]
         L.oracle_grouped_fprop.restype = ctypes.c_int
         L.oracle_grouped_fprop.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _vp]
+        L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_num_threads.argtypes = []
         L.oracle_wgrad_unquantized.restype = ctypes.c_int
         L.oracle_wgrad_unquantized.argtypes = [_vp, _i64, _vp, _i64, _vp, _i32, _i64, _vp]
         _lib = L
     return _lib
+
+
+def num_threads():
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().oracle_num_threads())
 
 
 def _p(a):

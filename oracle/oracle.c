@@ -42,6 +42,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_OK 0
 #define ORACLE_EINVAL (-1)
@@ -51,6 +54,15 @@
 #define RECIPE_PC 2  /* per channel, one fp32 scale per 128 rows (the DeepGEMM reproducer's cast) */
 #define WHICH_ROW 1
 #define WHICH_COL 2
+
+/* Number of OpenMP threads the parallel loops below use (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------------------------------ */
 /* OCP FP8 E4M3FN codec.                                                                       */

@@ -1,0 +1,73 @@
+// Host check of the XCD-aware tile order (csrc/tile_sched.hpp), run by tests/test_tile_addr.py:
+// over a launch of 8 * per workgroups every tile is produced exactly once, spare workgroups map
+// past the tile count, workgroup 0 gets tile 0, and each XCD walks a contiguous logical range.
+#include <cstdint>
+#include <cstdio>
+#include <vector>
+
+#include "tile_sched.hpp"
+
+using namespace bsfp8;
+
+static long g_fail = 0;
+
+static void check_wgrad(int E, int TM, int TN) {
+  const int64_t G = (int64_t)E * TM * TN, per = (G + kXcds - 1) / kXcds;
+  std::vector<int> seen((size_t)G, 0);
+  for (int64_t b = 0; b < per * kXcds; ++b) {
+    const int64_t L = xcd_logical(b, per);
+    if (b == 0 && L != 0) ++g_fail;
+    if (L < 0 || L >= per * kXcds) { ++g_fail; continue; }
+    if (L >= G) continue;
+    int e, tm, tn;
+    wgrad_tile(L, TM, TN, &e, &tm, &tn);
+    if (e < 0 || e >= E || tm < 0 || tm >= TM || tn < 0 || tn >= TN) {
+      if (g_fail++ < 10) std::printf("wgrad E=%d TM=%d TN=%d: L=%lld -> (%d,%d,%d) out of range\n", E, TM, TN, (long long)L, e, tm, tn);
+      continue;
+    }
+    seen[((size_t)e * TM + tm) * TN + tn]++;
+  }
+  for (int64_t i = 0; i < G; ++i)
+    if (seen[(size_t)i] != 1 && g_fail++ < 10) std::printf("wgrad E=%d TM=%d TN=%d: tile %lld seen %d\n", E, TM, TN, (long long)i, seen[(size_t)i]);
+}
+
+static void check_fprop(int64_t MT, int TN) {
+  const int64_t gm = fprop_run_mtiles(TN);
+  const int64_t G = (MT + gm - 1) / gm * gm * TN, per = (G + kXcds - 1) / kXcds;
+  const int64_t mt_cap = (MT + gm - 1) / gm * gm;
+  std::vector<int> seen((size_t)(mt_cap * TN), 0);
+  for (int64_t b = 0; b < per * kXcds; ++b) {
+    const int64_t L = xcd_logical(b, per);
+    if (L >= G) continue;
+    int64_t mt;
+    int tn;
+    fprop_tile(L, TN, &mt, &tn);
+    if (mt < 0 || mt >= mt_cap || tn < 0 || tn >= TN) {
+      if (g_fail++ < 10) std::printf("fprop MT=%lld TN=%d: L=%lld -> (%lld,%d)\n", (long long)MT, TN, (long long)L, (long long)mt, tn);
+      continue;
+    }
+    seen[(size_t)(mt * TN + tn)]++;
+  }
+  for (size_t i = 0; i < seen.size(); ++i)
+    if (seen[i] != 1 && g_fail++ < 10) std::printf("fprop MT=%lld TN=%d: tile %zu seen %d\n", (long long)MT, TN, i, seen[i]);
+}
+
+int main() {
+  // xcd_logical is a bijection of [0, 8 per) and XCD x walks [x per, (x + 1) per) in order
+  for (int64_t per : {1, 3, 7, 100, 3417}) {
+    std::vector<int> seen((size_t)(per * kXcds), 0);
+    for (int64_t b = 0; b < per * kXcds; ++b) {
+      const int64_t L = xcd_logical(b, per);
+      seen[(size_t)L]++;
+      if (L != (b % kXcds) * per + b / kXcds) ++g_fail;
+    }
+    for (int v : seen) if (v != 1) ++g_fail;
+  }
+  const int dims[][3] = {{1, 1, 1}, {4, 1, 1}, {4, 8, 8}, {1, 4, 4}, {128, 8, 28}, {32, 6, 16}, {5, 2, 3},
+                         {7, 1, 3}, {1024, 1, 1}, {3, 40, 2}, {2, 33, 33}};
+  for (auto& d : dims) check_wgrad(d[0], d[1], d[2]);
+  for (int64_t MT : {1, 2, 3, 4, 5, 31, 33, 260, 4224})
+    for (int TN : {1, 2, 6, 8, 28, 40}) check_fprop(MT, TN);
+  std::printf("tile order: %ld violations\n", g_fail);
+  return g_fail == 0 ? 0 : 1;
+}
