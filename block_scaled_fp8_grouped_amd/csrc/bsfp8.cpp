@@ -31,6 +31,10 @@ bool valid_dim(int64_t d) { return d > 0 && d % 32 == 0 && d <= (int64_t(1) << 4
 // The GEMM kernels address a 256-row operand tile with 32-bit offsets: 256 * row length must
 // stay below 2^32, i.e. a K extent (k for fprop, a group's padded rows for wgrad) below 2^24.
 constexpr int64_t kMaxKExtent = (int64_t(1) << 24) - 128;
+// The GEMM epilogues address a 128-row block of the output with 32-bit byte offsets and mark
+// lanes past the last column with offsets from 2^31 up: 128 * 4 * (output row length) must stay
+// below 2^31.
+constexpr int64_t kMaxOutCols = int64_t(1) << 21;
 
 }  // namespace
 
@@ -95,7 +99,7 @@ int bsfp8_grouped_gemm_wgrad(const uint8_t* dy_col_q, const void* dy_col_s, int6
   if (!valid_recipe(recipe)) return BSFP8_ERR_RECIPE;
   if (!valid_groups(num_groups)) return BSFP8_ERR_NUM_GROUPS;
   if (!valid_dim(n) || !valid_dim(h) || capacity_rows < 0) return BSFP8_ERR_SHAPE;
-  if (capacity_rows + 127 > kMaxKExtent) return BSFP8_ERR_SHAPE;
+  if (capacity_rows + 127 > kMaxKExtent || h > kMaxOutCols) return BSFP8_ERR_SHAPE;
   if (accumulate != 0 && accumulate != 1) return BSFP8_ERR_ARGUMENT;
   if (split_sizes == nullptr || out == nullptr) return BSFP8_ERR_NULL_POINTER;
   // the operands are read only when some group is non-empty, which needs capacity_rows > 0
@@ -112,7 +116,8 @@ int bsfp8_grouped_gemm_fprop(const uint8_t* x_row_q, const uint8_t* x_row_s, int
                              const uint8_t* w_q, const uint8_t* w_s, int64_t n, const int32_t* split_sizes,
                              int32_t num_groups, void* out, int out_dtype, uint32_t* status, void* stream) {
   if (!valid_groups(num_groups)) return BSFP8_ERR_NUM_GROUPS;
-  if (!valid_dim(k) || !valid_dim(n) || capacity_rows < 0 || k > kMaxKExtent) return BSFP8_ERR_SHAPE;
+  if (!valid_dim(k) || !valid_dim(n) || capacity_rows < 0 || k > kMaxKExtent || n > kMaxOutCols)
+    return BSFP8_ERR_SHAPE;
   if (out_dtype != BSFP8_OUT_F32 && out_dtype != BSFP8_OUT_BF16) return BSFP8_ERR_ARGUMENT;
   if (capacity_rows == 0) return BSFP8_OK;  // zero-row early return: nothing is dereferenced
   if (x_row_q == nullptr || x_row_s == nullptr || w_q == nullptr || w_s == nullptr || split_sizes == nullptr ||

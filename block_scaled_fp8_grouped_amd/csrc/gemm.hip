@@ -25,8 +25,7 @@
 // over all banks.  A lane of a 32 x 32 fragment owns row (lane % 32) and reads, for the K half
 // s of the step, chunks 4s + h and 4s + 2 + h (h = lane / 32): the first lies in 32-block 2s,
 // the second in 2s + 1, so each half-fragment has a single block scale.  The next step's loads
-// are issued only after this step's fragments have been read into registers, so they overlap
-// the step's MFMAs.
+// are issued once the first K half's fragments are read and overlap the step's MFMAs.
 //
 // Determinism: one workgroup per output tile, fixed instruction order, no atomics, no split-K.
 // Rows past a group's live rows are clamped to its last live row on load (never read beyond
@@ -60,9 +59,17 @@ struct GemmArgs {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-// fp32 value 2^(byte - 127) of an E8M0 scale byte (byte 0 is the fp32 subnormal 2^-127).
-__device__ __forceinline__ float e8m0_value(uint32_t byte) {
-  return byte ? __uint_as_float(byte << 23) : __uint_as_float(0x00400000u);
+// fp32 value 2^(byte - 127) of an E8M0 scale byte: the exponent field is the byte itself; byte 0
+// is the fp32 subnormal 2^-127 (0x00400000, below every byte << 23 for byte >= 1).
+__device__ __forceinline__ float e8m0_value(uint32_t byte) { return __uint_as_float(max(byte << 23, 0x00400000u)); }
+
+// Orders a wave's LDS writes before its later LDS reads from other lanes of the same wave (the
+// fence keeps the compiler from moving LDS accesses across; the wait drains the wave's LDS queue).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Eight e4m3 codes (two dwords) -> eight bf16 values times `scale`.
@@ -319,6 +326,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
           bs[j][1] = e8m0_value(cur[S::SB_OFF + (2 * s + 1) * BN + row]);
         }
       }
+      // the next step's loads go out once this half's reads are issued: issued before the first
+      // read of `cur`, the compiler would make every read of the step wait for them
       if (s == 0 && kk + 1 < nk) issue(kk + 1, nxt);
       // widen and multiply: 4 bf16 MFMAs (K = 16 each) per fragment pair
 #pragma unroll
@@ -371,93 +380,70 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   }
 
   // ---------------- epilogue ----------------
-  // The accumulators leave through LDS, half a tile (BM / WAVES_M rows) at a time: the waves
-  // owning those rows write their fragments into a row-major fp32 block (row pitch padded so the
-  // two 32-lane halves of a fragment write land in different banks), then every thread moves
-  // 16-byte runs of full rows to HBM -- 64 threads cover one 1 KB row segment -- issuing all of
-  // its loads of main_grad before the first add.  Fragment element r of lane (h, l32) sits at
-  // row 8 (r / 4) + 4 h + r % 4, column l32 of its 32 x 32 fragment.
+  // Each wave moves its own WM x WN block to HBM, one 32-row fragment row at a time, through a
+  // private LDS buffer, so no wave waits for another: the fragments of the row are written into
+  // a row-major fp32 block (row pitch padded so that the two 32-lane halves of a fragment write,
+  // rows 4 apart, fall in different banks), read back as 16-byte runs of whole rows (WN / 4
+  // lanes per row) and stored.  With accumulation the main_grad loads of the next fragment row
+  // are in flight while this one is moved.  Fragment element r of lane (h, l32) sits at row
+  // 8 (r / 4) + 4 h + r % 4, column l32 of its 32 x 32 fragment.
+  // Global accesses go through a buffer resource that spans exactly the block's valid rows
+  // (from its first column to the end of its last valid row); lanes past the last column get
+  // an offset beyond that range.  The hardware drops out-of-range stores and returns zeros for
+  // out-of-range loads, so every access is issued unconditionally.
   {
-    constexpr int HR = WM;                 // rows per pass (one wave row)
-    constexpr int PITCH = BN + 8;          // fp32 words per LDS row
-    constexpr int V4_PER_ROW = BN / 4;
-    constexpr int ROWS_PER_IT = NT / V4_PER_ROW;
-    constexpr int ITS = HR / ROWS_PER_IT;  // float4 per thread per pass
-    static_assert(HR * PITCH * 4 <= 2 * S::STAGE, "epilogue LDS block");
-    static_assert(NT % V4_PER_ROW == 0 && HR % ROWS_PER_IT == 0, "epilogue thread map");
-    float* blk = (float*)smem;
-    const int c4 = tid % V4_PER_ROW, r_in = tid / V4_PER_ROW;
+    constexpr int PITCH = WN + 8;  // fp32 words per LDS row
+    constexpr int LPR = WN / 4;    // lanes per row
+    constexpr int RPI = 64 / LPR;  // rows per instruction
+    constexpr int IPF = 32 / RPI;  // instructions per fragment row
+    constexpr int ES = (MODE == kModeFprop && OUT == BSFP8_OUT_BF16) ? 2 : 4;  // output element bytes
+    static_assert(NW * 32 * PITCH * 4 <= 2 * S::STAGE && 64 % LPR == 0, "epilogue buffers");
+    float* buf = (float*)smem + wave * 32 * PITCH;
+    const int c4 = lane % LPR, rl = lane / LPR;
+    const int64_t row0 = a_row0 + wm * WM;  // first row of this wave's block within the group
+    const int64_t col0 = b_row0 + wn * WN;  // first column of the block
+    const int64_t left = (MODE == kModeWgrad ? args.M : (int64_t)gi.k) - row0;
+    const int vrows = left < 0 ? 0 : (left > WM ? WM : (int)left);  // valid rows of the block
+    const int64_t org = (MODE == kModeWgrad ? (int64_t)e * args.M + row0 : gi.off + row0) * args.N + col0;
+    const uint32_t nbytes = vrows > 0 && col0 < args.N ? (uint32_t)(((int64_t)(vrows - 1) * args.N + args.N - col0) * ES) : 0u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((uint8_t*)args.out + org * ES, (short)0, (int)nbytes, 0x00020000);
+    // byte offsets below WM * N * ES < 2^31 (host bound on N); a lane past the last column starts
+    // at 2^31, so all its offsets stay at or above 2^31 > nbytes
+    const uint32_t lane_off = (uint32_t)(rl * args.N + 4 * c4) * ES | (col0 + 4 * c4 < args.N ? 0u : 0x80000000u);
+    const uint32_t row_step = (uint32_t)(RPI * args.N * ES), frag_step = (uint32_t)(32 * args.N * ES);
+    auto off = [&](int i, int it) { return lane_off + (uint32_t)i * frag_step + (uint32_t)it * row_step; };
+    v4f mg[2][IPF];
+    auto load_mg = [&](int i, v4f* m) {
 #pragma unroll
-    for (int pass = 0; pass < S::WAVES_M; ++pass) {
-      if (wm == pass) {
+      for (int it = 0; it < IPF; ++it)
+        m[it] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off(i, it), 0, 0));
+    };
+    if constexpr (MODE == kModeWgrad && ACCUM) load_mg(0, mg[0]);
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-              blk[row * PITCH + wn * WN + j * 32 + l32] = acc[i][j][r];
-            }
+    for (int i = 0; i < FM; ++i) {
+      if constexpr (MODE == kModeWgrad && ACCUM) {
+        if (i + 1 < FM) load_mg(i + 1, mg[(i + 1) & 1]);
       }
-      __syncthreads();
-      const int64_t prow0 = a_row0 + (int64_t)pass * HR;  // first row of this pass in the group
-      const bool col_ok = b_row0 + 4 * c4 < args.N;
-      constexpr int BATCH = ITS < 16 ? ITS : 16;  // rows in flight per thread
 #pragma unroll
-      for (int b0 = 0; b0 < ITS; b0 += BATCH) {
-        float4 v[BATCH];
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int it = 0; it < BATCH; ++it)
-          v[it] = *(const float4*)(blk + (r_in + (b0 + it) * ROWS_PER_IT) * PITCH + 4 * c4);
-        if constexpr (MODE == kModeWgrad) {
-          float* o = (float*)args.out + ((int64_t)e * args.M + prow0) * args.N + b_row0 + 4 * c4;
-          if constexpr (ACCUM) {
-            float4 m[BATCH];
+        for (int r = 0; r < 16; ++r) buf[(8 * (r >> 2) + 4 * h + (r & 3)) * PITCH + j * 32 + l32] = acc[i][j][r];
+      wave_lds_sync();
 #pragma unroll
-            for (int it = 0; it < BATCH; ++it) {
-              const int row = r_in + (b0 + it) * ROWS_PER_IT;
-              if (col_ok && prow0 + row < args.M) m[it] = *(const float4*)(o + (int64_t)row * args.N);
-            }
-#pragma unroll
-            for (int it = 0; it < BATCH; ++it) {
-              const int row = r_in + (b0 + it) * ROWS_PER_IT;
-              if (col_ok && prow0 + row < args.M) {
-                float4 w;
-                w.x = m[it].x + v[it].x;
-                w.y = m[it].y + v[it].y;
-                w.z = m[it].z + v[it].z;
-                w.w = m[it].w + v[it].w;
-                *(float4*)(o + (int64_t)row * args.N) = w;
-              }
-            }
-          } else {
-#pragma unroll
-            for (int it = 0; it < BATCH; ++it) {
-              const int row = r_in + (b0 + it) * ROWS_PER_IT;
-              if (col_ok && prow0 + row < args.M) *(float4*)(o + (int64_t)row * args.N) = v[it];
-            }
-          }
+      for (int it = 0; it < IPF; ++it) {
+        v4f v = *(const v4f*)(buf + (rl + it * RPI) * PITCH + 4 * c4);
+        if constexpr (MODE == kModeWgrad && ACCUM) v = mg[i & 1][it] + v;
+        if constexpr (ES == 4) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rs, (int)off(i, it), 0, 0);
         } else {
-          const int64_t rows_left = gi.k - prow0;
-#pragma unroll
-          for (int it = 0; it < BATCH; ++it) {
-            const int row = r_in + (b0 + it) * ROWS_PER_IT;
-            if (col_ok && row < rows_left) {
-              const int64_t idx = (gi.off + prow0 + row) * args.N + b_row0 + 4 * c4;
-              if constexpr (OUT == BSFP8_OUT_F32) {
-                *(float4*)((float*)args.out + idx) = v[it];
-              } else {
-                uint2 w;
-                w.x = (uint32_t)f32_to_bf16_rne(v[it].x) | ((uint32_t)f32_to_bf16_rne(v[it].y) << 16);
-                w.y = (uint32_t)f32_to_bf16_rne(v[it].z) | ((uint32_t)f32_to_bf16_rne(v[it].w) << 16);
-                *(uint2*)((uint16_t*)args.out + idx) = w;
-              }
-            }
-          }
+          v2i w;
+          w[0] = (int)((uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16));
+          w[1] = (int)((uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16));
+          __builtin_amdgcn_raw_buffer_store_b64(w, rs, (int)off(i, it), 0, 0);
         }
       }
-      __syncthreads();
+      wave_lds_sync();  // every lane has read the buffer before the next fragment row is written
     }
   }
 }
@@ -496,8 +482,8 @@ int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, 
     a.per_xcd = (a.tiles + kXcds - 1) / kXcds;
     if (a.per_xcd * kXcds > 0x7fffffff) return BSFP8_ERR_SHAPE;
     dim3 grid((unsigned)(a.per_xcd * kXcds));
-    return accumulate ? launch<kModeWgrad, false, BM, BN, 128, 128, true, 0>(a, grid, stream)
-                      : launch<kModeWgrad, false, BM, BN, 128, 128, false, 0>(a, grid, stream);
+    return accumulate ? launch<kModeWgrad, false, BM, BN, 128, 64, true, 0>(a, grid, stream)
+                      : launch<kModeWgrad, false, BM, BN, 128, 64, false, 0>(a, grid, stream);
   }
   constexpr int BM = 128, BN = 128;
   a.tiles_m = (int)((n + BM - 1) / BM);

@@ -135,11 +135,13 @@ int bsfp8_grouped_quantize(const void* in_bf16, int64_t capacity_rows, int64_t c
  *   accumulate == 0 : out[e] = dW[e]           (an empty group gets zeros)
  *   accumulate == 1 : out[e] = out[e] + dW[e]  (one fp32 add per element; an empty group's
  *                                               slice is neither read nor written)
- * MX recipe: products use the E8M0 scales inside the MFMA, fp32 accumulation.
+ * MX recipe: every e4m3 value is widened exactly with its E8M0 scale folded in; products
+ *   accumulate in fp32.
  * Per-channel recipe: each 128-row block's unit-scale partial sum p is folded in as
  *   acc = fma(p, sdy_i * sx_j, acc) in block order.
- * n and h must be multiples of 32; capacity_rows + 127 must stay below 2^24 - 128
- * (BSFP8_ERR_SHAPE otherwise): the kernels address an operand tile with 32-bit offsets.
+ * n and h must be multiples of 32, h at most 2^21; capacity_rows + 127 must stay below
+ * 2^24 - 128 (BSFP8_ERR_SHAPE otherwise): the kernels address an operand tile and a 128-row
+ * output block with 32-bit offsets.
  */
 int bsfp8_grouped_gemm_wgrad(const uint8_t* dy_col_q, const void* dy_col_s, int64_t n,
                              const uint8_t* x_col_q, const void* x_col_s, int64_t h,
@@ -157,7 +159,8 @@ int bsfp8_grouped_gemm_wgrad(const uint8_t* dy_col_q, const void* dy_col_s, int6
  * out               [capacity_rows][n], fp32 or bf16 (round to nearest even from fp32):
  *     out[off_e + t][j] = sum_c deq(x)[off_e + t][c] * deq(W_e)[j][c]   for t < k_e
  *   rows at or past sum(k_e) are not written.
- * k and n must be multiples of 32, k below 2^24 - 128.  capacity_rows == 0 returns BSFP8_OK
+ * k and n must be multiples of 32, k below 2^24 - 128, n at most 2^21 (BSFP8_ERR_SHAPE
+ * otherwise).  capacity_rows == 0 returns BSFP8_OK
  * without touching any pointer.
  */
 int bsfp8_grouped_gemm_fprop(const uint8_t* x_row_q, const uint8_t* x_row_s, int64_t capacity_rows,

@@ -107,7 +107,7 @@ def test_quantize_zero_rows_returns_without_touching_pointers():
 @pytest.mark.parametrize("kw,code", [
     (dict(recipe=5), -3), (dict(E=0), -2), (dict(E=2000), -2),
     (dict(n=100), -4), (dict(h=0), -4), (dict(R=-5), -4),
-    (dict(acc=2), -7), (dict(R=(1 << 24)), -4),
+    (dict(acc=2), -7), (dict(R=(1 << 24)), -4), (dict(h=(1 << 21) + 32), -4),
     (dict(splits=None), -1), (dict(out=None), -1), (dict(dyq=None), -1), (dict(xs=None), -1),
     (dict(out=P + 4), -5), (dict(dys=P + 1), -5), (dict(splits=P + 2), -5),
 ])
@@ -117,6 +117,7 @@ def test_wgrad_rejects_before_launch(kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(E=0), -2), (dict(k=48), -4), (dict(n=-32), -4), (dict(dtype=2), -7), (dict(k=1 << 24), -4),
+    (dict(n=(1 << 21) + 32), -4),
     (dict(xq=None), -1), (dict(ws=None), -1), (dict(splits=None), -1), (dict(out=None), -1),
     (dict(out=P + 2), -5), (dict(wq=P + 8), -5),
 ])
