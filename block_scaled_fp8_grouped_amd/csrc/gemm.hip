@@ -17,8 +17,10 @@
 // Per-channel recipe (fp32 scales per 128 rows): unit-scale widening, one partial sum p per
 // 128-row K step, folded as acc = fma(p, sa_i * sb_j, acc) in K order.
 //
-// Tiling.  Workgroup tile BM x BN (256 x 256 for MX, 128 x 128 for the per-channel recipe),
-// K step 128, 4 waves each owning a WM x WN block of 32 x 32 fragments.  Per K step the A and
+// Tiling.  Workgroup tile BM x BN, K step 128, each wave owning a WM x WN block of 32 x 32
+// fragments.  MX recipe: 256 x 256 with 8 waves of 128 x 64 (two waves per SIMD, 128 fp32
+// accumulators each, so one wave's MFMAs run while the other waits on LDS or the barrier);
+// per-channel recipe: 128 x 128 with 4 waves of 64 x 64.  Per K step the A and
 // B tiles (rows of 128 bytes) and their scales are moved straight from HBM into LDS by
 // global_load_lds (16 bytes per lane, no staging registers), double-buffered; the 16-byte
 // chunks of each row are XOR-swizzled so that the fragment reads of consecutive rows spread
@@ -54,6 +56,18 @@ struct GemmArgs {
   int64_t per_xcd;       // launch = 8 * per_xcd workgroups, see xcd_logical()
   void* out;
   uint32_t* status;
+};
+
+// 16 bytes per lane from a buffer resource straight into LDS (lane l -> lds + 16 l); lanes whose
+// offset lies past the resource's range receive zeros.  (A plain __device__ wrapper: the host
+// pass of the kernel templates must not see the builtin.)
+__device__ __forceinline__ void buffer_dma16(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
 };
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -177,33 +191,37 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   // ---------------- loads of one K step, straight into LDS ----------------
   // One DMA instruction moves 64 lanes x 16 bytes = 8 rows x 128 bytes; lane l fills LDS slot
   // l of the region, i.e. row 8g + l/8, swizzled chunk l%8, which holds K chunk (l%8) ^ swz(row).
-  // Rows past the valid ones are clamped to the last valid row.  K chunks at or past kext
-  // (fprop tail only) are fetched from the row start and zeroed in LDS after the wait, so no
-  // byte past a row is ever read.  The row part of a lane's offset is 32-bit from a uniform
-  // tile base (the host bounds 256 * ld below 2^32).
+  // The operand tiles are read through buffer resources that end with the tile's last valid
+  // row: rows past it come back as zeros from the hardware range check (and are never stored),
+  // so no lane needs a clamp.  A K chunk past kext (fprop tail step only) holds bytes of the
+  // next row; the tail step masks it when reading fragments.  Each lane keeps its step-0 offset
+  // in 32 bits (the host bounds 256 * ld + 128 by 2^32) and adds k0.
   const int a_last = (int)(a_valid - 1 - a_row0), b_last = (int)(b_valid - 1 - b_row0);  // >= 0
-  const uint8_t* a_tile = a_data + a_row0 * lda;
-  const uint8_t* b_tile = b_data + b_row0 * ldb;
-  auto dma16 = [&](const void* g, uint8_t* l) {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
-  };
+  const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a_data + a_row0 * lda), (short)0, (int)tile_range(a_valid - a_row0, lda), 0x00020000);
+  const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(b_data + b_row0 * ldb), (short)0, (int)tile_range(b_valid - b_row0, ldb), 0x00020000);
   auto dma4 = [&](const void* g, uint8_t* l) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
   };
-  uint32_t fa_sc = 0;  // fprop: the 4 A-scale bytes this thread stages through registers
+  constexpr int FA_ROWS = 4 * BM / NT;  // fprop: A-scale bytes (rows) each thread stages per K step
+  uint32_t fa_sc = 0;                    // fprop: those bytes, staged through a register
+  uint32_t a_off[S::A_INS], b_off[S::B_INS];
+#pragma unroll
+  for (int u = 0; u < S::A_INS; ++u) a_off[u] = tile_dma_voffset(wave * S::A_INS + u, lane, (uint32_t)lda, 0);
+#pragma unroll
+  for (int u = 0; u < S::B_INS; ++u) b_off[u] = tile_dma_voffset(wave * S::B_INS + u, lane, (uint32_t)ldb, 0);
   auto issue = [&](int kk, uint8_t* __restrict__ base) {
-    const int64_t k0 = (int64_t)kk * BK;
-    // wgrad K extents are multiples of 128: no tail, so the K part is never redirected
-    const int64_t ktail = MODE == kModeFprop ? kext : INT64_MAX;
+    const uint32_t k0 = (uint32_t)kk * BK;
 #pragma unroll
     for (int u = 0; u < S::A_INS; ++u) {
       const int g = wave * S::A_INS + u;
-      dma16(a_tile + tile_dma_offset(g, lane, a_last, lda, k0, ktail), base + S::A_OFF + g * 1024);
+      buffer_dma16(a_rs, base + S::A_OFF + g * 1024, a_off[u] + k0);
     }
 #pragma unroll
     for (int u = 0; u < S::B_INS; ++u) {
       const int g = wave * S::B_INS + u;
-      dma16(b_tile + tile_dma_offset(g, lane, b_last, ldb, k0, ktail), base + S::B_OFF + g * 1024);
+      buffer_dma16(b_rs, base + S::B_OFF + g * 1024, b_off[u] + k0);
     }
     if constexpr (PC) {
       // one fp32 per row: BM + BN dwords, 64 per instruction
@@ -243,37 +261,31 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
         }
       }
       if constexpr (MODE == kModeFprop) {
-        // A scales: thread t -> block t / 64 of this K step, rows 4 * (t % 64) .. + 4
-        static_assert(BM == 256 && NT == 256, "fprop A-scale staging shape");
-        const int blk = tid >> 6;
+        // A scales: thread t -> block t / (NT / 4) of this K step, rows FA_ROWS * (t % (NT / 4))
+        // and the next FA_ROWS - 1
+        static_assert(FA_ROWS == 2 || FA_ROWS == 4, "fprop A-scale staging shape");
+        const int blk = tid / (NT / 4), r0 = FA_ROWS * (tid % (NT / 4));
         const int64_t kb = (int64_t)kk * 4 + blk;
-        uint32_t w = 0x7f7f7f7fu;
+        uint32_t w = FA_ROWS == 4 ? 0x7f7f7f7fu : 0x7f7fu;
         if (kb * 32 < kext) {
+          // the group's scale bytes of this block through a buffer resource spanning its valid
+          // rows: rows past them read as 0 (their products are never stored)
+          const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(a_sc + kb * a_sld + a_row0), (short)0, a_last + 1, 0x00020000);
           w = 0;
-          const uint8_t* src = a_sc + kb * a_sld + a_row0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w |= (uint32_t)src[min(4 * lane + i, a_last)] << (8 * i);
+          for (int i = 0; i < FA_ROWS; ++i) w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, r0 + i, 0, 0) << (8 * i);
         }
         fa_sc = w;
       }
     }
   };
-  // after the DMA has landed: zero K chunks past kext (fprop tail) and place register-staged bytes
-  auto settle = [&](int kk, uint8_t* base) {
+  // after the DMA has landed: place the register-staged A-scale bytes (fprop)
+  auto settle = [&](uint8_t* base) {
     if constexpr (MODE == kModeFprop) {
-      if ((int64_t)(kk + 1) * BK > kext) {
-#pragma unroll
-        for (int u = 0; u < S::A_INS; ++u) {
-          const int g = wave * S::A_INS + u;
-          if (tile_dma_is_tail(g, lane, (int64_t)kk * BK, kext)) *(v4i*)(base + S::A_OFF + g * 1024 + 16 * lane) = v4i{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int u = 0; u < S::B_INS; ++u) {
-          const int g = wave * S::B_INS + u;
-          if (tile_dma_is_tail(g, lane, (int64_t)kk * BK, kext)) *(v4i*)(base + S::B_OFF + g * 1024 + 16 * lane) = v4i{0, 0, 0, 0};
-        }
-      }
-      *(uint32_t*)(base + S::SA_OFF + (tid >> 6) * BM + 4 * lane) = fa_sc;
+      uint8_t* d = base + S::SA_OFF + (tid / (NT / 4)) * BM + FA_ROWS * (tid % (NT / 4));
+      if constexpr (FA_ROWS == 4) *(uint32_t*)d = fa_sc;
+      else *(uint16_t*)d = (uint16_t)fa_sc;
     }
   };
   auto wait_dma = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
@@ -289,7 +301,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   // One K step.  `cur` (read) and `nxt` (DMA target) are distinct LDS stages; passing them as
   // restrict pointers lets the compiler see that the fragment reads of `cur` need not wait for
   // the DMA into `nxt`, so the loads overlap this step's MFMAs.
-  auto step = [&](int kk, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+  auto step = [&](auto tail_tag, int kk, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+    // the fprop step that runs past kext: chunks at or past it read as zeros
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const int64_t k0 = (int64_t)kk * BK;
+    auto chunk = [&](const uint8_t* p, int c) {
+      const v4i v = *(const v4i*)p;
+      if constexpr (TAIL) return k0 + 16 * c < kext ? v : v4i{0, 0, 0, 0};
+      else return v;
+    };
     v16f part[FM][FN];
     if constexpr (PC) {
 #pragma unroll
@@ -307,8 +327,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int row = wm * WM + i * 32 + l32;
-        const v4i lo = *(const v4i*)(cur + S::A_OFF + row * BK + (((4 * s + h) ^ swz(row)) << 4));
-        const v4i hi = *(const v4i*)(cur + S::A_OFF + row * BK + (((4 * s + 2 + h) ^ swz(row)) << 4));
+        const v4i lo = chunk(cur + S::A_OFF + row * BK + (((4 * s + h) ^ swz(row)) << 4), 4 * s + h);
+        const v4i hi = chunk(cur + S::A_OFF + row * BK + (((4 * s + 2 + h) ^ swz(row)) << 4), 4 * s + 2 + h);
         af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         if constexpr (!PC) {
           as[i][0] = e8m0_value(cur[S::SA_OFF + (2 * s) * BM + row]);
@@ -318,8 +338,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int row = wn * WN + j * 32 + l32;
-        const v4i lo = *(const v4i*)(cur + S::B_OFF + row * BK + (((4 * s + h) ^ swz(row)) << 4));
-        const v4i hi = *(const v4i*)(cur + S::B_OFF + row * BK + (((4 * s + 2 + h) ^ swz(row)) << 4));
+        const v4i lo = chunk(cur + S::B_OFF + row * BK + (((4 * s + h) ^ swz(row)) << 4), 4 * s + h);
+        const v4i hi = chunk(cur + S::B_OFF + row * BK + (((4 * s + 2 + h) ^ swz(row)) << 4), 4 * s + 2 + h);
         bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         if constexpr (!PC) {
           bs[j][0] = e8m0_value(cur[S::SB_OFF + (2 * s) * BN + row]);
@@ -366,17 +386,25 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
 
   issue(0, smem);
   wait_dma();
-  settle(0, smem);
+  settle(smem);
   __syncthreads();
-  for (int kk = 0; kk < nk; ++kk) {
+  // fprop K not a multiple of 128: the last step is the tail step
+  const int nfull = MODE == kModeFprop && kext % BK != 0 ? nk - 1 : nk;
+  for (int kk = 0; kk < nfull; ++kk) {
     uint8_t* cur = smem + (kk & 1) * S::STAGE;
     uint8_t* nxt = smem + ((kk & 1) ^ 1) * S::STAGE;
-    step(kk, cur, nxt);
+    step(BoolC<false>(), kk, cur, nxt);
     if (kk + 1 < nk) {
       wait_dma();
-      settle(kk + 1, nxt);
+      settle(nxt);
     }
     __syncthreads();
+  }
+  if constexpr (MODE == kModeFprop) {
+    if (nfull < nk) {  // the tail step (its loads were issued by the step before)
+      step(BoolC<true>(), nfull, smem + (nfull & 1) * S::STAGE, smem + ((nfull & 1) ^ 1) * S::STAGE);
+      __syncthreads();
+    }
   }
 
   // ---------------- epilogue ----------------
@@ -522,8 +550,8 @@ int launch_grouped_gemm_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R,
   if (a.per_xcd * kXcds > 0x7fffffff) return BSFP8_ERR_SHAPE;
   dim3 grid((unsigned)(a.per_xcd * kXcds));
   return out_dtype == BSFP8_OUT_F32
-             ? launch<kModeFprop, false, BM, BN, 128, 128, false, BSFP8_OUT_F32>(a, grid, stream)
-             : launch<kModeFprop, false, BM, BN, 128, 128, false, BSFP8_OUT_BF16>(a, grid, stream);
+             ? launch<kModeFprop, false, BM, BN, 128, 64, false, BSFP8_OUT_F32>(a, grid, stream)
+             : launch<kModeFprop, false, BM, BN, 128, 64, false, BSFP8_OUT_BF16>(a, grid, stream);
 }
 
 }  // namespace bsfp8

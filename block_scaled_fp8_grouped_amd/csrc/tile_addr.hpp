@@ -17,25 +17,27 @@ namespace bsfp8 {
 // one fragment read spreads over the banks) see all eight chunk positions twice.
 BSFP8_HD int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// One 16-byte DMA lane of an operand tile: LDS region g holds tile rows 8g .. 8g + 7; lane
-// `lane` of the instruction fills slot lane (row 8g + lane / 8, swizzled chunk lane % 8).
-// Returns the byte offset of its source, relative to the tile's first row, for K step k0:
-//   row: clamped to `last` (the last valid row of the tile, >= 0);
-//   K  : the chunk's K offset, or 0 (the row start) when the chunk lies at or past kext.
-// Both parts are non-negative; the row part is below 2^32 when 256 * ld < 2^32.
-BSFP8_HD uint64_t tile_dma_offset(int g, int lane, int last, int64_t ld, int64_t k0, int64_t kext) {
-  const int lrow = lane >> 3, lslot = lane & 7;
-  int row = g * 8 + lrow;
-  row = row < last ? row : last;
-  const int64_t kof = k0 + 16 * (lslot ^ ((lrow ^ g) & 7));
-  const uint32_t row_part = (uint32_t)row * (uint32_t)ld;
-  return (uint64_t)row_part + (uint64_t)(kof < kext ? kof : 0);
+// Byte offset, within a 128-byte K step of a row, of the 16-byte chunk that DMA lane `lane` of
+// LDS region g moves: LDS region g holds tile rows 8g .. 8g + 7, and lane `lane` fills slot
+// lane (row 8g + lane / 8, swizzled chunk lane % 8), which holds K chunk (lane % 8) ^ swz(row).
+BSFP8_HD int dma_chunk(int g, int lane) { return 16 * ((lane & 7) ^ (((lane >> 3) ^ g) & 7)); }
+
+// Source offset of that lane for K step k0, relative to the tile's first row (row-major rows of
+// ld bytes).  Rows past the valid ones and chunks past the K extent are not redirected: the
+// kernels read through a buffer resource whose range ends with the tile's last valid row, so
+// the hardware returns zeros past it; a chunk past the K extent of a valid row (fprop tail)
+// holds bytes of the next row and is masked when the fragments are read.  Below 2^32 when
+// 256 * ld + 128 <= 2^32.
+BSFP8_HD uint32_t tile_dma_voffset(int g, int lane, uint32_t ld, uint32_t k0) {
+  return (uint32_t)(g * 8 + (lane >> 3)) * ld + (uint32_t)dma_chunk(g, lane) + k0;
 }
 
-// Whether that lane's chunk is a K tail chunk (zeroed in LDS after the DMA lands).
-BSFP8_HD bool tile_dma_is_tail(int g, int lane, int64_t k0, int64_t kext) {
-  const int lrow = lane >> 3, lslot = lane & 7;
-  return k0 + 16 * (lslot ^ ((lrow ^ g) & 7)) >= kext;
+// Byte range of the buffer resource over an operand tile: `rows` valid rows of ld bytes from
+// the tile's first row, clamped to the 32-bit range field (the tile's own offsets stay below
+// 256 * ld + 128 <= 2^32 - 2^15, so a clamped range cuts off none of them).
+BSFP8_HD uint32_t tile_range(int64_t rows, int64_t ld) {
+  const int64_t b = rows * ld;
+  return b > (int64_t)0xFFFFFFFF ? 0xFFFFFFFFu : (uint32_t)b;
 }
 
 // First row of the four E8M0 scale rows one 4-byte DMA lane moves: rows part*256 + 4*lane ..
