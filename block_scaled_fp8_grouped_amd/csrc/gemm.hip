@@ -53,7 +53,6 @@ struct GemmArgs {
   int E;
   int tiles_m, tiles_n;  // wgrad: per-group tile grid; fprop: tiles_n only
   int64_t tiles;         // logical tiles (fprop: an upper bound; spare ones exit)
-  int64_t per_xcd;       // launch = 8 * per_xcd workgroups, see xcd_logical()
   void* out;
   uint32_t* status;
 };
@@ -110,7 +109,8 @@ struct GemmShape {
   static_assert(2 * STAGE + (int)sizeof(GroupScanSmem<NT>) <= 160 * 1024, "LDS budget");
 };
 
-template <int MODE, bool PC, int BM, int BN, int WM, int WN, bool ACCUM, int OUT>
+// KTAIL (fprop only): K is not a multiple of 128, so the last K step runs past it.
+template <int MODE, bool PC, int BM, int BN, int WM, int WN, bool ACCUM, int OUT, bool KTAIL>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kernel(GemmArgs args) {
   using S = GemmShape<MODE, PC, BM, BN, WM, WN>;
   constexpr int NT = S::NT, NW = S::NW, BK = S::BK, FM = S::FM, FN = S::FN;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   int e, tm, tn;
   // workgroup -> logical tile in the XCD-aware order; workgroup 0 always has tile 0 and is
   // the one that reports the status bits
-  const int64_t L = xcd_logical(blockIdx.x, args.per_xcd);
+  const int64_t L = xcd_logical(blockIdx.x);
   if (L >= args.tiles) return;
   if constexpr (MODE == kModeWgrad) {
     wgrad_tile(L, args.tiles_m, args.tiles_n, &e, &tm, &tn);
@@ -262,9 +262,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
       }
       if constexpr (MODE == kModeFprop) {
         // A scales: thread t -> block t / (NT / 4) of this K step, rows FA_ROWS * (t % (NT / 4))
-        // and the next FA_ROWS - 1
+        // and the next FA_ROWS - 1 (t / (NT / 4) = wave / (NW / 4), t % (NT / 4) = (wave % (NW / 4)) * 64 + lane)
         static_assert(FA_ROWS == 2 || FA_ROWS == 4, "fprop A-scale staging shape");
-        const int blk = tid / (NT / 4), r0 = FA_ROWS * (tid % (NT / 4));
+        // blk from the (scalar) wave index: the buffer resource below must be wave-uniform
+        const int blk = wave / (NW / 4), r0 = FA_ROWS * ((wave % (NW / 4)) * 64 + lane);
         const int64_t kb = (int64_t)kk * 4 + blk;
         uint32_t w = FA_ROWS == 4 ? 0x7f7f7f7fu : 0x7f7fu;
         if (kb * 32 < kext) {
@@ -283,7 +284,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   // after the DMA has landed: place the register-staged A-scale bytes (fprop)
   auto settle = [&](uint8_t* base) {
     if constexpr (MODE == kModeFprop) {
-      uint8_t* d = base + S::SA_OFF + (tid / (NT / 4)) * BM + FA_ROWS * (tid % (NT / 4));
+      uint8_t* d = base + S::SA_OFF + (wave / (NW / 4)) * BM + FA_ROWS * ((wave % (NW / 4)) * 64 + lane);
       if constexpr (FA_ROWS == 4) *(uint32_t*)d = fa_sc;
       else *(uint16_t*)d = (uint16_t)fa_sc;
     }
@@ -389,7 +390,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   settle(smem);
   __syncthreads();
   // fprop K not a multiple of 128: the last step is the tail step
-  const int nfull = MODE == kModeFprop && kext % BK != 0 ? nk - 1 : nk;
+  static_assert(!KTAIL || MODE == kModeFprop, "only fprop has a K tail");
+  const int nfull = KTAIL ? nk - 1 : nk;
   for (int kk = 0; kk < nfull; ++kk) {
     uint8_t* cur = smem + (kk & 1) * S::STAGE;
     uint8_t* nxt = smem + ((kk & 1) ^ 1) * S::STAGE;
@@ -400,11 +402,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
     }
     __syncthreads();
   }
-  if constexpr (MODE == kModeFprop) {
-    if (nfull < nk) {  // the tail step (its loads were issued by the step before)
-      step(BoolC<true>(), nfull, smem + (nfull & 1) * S::STAGE, smem + ((nfull & 1) ^ 1) * S::STAGE);
-      __syncthreads();
-    }
+  if constexpr (KTAIL) {  // the tail step (its loads were issued by the step before)
+    step(BoolC<true>(), nfull, smem + (nfull & 1) * S::STAGE, smem + ((nfull & 1) ^ 1) * S::STAGE);
+    __syncthreads();
   }
 
   // ---------------- epilogue ----------------
@@ -480,10 +480,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
 // Launchers
 // ------------------------------------------------------------------------------------------
 
-template <int MODE, bool PC, int BM, int BN, int WM, int WN, bool ACCUM, int OUT>
+template <int MODE, bool PC, int BM, int BN, int WM, int WN, bool ACCUM, int OUT, bool KTAIL = false>
 static int launch(const GemmArgs& a, dim3 grid, hipStream_t stream) {
   using S = GemmShape<MODE, PC, BM, BN, WM, WN>;
-  hipLaunchKernelGGL((grouped_gemm_kernel<MODE, PC, BM, BN, WM, WN, ACCUM, OUT>), grid, dim3(S::NT), 0, stream, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<MODE, PC, BM, BN, WM, WN, ACCUM, OUT, KTAIL>), grid, dim3(S::NT), 0, stream, a);
   return hipGetLastError() == hipSuccess ? BSFP8_OK : BSFP8_ERR_LAUNCH;
 }
 
@@ -507,9 +507,8 @@ int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, 
     a.tiles_m = (int)((n + BM - 1) / BM);
     a.tiles_n = (int)((h + BN - 1) / BN);
     a.tiles = (int64_t)E * a.tiles_m * a.tiles_n;
-    a.per_xcd = (a.tiles + kXcds - 1) / kXcds;
-    if (a.per_xcd * kXcds > 0x7fffffff) return BSFP8_ERR_SHAPE;
-    dim3 grid((unsigned)(a.per_xcd * kXcds));
+    if (xcd_launch_size(a.tiles) > 0x7fffffff) return BSFP8_ERR_SHAPE;
+    dim3 grid((unsigned)xcd_launch_size(a.tiles));
     return accumulate ? launch<kModeWgrad, false, BM, BN, 128, 64, true, 0>(a, grid, stream)
                       : launch<kModeWgrad, false, BM, BN, 128, 64, false, 0>(a, grid, stream);
   }
@@ -517,9 +516,8 @@ int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, 
   a.tiles_m = (int)((n + BM - 1) / BM);
   a.tiles_n = (int)((h + BN - 1) / BN);
   a.tiles = (int64_t)E * a.tiles_m * a.tiles_n;
-  a.per_xcd = (a.tiles + kXcds - 1) / kXcds;
-  if (a.per_xcd * kXcds > 0x7fffffff) return BSFP8_ERR_SHAPE;
-  dim3 grid((unsigned)(a.per_xcd * kXcds));
+  if (xcd_launch_size(a.tiles) > 0x7fffffff) return BSFP8_ERR_SHAPE;
+  dim3 grid((unsigned)xcd_launch_size(a.tiles));
   return accumulate ? launch<kModeWgrad, true, BM, BN, 64, 64, true, 0>(a, grid, stream)
                     : launch<kModeWgrad, true, BM, BN, 64, 64, false, 0>(a, grid, stream);
 }
@@ -546,9 +544,12 @@ int launch_grouped_gemm_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R,
   const int64_t mt = (R + (int64_t)(BM - 1) * E) / BM;
   if (mt <= 0) return BSFP8_OK;
   a.tiles = (mt + gm - 1) / gm * gm * a.tiles_n;
-  a.per_xcd = (a.tiles + kXcds - 1) / kXcds;
-  if (a.per_xcd * kXcds > 0x7fffffff) return BSFP8_ERR_SHAPE;
-  dim3 grid((unsigned)(a.per_xcd * kXcds));
+  if (xcd_launch_size(a.tiles) > 0x7fffffff) return BSFP8_ERR_SHAPE;
+  dim3 grid((unsigned)xcd_launch_size(a.tiles));
+  if (K % 128 != 0)
+    return out_dtype == BSFP8_OUT_F32
+               ? launch<kModeFprop, false, BM, BN, 128, 64, false, BSFP8_OUT_F32, true>(a, grid, stream)
+               : launch<kModeFprop, false, BM, BN, 128, 64, false, BSFP8_OUT_BF16, true>(a, grid, stream);
   return out_dtype == BSFP8_OUT_F32
              ? launch<kModeFprop, false, BM, BN, 128, 64, false, BSFP8_OUT_F32>(a, grid, stream)
              : launch<kModeFprop, false, BM, BN, 128, 64, false, BSFP8_OUT_BF16>(a, grid, stream);

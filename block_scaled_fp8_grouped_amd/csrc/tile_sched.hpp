@@ -1,10 +1,12 @@
 // Tile order of the grouped GEMMs on MI355X: 8 XCDs of 32 CUs, each XCD with its own L2.
 //
 // The hardware hands workgroup b to XCD b % 8, and each XCD takes its workgroups in increasing
-// b.  xcd_logical() renumbers the launch so that XCD x walks the contiguous logical range
-// [x * per, (x + 1) * per); the logical order then packs tiles that share operand panels into
-// runs of 32 (one per CU of an XCD), so the 32 workgroups running together on one XCD read the
-// same few A and B panels at the same K positions through that XCD's L2.
+// b.  xcd_logical() renumbers the launch so that the logical tiles go to the XCDs in runs of
+// 32 (one per CU of an XCD), run r to XCD r % 8: the 32 workgroups running together on one XCD
+// then read the same few A and B panels at the same K positions through that XCD's L2, and
+// every XCD gets the same share of the tiles (also when the tile count is only an upper bound
+// and the spare tiles at its end exit at once).  The logical order packs tiles that share
+// operand panels into those runs:
 //   wgrad: per group, blocks of `gn` tile columns; inside a block, tile rows then columns
 //          (TM x gn tiles with gn = 32 / TM share all A panels and gn B panels).
 //   fprop: runs of `gm` m-tiles (rows of one group's tokens) times all TN weight tiles.
@@ -20,8 +22,18 @@ namespace bsfp8 {
 constexpr int kXcds = 8;
 constexpr int kCusPerXcd = 32;
 
-// Logical tile of workgroup b in a launch of 8 * per workgroups.
-BSFP8_HD int64_t xcd_logical(int64_t b, int64_t per) { return (b % kXcds) * per + b / kXcds; }
+// Launch size for `tiles` logical tiles: a whole number of rounds of 8 runs of 32.
+BSFP8_HD int64_t xcd_launch_size(int64_t tiles) {
+  const int64_t round = (int64_t)kXcds * kCusPerXcd;
+  return (tiles + round - 1) / round * round;
+}
+
+// Logical tile of workgroup b (launch of xcd_launch_size() workgroups): XCD b % 8 takes its
+// j-th workgroup (j = b / 8) from run (j / 32) * 8 + b % 8, position j % 32.
+BSFP8_HD int64_t xcd_logical(int64_t b) {
+  const int64_t x = b % kXcds, j = b / kXcds;
+  return ((j / kCusPerXcd) * kXcds + x) * kCusPerXcd + j % kCusPerXcd;
+}
 
 // Columns per block of the wgrad order for a TM-row tile grid.
 BSFP8_HD int wgrad_block_cols(int tm_count) {

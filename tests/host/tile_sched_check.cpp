@@ -1,6 +1,8 @@
 // Host check of the XCD-aware tile order (csrc/tile_sched.hpp), run by tests/test_tile_addr.py:
-// over a launch of 8 * per workgroups every tile is produced exactly once, spare workgroups map
-// past the tile count, workgroup 0 gets tile 0, and each XCD walks a contiguous logical range.
+// over a launch of xcd_launch_size() workgroups every tile is produced exactly once, spare
+// workgroups map past the tile count, workgroup 0 gets tile 0, each XCD walks whole runs of 32
+// consecutive logical tiles in increasing order, and the XCDs' shares of the real tiles differ
+// by at most one run.
 #include <cstdint>
 #include <cstdio>
 #include <vector>
@@ -12,12 +14,12 @@ using namespace bsfp8;
 static long g_fail = 0;
 
 static void check_wgrad(int E, int TM, int TN) {
-  const int64_t G = (int64_t)E * TM * TN, per = (G + kXcds - 1) / kXcds;
+  const int64_t G = (int64_t)E * TM * TN, B = xcd_launch_size(G);
   std::vector<int> seen((size_t)G, 0);
-  for (int64_t b = 0; b < per * kXcds; ++b) {
-    const int64_t L = xcd_logical(b, per);
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t L = xcd_logical(b);
     if (b == 0 && L != 0) ++g_fail;
-    if (L < 0 || L >= per * kXcds) { ++g_fail; continue; }
+    if (L < 0 || L >= B) { ++g_fail; continue; }
     if (L >= G) continue;
     int e, tm, tn;
     wgrad_tile(L, TM, TN, &e, &tm, &tn);
@@ -33,11 +35,11 @@ static void check_wgrad(int E, int TM, int TN) {
 
 static void check_fprop(int64_t MT, int TN) {
   const int64_t gm = fprop_run_mtiles(TN);
-  const int64_t G = (MT + gm - 1) / gm * gm * TN, per = (G + kXcds - 1) / kXcds;
+  const int64_t G = (MT + gm - 1) / gm * gm * TN, B = xcd_launch_size(G);
   const int64_t mt_cap = (MT + gm - 1) / gm * gm;
   std::vector<int> seen((size_t)(mt_cap * TN), 0);
-  for (int64_t b = 0; b < per * kXcds; ++b) {
-    const int64_t L = xcd_logical(b, per);
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t L = xcd_logical(b);
     if (L >= G) continue;
     int64_t mt;
     int tn;
@@ -53,15 +55,29 @@ static void check_fprop(int64_t MT, int TN) {
 }
 
 int main() {
-  // xcd_logical is a bijection of [0, 8 per) and XCD x walks [x per, (x + 1) per) in order
-  for (int64_t per : {1, 3, 7, 100, 3417}) {
-    std::vector<int> seen((size_t)(per * kXcds), 0);
-    for (int64_t b = 0; b < per * kXcds; ++b) {
-      const int64_t L = xcd_logical(b, per);
+  // xcd_logical is a bijection of [0, B); XCD x takes runs x, x + 8, ... in order; for any
+  // tile count the real tiles per XCD differ by at most one run
+  for (int64_t tiles : {1, 31, 32, 255, 256, 257, 1000, 27328, 33792}) {
+    const int64_t B = xcd_launch_size(tiles);
+    if (B % 256 != 0 || B < tiles || B - tiles >= 256) ++g_fail;
+    std::vector<int> seen((size_t)B, 0);
+    std::vector<int64_t> real(kXcds, 0), prev(kXcds, -1);
+    for (int64_t b = 0; b < B; ++b) {
+      const int64_t L = xcd_logical(b);
+      if (L < 0 || L >= B) { ++g_fail; continue; }
       seen[(size_t)L]++;
-      if (L != (b % kXcds) * per + b / kXcds) ++g_fail;
+      const int x = (int)(b % kXcds);
+      if ((L / kCusPerXcd) % kXcds != x) ++g_fail;  // run r belongs to XCD r % 8
+      if (L <= prev[x]) ++g_fail;                     // each XCD walks increasing tiles
+      prev[x] = L;
+      if (L < tiles) real[x]++;
     }
     for (int v : seen) if (v != 1) ++g_fail;
+    int64_t lo = real[0], hi = real[0];
+    for (int64_t r : real) { lo = r < lo ? r : lo; hi = r > hi ? r : hi; }
+    if (hi - lo > kCusPerXcd) {
+      if (g_fail++ < 10) std::printf("tiles=%lld: XCD shares %lld..%lld\n", (long long)tiles, (long long)lo, (long long)hi);
+    }
   }
   const int dims[][3] = {{1, 1, 1}, {4, 1, 1}, {4, 8, 8}, {1, 4, 4}, {128, 8, 28}, {32, 6, 16}, {5, 2, 3},
                          {7, 1, 3}, {1024, 1, 1}, {3, 40, 2}, {2, 33, 33}};
