@@ -2,8 +2,10 @@
 // scales (DeepGEMM #365 reproducer: per-channel cast and K-major pack; TE #3484: MXFP8 block
 // scaling over a padded token buffer; TE PR #3224: columnwise scales strided per group member).
 //
-// One workgroup (4 waves) owns a tile of 128 rows of one group x 128 channels.  The tile is
-// read once from HBM (16-byte loads, 256 contiguous bytes per row) into LDS; then
+// One workgroup (4 waves) walks 8 consecutive 128-row tiles of one 128-channel column: the
+// split sizes are scanned once for the first tile and later tiles step forward through the
+// groups; each tile is read once from HBM (16-byte loads, 256 contiguous bytes per row) into
+// registers while the previous tile is being quantized, then staged in LDS; then
 //   colwise: wave w takes tokens [32w, 32w + 32) of the tile and lane l the channel pair
 //            (2l, 2l+1): one LDS dword per token, conflict-free, the block amax, the scale and
 //            32 codes per channel, written as 32 contiguous bytes of the channel's K-major run;
@@ -19,6 +21,15 @@ namespace bsfp8 {
 constexpr int kQThreads = 256;
 constexpr int kQRows = 128;
 constexpr int kQCols = 128;
+constexpr int kQTilesPerWG = 8;  // consecutive 128-row tiles one workgroup walks
+
+// Where one 128-row tile of the token buffer lives.
+struct QTile {
+  int64_t row0;  // first token row
+  int64_t jblk;  // 128-row block index inside its group
+  int64_t p, kp; // the group's packed offset and padded length (colwise layout)
+  int nlive;     // live rows of the tile (<= 128)
+};
 
 template <int RECIPE, bool ROW, bool COL>
 __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
@@ -32,132 +43,167 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-
-  int64_t row0, P = 0, kp = 0, jblk = 0;
-  int nlive;
-  if (splits != nullptr) {
-    GroupInfo gi;
-    const uint32_t flags = group_scan<kQThreads>(splits, E, R, kQRows, blockIdx.x, 0, gsm, gi);
-    report_status(status, flags);
-    if (gi.e < 0) return;
-    jblk = (int64_t)blockIdx.x - gi.tile;  // 128-row block index inside the group
-    row0 = gi.off + kQRows * jblk;
-    const int64_t left = gi.k - kQRows * jblk;
-    nlive = (int)(left < kQRows ? left : kQRows);
-    P = gi.p;
-    kp = gi.kp;
-  } else {
-    row0 = (int64_t)blockIdx.x * kQRows;
-    if (row0 >= R) return;
-    const int64_t left = R - row0;
-    nlive = (int)(left < kQRows ? left : kQRows);
-  }
-  const int64_t c0 = (int64_t)blockIdx.y * kQCols;
+  // workgroup -> (run of kQTilesPerWG row tiles, 128-channel tile), channel tiles fastest: the
+  // workgroups in flight together read neighbouring pieces of the same rows
+  const int64_t ctiles = (C + kQCols - 1) / kQCols;
+  const int64_t rt0 = (int64_t)blockIdx.x / ctiles * kQTilesPerWG, ctile = (int64_t)blockIdx.x % ctiles;
+  const int64_t c0 = ctile * kQCols;
   const int ncols = (int)((C - c0) < kQCols ? (C - c0) : kQCols);  // a multiple of 32
 
-  // ---- load the tile: 16 lanes per row, 8 channels (16 bytes) each ----
-#pragma unroll
-  for (int pass = 0; pass < kQRows / 16; ++pass) {
-    const int r = pass * 16 + (tid >> 4);
-    const int ch = tid & 15;
-    v4i v = {0, 0, 0, 0};
-    if (r < nlive && ch * 8 < ncols) v = *(const v4i*)(in + (row0 + r) * C + c0 + ch * 8);
-    *(v4i*)&tile[r][ch * 4] = v;
+  // group of the run's first tile from the scan of the split sizes; later tiles walk forward
+  GroupInfo g{};
+  if (splits != nullptr) {
+    const uint32_t flags = group_scan<kQThreads>(splits, E, R, kQRows, rt0, 0, gsm, g);
+    report_status(status, flags);
+    if (g.e < 0) return;
   }
-  __syncthreads();
+  auto place = [&](int64_t rt, QTile& q) -> bool {
+    if (splits == nullptr) {
+      q.row0 = rt * kQRows;
+      if (q.row0 >= R) return false;
+      q.nlive = (int)(R - q.row0 < kQRows ? R - q.row0 : kQRows);
+      q.jblk = q.p = q.kp = 0;
+      return true;
+    }
+    while (rt >= g.tile + (g.k + kQRows - 1) / kQRows) {  // past this group (or it is empty)
+      g.tile += (g.k + kQRows - 1) / kQRows;
+      g.off += g.k;
+      g.p += g.kp;
+      if (++g.e >= E) return false;
+      g.k = splits[g.e];  // validated by the scan: 0 <= k, sum <= capacity
+      g.kp = (g.k + 127) / 128 * 128;
+    }
+    q.jblk = rt - g.tile;
+    q.row0 = g.off + kQRows * q.jblk;
+    const int64_t left = g.k - kQRows * q.jblk;
+    q.nlive = (int)(left < kQRows ? left : kQRows);
+    q.p = g.p;
+    q.kp = g.kp;
+    return true;
+  };
 
-  if constexpr (COL) {
-    // ---- colwise: wave -> 32 tokens, lane -> channel pair ----
-    const int c = 2 * lane;
-    uint32_t w[32];
-    uint32_t m0 = 0, m1 = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      w[i] = tile[wave * 32 + i][lane];
-      m0 = max(m0, w[i] & 0x7fffu);
-      m1 = max(m1, (w[i] >> 16) & 0x7fffu);
-    }
-    float s0, s1;
-    uint32_t sbits = 0;
-    if constexpr (RECIPE == BSFP8_RECIPE_MX_1X32_E8M0) {
-      const int e0 = e8m0_exponent(__uint_as_float(m0 << 16));
-      const int e1 = e8m0_exponent(__uint_as_float(m1 << 16));
-      s0 = exp2_neg(e0);
-      s1 = exp2_neg(e1);
-      sbits = (uint32_t)(e0 + 127) | ((uint32_t)(e1 + 127) << 8);
-    } else {
-      pc_amax[wave][c] = __uint_as_float(m0 << 16);
-      pc_amax[wave][c + 1] = __uint_as_float(m1 << 16);
-      __syncthreads();
-      float a0 = pc_amax[0][c], a1 = pc_amax[0][c + 1];
-#pragma unroll
-      for (int q = 1; q < 4; ++q) {
-        a0 = fmaxf(a0, pc_amax[q][c]);
-        a1 = fmaxf(a1, pc_amax[q][c + 1]);
-      }
-      float sf0 = a0 / 448.0f, sf1 = a1 / 448.0f;
-      if (sf0 == 0.0f) sf0 = zero_amax_scale;
-      if (sf1 == 0.0f) sf1 = zero_amax_scale;
-      if (sf0 < 1e-30f) sf0 = 1e-30f;
-      if (sf1 < 1e-30f) sf1 = 1e-30f;
-      s0 = 1.0f / sf0;
-      s1 = 1.0f / sf1;
-      if (wave == 0 && c0 + c < C) {
-        float2 sv;
-        sv.x = sf0;
-        sv.y = sf1;
-        *(float2*)((float*)col_s + C * P / 128 + jblk * C + c0 + c) = sv;
-      }
-    }
-    v4i q0[2], q1[2];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t lo = e4m3x4(bf16_lo(w[4 * i]) * s0, bf16_lo(w[4 * i + 1]) * s0, bf16_lo(w[4 * i + 2]) * s0,
-                                 bf16_lo(w[4 * i + 3]) * s0);
-      const uint32_t hi = e4m3x4(bf16_hi(w[4 * i]) * s1, bf16_hi(w[4 * i + 1]) * s1, bf16_hi(w[4 * i + 2]) * s1,
-                                 bf16_hi(w[4 * i + 3]) * s1);
-      q0[i >> 2][i & 3] = (int)lo;
-      q1[i >> 2][i & 3] = (int)hi;
-    }
-    if (c0 + c < C) {
-      uint8_t* dst = col_q + C * P + (c0 + c) * kp + kQRows * jblk + 32 * wave;
-      *(v4i*)dst = q0[0];
-      *(v4i*)(dst + 16) = q0[1];
-      *(v4i*)(dst + kp) = q1[0];
-      *(v4i*)(dst + kp + 16) = q1[1];
-      if constexpr (RECIPE == BSFP8_RECIPE_MX_1X32_E8M0) {
-        *(uint16_t*)((uint8_t*)col_s + C * P / 32 + (4 * jblk + wave) * C + c0 + c) = (uint16_t)sbits;
-      }
-    }
-  }
-
-  if constexpr (ROW) {
-    // ---- rowwise: 16 lanes per row (8 channels each), 4 lanes per 32-channel block ----
+  // this thread's share of a tile: 16 lanes per row, 8 channels (16 bytes) each
+  v4i pre[kQRows / 16];
+  auto load_tile = [&](const QTile& q) {
 #pragma unroll
     for (int pass = 0; pass < kQRows / 16; ++pass) {
       const int r = pass * 16 + (tid >> 4);
       const int ch = tid & 15;
-      const v4i v = *(const v4i*)&tile[r][ch * 4];
-      uint32_t m = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m = max(m, max((uint32_t)v[i] & 0x7fffu, ((uint32_t)v[i] >> 16) & 0x7fffu));
-      m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
-      m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
-      const int e = e8m0_exponent(__uint_as_float(m << 16));
-      const float s = exp2_neg(e);
-      v2i q;
-      q[0] = (int)e4m3x4(bf16_lo(v[0]) * s, bf16_hi(v[0]) * s, bf16_lo(v[1]) * s, bf16_hi(v[1]) * s);
-      q[1] = (int)e4m3x4(bf16_lo(v[2]) * s, bf16_hi(v[2]) * s, bf16_lo(v[3]) * s, bf16_hi(v[3]) * s);
-      if (r < nlive && ch * 8 < ncols) *(v2i*)(row_q + (row0 + r) * C + c0 + ch * 8) = q;
-      if ((ch & 3) == 0) rs_tile[ch >> 2][r] = (uint8_t)(e + 127);
+      pre[pass] = v4i{0, 0, 0, 0};
+      if (r < q.nlive && ch * 8 < ncols) pre[pass] = *(const v4i*)(in + (q.row0 + r) * C + c0 + ch * 8);
     }
+  };
+
+  QTile cur;
+  if (!place(rt0, cur)) return;
+  load_tile(cur);
+  for (int t = 0; t < kQTilesPerWG; ++t) {
+#pragma unroll
+    for (int pass = 0; pass < kQRows / 16; ++pass) *(v4i*)&tile[pass * 16 + (tid >> 4)][(tid & 15) * 4] = pre[pass];
     __syncthreads();
+    // the next tile's loads are in flight while this one is quantized
+    QTile nxt;
+    const bool more = t + 1 < kQTilesPerWG && place(rt0 + t + 1, nxt);
+    if (more) load_tile(nxt);
+    const int64_t row0 = cur.row0, P = cur.p, kp = cur.kp, jblk = cur.jblk;
+    const int nlive = cur.nlive;
+
+    if constexpr (COL) {
+      // ---- colwise: wave -> 32 tokens, lane -> channel pair ----
+      const int c = 2 * lane;
+      uint32_t w[32];
+      uint32_t m0 = 0, m1 = 0;
 #pragma unroll
-    for (int i = 0; i < (kQCols / 32) * kQRows / kQThreads; ++i) {
-      const int idx = tid + i * kQThreads;
-      const int b = idx / kQRows, r = idx % kQRows;
-      if (r < nlive && b * 32 < ncols) row_s[(c0 / 32 + b) * R + row0 + r] = rs_tile[b][r];
+      for (int i = 0; i < 32; ++i) {
+        w[i] = tile[wave * 32 + i][lane];
+        m0 = max(m0, w[i] & 0x7fffu);
+        m1 = max(m1, (w[i] >> 16) & 0x7fffu);
+      }
+      float s0, s1;
+      uint32_t sbits = 0;
+      if constexpr (RECIPE == BSFP8_RECIPE_MX_1X32_E8M0) {
+        const int e0 = e8m0_exponent(__uint_as_float(m0 << 16));
+        const int e1 = e8m0_exponent(__uint_as_float(m1 << 16));
+        s0 = exp2_neg(e0);
+        s1 = exp2_neg(e1);
+        sbits = (uint32_t)(e0 + 127) | ((uint32_t)(e1 + 127) << 8);
+      } else {
+        pc_amax[wave][c] = __uint_as_float(m0 << 16);
+        pc_amax[wave][c + 1] = __uint_as_float(m1 << 16);
+        __syncthreads();
+        float a0 = pc_amax[0][c], a1 = pc_amax[0][c + 1];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) {
+          a0 = fmaxf(a0, pc_amax[q][c]);
+          a1 = fmaxf(a1, pc_amax[q][c + 1]);
+        }
+        float sf0 = a0 / 448.0f, sf1 = a1 / 448.0f;
+        if (sf0 == 0.0f) sf0 = zero_amax_scale;
+        if (sf1 == 0.0f) sf1 = zero_amax_scale;
+        if (sf0 < 1e-30f) sf0 = 1e-30f;
+        if (sf1 < 1e-30f) sf1 = 1e-30f;
+        s0 = 1.0f / sf0;
+        s1 = 1.0f / sf1;
+        if (wave == 0 && c0 + c < C) {
+          float2 sv;
+          sv.x = sf0;
+          sv.y = sf1;
+          *(float2*)((float*)col_s + C * P / 128 + jblk * C + c0 + c) = sv;
+        }
+      }
+      v4i q0[2], q1[2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = e4m3x4(bf16_lo(w[4 * i]) * s0, bf16_lo(w[4 * i + 1]) * s0, bf16_lo(w[4 * i + 2]) * s0,
+                                   bf16_lo(w[4 * i + 3]) * s0);
+        const uint32_t hi = e4m3x4(bf16_hi(w[4 * i]) * s1, bf16_hi(w[4 * i + 1]) * s1, bf16_hi(w[4 * i + 2]) * s1,
+                                   bf16_hi(w[4 * i + 3]) * s1);
+        q0[i >> 2][i & 3] = (int)lo;
+        q1[i >> 2][i & 3] = (int)hi;
+      }
+      if (c0 + c < C) {
+        uint8_t* dst = col_q + C * P + (c0 + c) * kp + kQRows * jblk + 32 * wave;
+        *(v4i*)dst = q0[0];
+        *(v4i*)(dst + 16) = q0[1];
+        *(v4i*)(dst + kp) = q1[0];
+        *(v4i*)(dst + kp + 16) = q1[1];
+        if constexpr (RECIPE == BSFP8_RECIPE_MX_1X32_E8M0) {
+          *(uint16_t*)((uint8_t*)col_s + C * P / 32 + (4 * jblk + wave) * C + c0 + c) = (uint16_t)sbits;
+        }
+      }
     }
+
+    if constexpr (ROW) {
+      // ---- rowwise: 16 lanes per row (8 channels each), 4 lanes per 32-channel block ----
+#pragma unroll
+      for (int pass = 0; pass < kQRows / 16; ++pass) {
+        const int r = pass * 16 + (tid >> 4);
+        const int ch = tid & 15;
+        const v4i v = *(const v4i*)&tile[r][ch * 4];
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = max(m, max((uint32_t)v[i] & 0x7fffu, ((uint32_t)v[i] >> 16) & 0x7fffu));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+        const int e = e8m0_exponent(__uint_as_float(m << 16));
+        const float s = exp2_neg(e);
+        v2i q;
+        q[0] = (int)e4m3x4(bf16_lo(v[0]) * s, bf16_hi(v[0]) * s, bf16_lo(v[1]) * s, bf16_hi(v[1]) * s);
+        q[1] = (int)e4m3x4(bf16_lo(v[2]) * s, bf16_hi(v[2]) * s, bf16_lo(v[3]) * s, bf16_hi(v[3]) * s);
+        if (r < nlive && ch * 8 < ncols) *(v2i*)(row_q + (row0 + r) * C + c0 + ch * 8) = q;
+        if ((ch & 3) == 0) rs_tile[ch >> 2][r] = (uint8_t)(e + 127);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < (kQCols / 32) * kQRows / kQThreads; ++i) {
+        const int idx = tid + i * kQThreads;
+        const int b = idx / kQRows, r = idx % kQRows;
+        if (r < nlive && b * 32 < ncols) row_s[(c0 / 32 + b) * R + row0 + r] = rs_tile[b][r];
+      }
+    }
+    __syncthreads();  // the LDS tile and row scales are free for the next tile
+    if (!more) break;
+    cur = nxt;
   }
 }
 
@@ -170,11 +216,11 @@ static inline int64_t quantize_row_tiles(int64_t R, int E, bool grouped) {
 int launch_grouped_quantize(const void* in, int64_t R, int64_t C, const int32_t* splits, int E, int recipe,
                             int which, float zas, uint8_t* row_q, uint8_t* row_s, uint8_t* col_q, void* col_s,
                             uint32_t* status, hipStream_t stream) {
-  const int64_t gx = quantize_row_tiles(R, E, splits != nullptr);
+  const int64_t gx = (quantize_row_tiles(R, E, splits != nullptr) + kQTilesPerWG - 1) / kQTilesPerWG;
   const int64_t gy = (C + kQCols - 1) / kQCols;
   if (gx <= 0 || gy <= 0) return BSFP8_OK;
-  if (gx > 0x7fffffff || gy > 65535) return BSFP8_ERR_SHAPE;
-  dim3 grid((unsigned)gx, (unsigned)gy), block(kQThreads);
+  if (gx * gy > 0x7fffffff) return BSFP8_ERR_SHAPE;
+  dim3 grid((unsigned)(gx * gy)), block(kQThreads);
   const uint16_t* x = (const uint16_t*)in;
   const bool row = (which & BSFP8_ROWWISE) != 0, col = (which & BSFP8_COLWISE) != 0;
   if (recipe == BSFP8_RECIPE_MX_1X32_E8M0) {
