@@ -205,7 +205,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
   };
   constexpr int FA_ROWS = 4 * BM / NT;  // fprop: A-scale bytes (rows) each thread stages per K step
-  uint32_t fa_sc = 0;                    // fprop: those bytes, staged through a register
+  uint8_t fa_b[FA_ROWS];                 // fprop: those bytes, held in registers until settle
   uint32_t a_off[S::A_INS], b_off[S::B_INS];
 #pragma unroll
   for (int u = 0; u < S::A_INS; ++u) a_off[u] = tile_dma_voffset(wave * S::A_INS + u, lane, (uint32_t)lda, 0);
@@ -213,6 +213,27 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   for (int u = 0; u < S::B_INS; ++u) b_off[u] = tile_dma_voffset(wave * S::B_INS + u, lane, (uint32_t)ldb, 0);
   auto issue = [&](int kk, uint8_t* __restrict__ base) {
     const uint32_t k0 = (uint32_t)kk * BK;
+    if constexpr (MODE == kModeFprop) {
+      // A scales first: waiting for these register loads (in settle) then does not wait for
+      // the DMAs behind them.  Thread t -> block t / (NT / 4) of this K step, rows
+      // FA_ROWS * (t % (NT / 4)) and the next FA_ROWS - 1 (t / (NT / 4) = wave / (NW / 4),
+      // t % (NT / 4) = (wave % (NW / 4)) * 64 + lane: the block index comes from the scalar wave
+      // index, so the buffer resource below is wave-uniform).
+      static_assert(FA_ROWS == 2 || FA_ROWS == 4, "fprop A-scale staging shape");
+      const int blk = wave / (NW / 4), r0 = FA_ROWS * ((wave % (NW / 4)) * 64 + lane);
+      const int64_t kb = (int64_t)kk * 4 + blk;
+      if (kb * 32 < kext) {
+        // the group's scale bytes of this block through a buffer resource spanning its valid
+        // rows: rows past them read as 0 (their products are never stored)
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a_sc + kb * a_sld + a_row0), (short)0, a_last + 1, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < FA_ROWS; ++i) fa_b[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, r0 + i, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < FA_ROWS; ++i) fa_b[i] = 0x7f;  // past K: unit scales over zero data
+      }
+    }
 #pragma unroll
     for (int u = 0; u < S::A_INS; ++u) {
       const int g = wave * S::A_INS + u;
@@ -260,33 +281,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
           dma4((is_a ? a_sc + a_row0 : b_sc + b_row0) + kb * (is_a ? a_sld : b_sld) + r4, dst);
         }
       }
-      if constexpr (MODE == kModeFprop) {
-        // A scales: thread t -> block t / (NT / 4) of this K step, rows FA_ROWS * (t % (NT / 4))
-        // and the next FA_ROWS - 1 (t / (NT / 4) = wave / (NW / 4), t % (NT / 4) = (wave % (NW / 4)) * 64 + lane)
-        static_assert(FA_ROWS == 2 || FA_ROWS == 4, "fprop A-scale staging shape");
-        // blk from the (scalar) wave index: the buffer resource below must be wave-uniform
-        const int blk = wave / (NW / 4), r0 = FA_ROWS * ((wave % (NW / 4)) * 64 + lane);
-        const int64_t kb = (int64_t)kk * 4 + blk;
-        uint32_t w = FA_ROWS == 4 ? 0x7f7f7f7fu : 0x7f7fu;
-        if (kb * 32 < kext) {
-          // the group's scale bytes of this block through a buffer resource spanning its valid
-          // rows: rows past them read as 0 (their products are never stored)
-          const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-              (void*)(a_sc + kb * a_sld + a_row0), (short)0, a_last + 1, 0x00020000);
-          w = 0;
-#pragma unroll
-          for (int i = 0; i < FA_ROWS; ++i) w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, r0 + i, 0, 0) << (8 * i);
-        }
-        fa_sc = w;
-      }
     }
   };
   // after the DMA has landed: place the register-staged A-scale bytes (fprop)
   auto settle = [&](uint8_t* base) {
     if constexpr (MODE == kModeFprop) {
       uint8_t* d = base + S::SA_OFF + (wave / (NW / 4)) * BM + FA_ROWS * ((wave % (NW / 4)) * 64 + lane);
-      if constexpr (FA_ROWS == 4) *(uint32_t*)d = fa_sc;
-      else *(uint16_t*)d = (uint16_t)fa_sc;
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < FA_ROWS; ++i) w |= (uint32_t)fa_b[i] << (8 * i);
+      if constexpr (FA_ROWS == 4) *(uint32_t*)d = w;
+      else *(uint16_t*)d = (uint16_t)w;
     }
   };
   auto wait_dma = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
