@@ -180,6 +180,8 @@ def main():
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())}")
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # GPU-side span of the timed steps (first kernel start to last kernel end), per step
+    event_ms_per_step = events[0][0].elapsed_time(events[-1][5]) / args.steps
     leg_ms = {name: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps for i, name in enumerate(legs)}
 
     wgrad_flop = 2.0 * n * h * T
@@ -224,6 +226,7 @@ def main():
             "kernel": "grouped_gemm_kernel<wgrad, MX, 256x256, accumulate>",
             "frac_of_fp8_peak": round(achieved / PEAK_FP8_MFMA_TFLOPS, 4),
         },
+        "event_ms_per_step": round(event_ms_per_step, 3),
         "legs": {
             "quantize_x": {"ms": round(leg_ms["quantize_x"], 3),
                            "GB/s": round(bytes_x / (leg_ms["quantize_x"] / 1e3) / 1e9, 1)},
