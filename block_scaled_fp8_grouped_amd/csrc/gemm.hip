@@ -100,9 +100,11 @@ struct GemmShape {
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int NW = WAVES_M * WAVES_N, NT = NW * 64;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  // LDS stage: A rows, B rows, then scales (MX: [4 blocks][rows] bytes; PC: one fp32 per row)
+  // LDS stage: A rows, B rows, then scales (MX: [4 blocks][rows] E8M0 bytes as they arrive, and
+  // the same decoded to fp32 [4 blocks][rows]; PC: one fp32 per row)
   static constexpr int A_OFF = 0, B_OFF = BM * BK, SA_OFF = (BM + BN) * BK, SB_OFF = SA_OFF + BM * 4;
-  static constexpr int STAGE = SB_OFF + BN * 4;
+  static constexpr int SAF_OFF = SB_OFF + BN * 4, SBF_OFF = SAF_OFF + 16 * BM;
+  static constexpr int STAGE = PC ? SB_OFF + BN * 4 : SBF_OFF + 16 * BN;
   static constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;  // 1 KB DMA instructions per wave
   static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
   static_assert(A_INS * 8 * NW == BM && B_INS * 8 * NW == BN, "DMA loader shape");
@@ -283,15 +285,32 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
       }
     }
   };
-  // after the DMA has landed: place the register-staged A-scale bytes (fprop)
+  // After the DMA has landed: decode the step's E8M0 scales once into the stage's fp32 area, so
+  // the fragment reads take fp32 scales with no per-read decode.  Each wave decodes the 256
+  // bytes its own scale DMA (or tail store) wrote -- visible to it after its own wait -- and the
+  // fprop A scales come from the register-staged bytes.
   auto settle = [&](uint8_t* base) {
-    if constexpr (MODE == kModeFprop) {
-      uint8_t* d = base + S::SA_OFF + (wave / (NW / 4)) * BM + FA_ROWS * ((wave % (NW / 4)) * 64 + lane);
-      uint32_t w = 0;
+    if constexpr (!PC) {
+      constexpr int SA_INS = 4 * BM / 256, SB_INS = 4 * BN / 256, PER = (SA_INS + SB_INS) / NW;
 #pragma unroll
-      for (int i = 0; i < FA_ROWS; ++i) w |= (uint32_t)fa_b[i] << (8 * i);
-      if constexpr (FA_ROWS == 4) *(uint32_t*)d = w;
-      else *(uint16_t*)d = (uint16_t)w;
+      for (int u = 0; u < PER; ++u) {
+        const int v = wave * PER + u;
+        const bool is_a = v < SA_INS;
+        if (MODE == kModeFprop && is_a) continue;
+        const int vv = is_a ? v : v - SA_INS;
+        const int per = (is_a ? BM : BN) / 256;
+        const int blk = vv / per, part = vv % per;
+        const int idx = (is_a ? blk * BM : blk * BN) + part * 256 + 4 * lane;  // first of 4 rows
+        const uint32_t w4 = *(const uint32_t*)(base + (is_a ? S::SA_OFF : S::SB_OFF) + idx);
+        float* f = (float*)(base + (is_a ? S::SAF_OFF : S::SBF_OFF)) + idx;
+        *(v4f*)f = v4f{e8m0_value(w4 & 0xffu), e8m0_value((w4 >> 8) & 0xffu), e8m0_value((w4 >> 16) & 0xffu),
+                       e8m0_value(w4 >> 24)};
+      }
+      if constexpr (MODE == kModeFprop) {
+        float* f = (float*)(base + S::SAF_OFF) + (wave / (NW / 4)) * BM + FA_ROWS * ((wave % (NW / 4)) * 64 + lane);
+#pragma unroll
+        for (int i = 0; i < FA_ROWS; ++i) f[i] = e8m0_value(fa_b[i]);
+      }
     }
   };
   auto wait_dma = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
@@ -337,8 +356,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
         const v4i hi = chunk(cur + S::A_OFF + row * BK + (((4 * s + 2 + h) ^ swz(row)) << 4), 4 * s + 2 + h);
         af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         if constexpr (!PC) {
-          as[i][0] = e8m0_value(cur[S::SA_OFF + (2 * s) * BM + row]);
-          as[i][1] = e8m0_value(cur[S::SA_OFF + (2 * s + 1) * BM + row]);
+          as[i][0] = ((const float*)(cur + S::SAF_OFF))[(2 * s) * BM + row];
+          as[i][1] = ((const float*)(cur + S::SAF_OFF))[(2 * s + 1) * BM + row];
         }
       }
 #pragma unroll
@@ -348,8 +367,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
         const v4i hi = chunk(cur + S::B_OFF + row * BK + (((4 * s + 2 + h) ^ swz(row)) << 4), 4 * s + 2 + h);
         bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         if constexpr (!PC) {
-          bs[j][0] = e8m0_value(cur[S::SB_OFF + (2 * s) * BN + row]);
-          bs[j][1] = e8m0_value(cur[S::SB_OFF + (2 * s + 1) * BN + row]);
+          bs[j][0] = ((const float*)(cur + S::SBF_OFF))[(2 * s) * BN + row];
+          bs[j][1] = ((const float*)(cur + S::SBF_OFF))[(2 * s + 1) * BN + row];
         }
       }
       // the next step's loads go out once this half's reads are issued: issued before the first
