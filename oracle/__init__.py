@@ -63,6 +63,8 @@ def lib():
                                            _vp, _i32, ctypes.c_int, _vp, _vp]
         L.oracle_grouped_fprop.restype = ctypes.c_int
         L.oracle_grouped_fprop.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _vp]
+        L.oracle_grouped_dgrad.restype = ctypes.c_int
+        L.oracle_grouped_dgrad.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _vp]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_wgrad_unquantized.restype = ctypes.c_int
@@ -186,6 +188,25 @@ def grouped_fprop(x_row_q, x_row_s, w_q, w_s, N, splits, cols_sel=None):
                                     0 if sel is None else sel.size, _p(out))
     if rc != 0:
         raise ValueError(f"oracle_grouped_fprop failed ({rc})")
+    return out
+
+
+def grouped_dgrad(dy_row_q, dy_row_s, w_col_q, w_col_s, k, splits, cols_sel=None):
+    """fp64 out[off_e + t][j] = sum_c dy[off_e + t][c] W[e][c][j] over the dequantized rowwise dy
+    [R, n] (scales [n/32, R]) and the colwise-quantized weight (grouped_quantize of W viewed as
+    [E*n, k] with splits [n] * E).  Returns float64 [R, len(cols_sel) or k]; rows not in any group
+    hold NaN."""
+    yq = _c(dy_row_q, np.uint8)
+    R, n = yq.shape
+    s = _c(splits, np.int32)
+    sel = None if cols_sel is None else _c(cols_sel, np.int32)
+    ns = k if sel is None else sel.size
+    out = np.full((R, ns), np.nan, np.float64)
+    rc = lib().oracle_grouped_dgrad(_p(yq), _p(_c(dy_row_s, np.uint8)), R, n, _p(_c(w_col_q, np.uint8)),
+                                    _p(_c(w_col_s, np.uint8)), k, _p(s), s.size, _p(sel),
+                                    0 if sel is None else sel.size, _p(out))
+    if rc != 0:
+        raise ValueError(f"oracle_grouped_dgrad failed ({rc})")
     return out
 
 

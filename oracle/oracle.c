@@ -447,6 +447,67 @@ int oracle_grouped_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R, int6
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* m-grouped data gradient: out[off_e + t][j] = sum_c dy[off_e + t][c] * W[e][c][j] in fp64, c  */
+/* ascending, over the dequantized rowwise dy and the weight quantized colwise (32-blocks along */
+/* c inside each expert).  The token axis is a free dimension here as in the forward GEMM.     */
+/* Rows >= sum(split_sizes) are not written.                                                  */
+/* ------------------------------------------------------------------------------------------ */
+
+/*
+ * dy_q [R][n], dy_s E8M0 [n/32][R] (rowwise).  w_q / w_s: the colwise output for the weight seen
+ * as E groups of n rows [E*n][k]: group e has P_e = e*np rows packed (np = 128 * ceil(n/128)), so
+ * its byte (c, j) -- row c of the group, channel j -- sits at k*np*e + j*np + c and its E8M0
+ * scale (b = c/32, j) at k*np*e/32 + b*k + j (the colwise layout above with C = k).
+ * cols_sel : NULL for all k columns, else n_sel column indices j.  out : fp64 [R][n_sel].
+ */
+int oracle_grouped_dgrad(const uint8_t* dy_q, const uint8_t* dy_s, int64_t R, int64_t n,
+                         const uint8_t* w_q, const uint8_t* w_s, int64_t k,
+                         const int32_t* splits, int32_t E, const int32_t* cols_sel,
+                         int32_t n_sel, double* out) {
+  group_t* g;
+  int32_t e;
+  int64_t ns = cols_sel ? n_sel : k;
+  int64_t np = 128 * ((n + 127) / 128);
+  if (E <= 0 || n <= 0 || n % 32 != 0 || k <= 0 || k % 32 != 0) return ORACLE_EINVAL;
+  g = (group_t*)malloc(sizeof(group_t) * (size_t)E);
+  if (!g) return ORACLE_ENOMEM;
+  if (group_layout(splits, E, R, g) != ORACLE_OK) { free(g); return ORACLE_EINVAL; }
+  for (e = 0; e < E; ++e) {
+    int64_t jj, t, c;
+    double* w; /* w[jj][c] = W[e][c][j] dequantized */
+    if (g[e].k == 0) continue;
+    w = (double*)malloc(sizeof(double) * (size_t)(ns * n));
+    if (!w) { free(g); return ORACLE_ENOMEM; }
+    for (jj = 0; jj < ns; ++jj) {
+      int64_t j = cols_sel ? cols_sel[jj] : jj;
+      for (c = 0; c < n; ++c)
+        w[jj * n + c] = oracle_e4m3_decode(w_q[k * np * e + j * np + c]) *
+                        ldexp(1.0, (int)w_s[k * np * e / 32 + (c / 32) * k + j] - 127);
+    }
+#pragma omp parallel private(jj, c)
+    {
+      double* yr = (double*)malloc(sizeof(double) * (size_t)n); /* one dequantized dy row */
+#pragma omp for schedule(static)
+      for (t = 0; t < g[e].k; ++t) {
+        int64_t r = g[e].off + t;
+        if (!yr) continue;
+        for (c = 0; c < n; ++c)
+          yr[c] = oracle_e4m3_decode(dy_q[r * n + c]) * ldexp(1.0, (int)dy_s[(c / 32) * R + r] - 127);
+        for (jj = 0; jj < ns; ++jj) {
+          double s = 0.0;
+          for (c = 0; c < n; ++c) s += yr[c] * w[jj * n + c];
+          out[r * ns + jj] = s;
+        }
+      }
+      free(yr);
+    }
+    free(w);
+  }
+  free(g);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* Unquantized brute force (tiny inputs): sum_t dy[off_e+t][i] * x[off_e+t][j] in fp64 from the */
 /* bf16 values, as the DeepGEMM reproducer's reference wgrad does in fp32.                     */
 /* ------------------------------------------------------------------------------------------ */

@@ -228,3 +228,58 @@ def test_fprop_equals_dense_matmul_per_group():
     sel = np.array([5, 63, 0], np.int32)
     part = oracle.grouped_fprop(xq["row_q"], xq["row_s"], wq["row_q"], wq["row_s"], N, splits, cols_sel=sel)
     assert np.array_equal(part[:T], got[:T, sel])
+
+
+def _dgrad_case(seed, splits, n, k, E, pad=10):
+    rng = np.random.default_rng(seed)
+    T = sum(splits)
+    dy = torch.from_numpy(rng.standard_normal((T + pad, n)).astype(np.float32)).to(torch.bfloat16)
+    dy[T:] = float("nan")  # padding that must never be read
+    w = torch.from_numpy(rng.standard_normal((E, n, k)).astype(np.float32)).to(torch.bfloat16)
+    dyq = oracle.grouped_quantize(W.bf16_bits(dy), splits, oracle.RECIPE_MX, oracle.ROWWISE)
+    # the weight quantized colwise: E groups of n rows, 32-blocks along n inside each expert
+    wc = oracle.grouped_quantize(W.bf16_bits(w.view(E * n, k)), [n] * E, oracle.RECIPE_MX, oracle.COLWISE)
+    # the same weight transposed per expert, [E*k][n], quantized rowwise (blocks along n)
+    wt = w.transpose(1, 2).contiguous().view(E * k, n)
+    wr = oracle.grouped_quantize(W.bf16_bits(wt), None, oracle.RECIPE_MX, oracle.ROWWISE)
+    return T, dyq, wc, wr
+
+
+@pytest.mark.parametrize("splits,n,k", [([40, 0, 77], 96, 64), ([128, 5], 256, 32), ([0, 33, 1, 0], 32, 96)])
+def test_dgrad_equals_fprop_on_the_transposed_weight(splits, n, k):
+    """The colwise weight of dgrad holds exactly the blocks of the rowwise transpose (32 along n),
+    so dgrad must reproduce the forward GEMM over W^T value for value: same products, same fp64
+    order (c ascending).  Pins the colwise index arithmetic of the dgrad oracle against the
+    rowwise path, which is itself pinned to a dense matmul."""
+    E = len(splits)
+    T, dyq, wc, wr = _dgrad_case(11, splits, n, k, E)
+    np_ = 128 * ((n + 127) // 128)
+    # the bytes agree element by element under the two layouts
+    for e in range(E):
+        for j in range(k):
+            row = wr["row_q"][e * k + j]
+            assert np.array_equal(wc["col_q"][k * np_ * e + j * np_: k * np_ * e + j * np_ + n], row)
+            assert not wc["col_q"][k * np_ * e + j * np_ + n: k * np_ * e + (j + 1) * np_].any()  # pad lanes
+            for b in range(n // 32):
+                assert wc["col_s"][k * np_ * e // 32 + b * k + j] == wr["row_s"][b, e * k + j]
+    d = oracle.grouped_dgrad(dyq["row_q"], dyq["row_s"], wc["col_q"], wc["col_s"], k, splits)
+    f = oracle.grouped_fprop(dyq["row_q"], dyq["row_s"], wr["row_q"], wr["row_s"], k, splits)
+    assert np.array_equal(d, f, equal_nan=True)
+    assert np.isnan(d[T:]).all()  # rows outside every group are not written
+
+
+def test_dgrad_equals_dense_matmul_per_group():
+    splits, n, k = [40, 0, 129, 3], 96, 64
+    E = len(splits)
+    T, dyq, wc, wr = _dgrad_case(12, splits, n, k, E, pad=20)
+    got = oracle.grouped_dgrad(dyq["row_q"], dyq["row_s"], wc["col_q"], wc["col_s"], k, splits)
+    Y = _rowwise_deq_torch(dyq["row_q"], dyq["row_s"])
+    Wt = _rowwise_deq_torch(wr["row_q"], wr["row_s"]).view(E, k, n)  # W_e^T
+    off = 0
+    for e, ke in enumerate(splits):
+        ref = (Y[off:off + ke] @ Wt[e].t()).numpy()  # dy_e @ W_e
+        assert np.allclose(got[off:off + ke], ref, rtol=1e-12, atol=1e-300)
+        off += ke
+    sel = np.array([63, 0, 17], np.int32)
+    part = oracle.grouped_dgrad(dyq["row_q"], dyq["row_s"], wc["col_q"], wc["col_s"], k, splits, cols_sel=sel)
+    assert np.array_equal(part[:T], got[:T, sel])
