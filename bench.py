@@ -184,6 +184,39 @@ def main():
     event_ms_per_step = events[0][0].elapsed_time(events[-1][5]) / args.steps
     leg_ms = {name: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps for i, name in enumerate(legs)}
 
+    # The data-gradient GEMM (dx_e = dy_e @ W_e), the next GEMM of the expert backward: timed on
+    # its own after the step (it is not part of the step or of `value`), with its two quantize
+    # passes (dy rowwise, the weight colwise along n).
+    log("dgrad leg")
+    nst = W.splits_tensor([N] * E, dev)
+    dyr = bs.alloc_quantized(R, n, E, bs.RECIPE_MX, bs.ROWWISE, dev)
+    wcq = bs.alloc_quantized(E * N, K, E, bs.RECIPE_MX, bs.COLWISE, dev)
+    dx = torch.empty(R, K, dtype=torch.bfloat16, device=dev)
+    w_nk = case["W"].view(E * N, K)
+
+    def dgrad_leg(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        bs.grouped_quantize(case["dy"], st, bs.RECIPE_MX, bs.ROWWISE, dyr, status=status)
+        if ev is not None:
+            ev[1].record(stream)
+        bs.grouped_quantize(w_nk, nst, bs.RECIPE_MX, bs.COLWISE, wcq, status=status)
+        if ev is not None:
+            ev[2].record(stream)
+        bs.grouped_gemm_dgrad(dyr, n, wcq, K, st, R, dx, bs.OUT_BF16, status=status)
+        if ev is not None:
+            ev[3].record(stream)
+
+    dgrad_leg()
+    dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(5)]
+    for ev in dev_ev:
+        dgrad_leg(ev)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    dleg = [sum(ev[i].elapsed_time(ev[i + 1]) for ev in dev_ev) / len(dev_ev) for i in range(3)]
+    del dx, dyr, wcq
+
     wgrad_flop = 2.0 * n * h * T
     fprop_flop = 2.0 * T * K * N
     # algorithmic HBM bytes: bf16 read once, e4m3 + E8M0 written once per requested layout
@@ -239,6 +272,12 @@ def main():
             "fprop": {"ms": round(leg_ms["fprop"], 3),
                       "TFLOP/s": round(fprop_flop / (leg_ms["fprop"] / 1e3) / 1e12, 1),
                       "algorithmic_GB": round(fprop_bytes / 1e9, 2)},
+            # outside the step: the data-gradient GEMM and its quantize passes
+            "quantize_dy_row": {"ms": round(dleg[0], 3),
+                                "GB/s": round(T * n * (2 + 1 + 1 / 32) / (dleg[0] / 1e3) / 1e9, 1)},
+            "quantize_w_col": {"ms": round(dleg[1], 3),
+                               "GB/s": round(E * N * K * (2 + 1 + 1 / 32) / (dleg[1] / 1e3) / 1e9, 1)},
+            "dgrad": {"ms": round(dleg[2], 3), "TFLOP/s": round(2.0 * T * N * K / (dleg[2] / 1e3) / 1e12, 1)},
         },
     }
     if args.calibrate_copy_gb > 0:

@@ -67,6 +67,9 @@ def lib():
         L.bsfp8_grouped_gemm_fprop.restype = ctypes.c_int
         L.bsfp8_grouped_gemm_fprop.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i32, _vp,
                                                ctypes.c_int, _vp, _vp]
+        L.bsfp8_grouped_gemm_dgrad.restype = ctypes.c_int
+        L.bsfp8_grouped_gemm_dgrad.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i32, _vp,
+                                               ctypes.c_int, _vp, _vp]
         L.bsfp8_strerror.restype = ctypes.c_char_p
         L.bsfp8_strerror.argtypes = [ctypes.c_int]
         _lib = L
@@ -181,4 +184,18 @@ def grouped_gemm_fprop(x_q, k, w_q, n, split_sizes, capacity_rows, out, out_dtyp
                                         _ptr(w_q["row_q"]), _ptr(w_q["row_s"]), n, _ptr(split_sizes), E,
                                         _ptr(out), out_dtype, _ptr(status), _stream(stream))
     _check(rc, "grouped_gemm_fprop")
+    return out
+
+
+def grouped_gemm_dgrad(dy_q, n, w_q, k, split_sizes, capacity_rows, out, out_dtype=OUT_F32, status=None,
+                       stream=None):
+    """bsfp8_grouped_gemm_dgrad: dy_q is the rowwise dict of dy [R, n]; w_q the colwise dict of the
+    weight viewed as [E*n, k] quantized with split sizes [n] * E (blocks of 32 along n inside each
+    expert); out is [R, k] fp32 or bf16: out[off_e + t] = dy[off_e + t] @ W_e (rows past
+    sum(split_sizes) untouched)."""
+    E = int(split_sizes.numel())
+    rc = lib().bsfp8_grouped_gemm_dgrad(_ptr(dy_q["row_q"]), _ptr(dy_q["row_s"]), capacity_rows, n,
+                                        _ptr(w_q["col_q"]), _ptr(w_q["col_s"]), k, _ptr(split_sizes), E,
+                                        _ptr(out), out_dtype, _ptr(status), _stream(stream))
+    _check(rc, "grouped_gemm_dgrad")
     return out

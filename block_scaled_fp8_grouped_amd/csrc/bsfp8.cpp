@@ -18,6 +18,9 @@ int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, 
 int launch_grouped_gemm_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R, int64_t K, const uint8_t* w_q,
                               const uint8_t* w_s, int64_t N, const int32_t* splits, int E, void* out, int out_dtype,
                               uint32_t* status, hipStream_t stream);
+int launch_grouped_gemm_dgrad(const uint8_t* dy_q, const uint8_t* dy_s, int64_t R, int64_t n, const uint8_t* w_q,
+                              const void* w_s, int64_t k, const int32_t* splits, int E, void* out, int out_dtype,
+                              uint32_t* status, hipStream_t stream);
 }  // namespace bsfp8
 
 namespace {
@@ -128,6 +131,25 @@ int bsfp8_grouped_gemm_fprop(const uint8_t* x_row_q, const uint8_t* x_row_s, int
     return BSFP8_ERR_ALIGNMENT;
   return bsfp8::launch_grouped_gemm_fprop(x_row_q, x_row_s, capacity_rows, k, w_q, w_s, n, split_sizes, num_groups,
                                           out, out_dtype, status, (hipStream_t)stream);
+}
+
+int bsfp8_grouped_gemm_dgrad(const uint8_t* dy_row_q, const uint8_t* dy_row_s, int64_t capacity_rows, int64_t n,
+                             const uint8_t* w_col_q, const void* w_col_s, int64_t k, const int32_t* split_sizes,
+                             int32_t num_groups, void* out, int out_dtype, uint32_t* status, void* stream) {
+  if (!valid_groups(num_groups)) return BSFP8_ERR_NUM_GROUPS;
+  // the weight rows are n rounded up to 128: that padded length bounds the 32-bit tile offsets
+  if (!valid_dim(n) || !valid_dim(k) || capacity_rows < 0 || n + 127 > kMaxKExtent || k > kMaxOutCols)
+    return BSFP8_ERR_SHAPE;
+  if (out_dtype != BSFP8_OUT_F32 && out_dtype != BSFP8_OUT_BF16) return BSFP8_ERR_ARGUMENT;
+  if (capacity_rows == 0) return BSFP8_OK;  // zero-row early return: nothing is dereferenced
+  if (dy_row_q == nullptr || dy_row_s == nullptr || w_col_q == nullptr || w_col_s == nullptr ||
+      split_sizes == nullptr || out == nullptr)
+    return BSFP8_ERR_NULL_POINTER;
+  if (!aligned16(dy_row_q) || !aligned16(dy_row_s) || !aligned16(w_col_q) || !aligned16(w_col_s) || !aligned16(out) ||
+      !aligned4(split_sizes) || !aligned4(status))
+    return BSFP8_ERR_ALIGNMENT;
+  return bsfp8::launch_grouped_gemm_dgrad(dy_row_q, dy_row_s, capacity_rows, n, w_col_q, w_col_s, k, split_sizes,
+                                          num_groups, out, out_dtype, status, (hipStream_t)stream);
 }
 
 const char* bsfp8_strerror(int code) {

@@ -49,6 +49,11 @@ struct GemmArgs {
   int64_t N;           // wgrad: h (x channels)    fprop: n (weight rows per expert)
   int64_t K;           // fprop: reduction length
   int64_t R;           // capacity rows
+  // m-grouped B operand (fprop: the rowwise weight; dgrad: the colwise-quantized weight):
+  int64_t b_ld;        // bytes per B row
+  int64_t b_estride;   // bytes of B data per group
+  int64_t bs_estride;  // B scale bytes per group (offset of the group's first scale)
+  int64_t bs_bstride;  // B scale bytes between consecutive 32-blocks along K
   const int32_t* splits;
   int E;
   int tiles_m, tiles_n;  // wgrad: per-group tile grid; fprop: tiles_n only
@@ -177,14 +182,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
     a_sld = args.M;
     b_sld = args.N;
   } else {
-    lda = ldb = args.K;
+    lda = args.K;
+    ldb = args.b_ld;
     kext = args.K;
     a_data = args.a_q + gi.off * args.K;
-    b_data = args.b_q + (int64_t)e * args.N * args.K;
+    b_data = args.b_q + (int64_t)e * args.b_estride;
     a_sc = (const uint8_t*)args.a_s + gi.off;
-    b_sc = (const uint8_t*)args.b_s + (int64_t)e * args.N;
+    b_sc = (const uint8_t*)args.b_s + (int64_t)e * args.bs_estride;
     a_sld = args.R;
-    b_sld = (int64_t)args.E * args.N;
+    b_sld = args.bs_bstride;
     a_valid = gi.k;
     b_valid = args.N;
   }
@@ -546,18 +552,25 @@ int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, 
                     : launch<kModeWgrad, true, BM, BN, 64, 64, false, 0>(a, grid, stream);
 }
 
-int launch_grouped_gemm_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R, int64_t K, const uint8_t* w_q,
-                              const uint8_t* w_s, int64_t N, const int32_t* splits, int E, void* out, int out_dtype,
-                              uint32_t* status, hipStream_t stream) {
+// m-grouped GEMM: out[off_e + t][j] = sum_c A[off_e + t][c] B_e[j][c] over the rowwise A
+// [R][K] and a per-group B described by its row length and strides (see GemmArgs).
+static int launch_mgrouped(const uint8_t* a_q, const uint8_t* a_s, int64_t R, int64_t K, const uint8_t* b_q,
+                           const uint8_t* b_s, int64_t N, int64_t b_ld, int64_t b_estride, int64_t bs_estride,
+                           int64_t bs_bstride, const int32_t* splits, int E, void* out, int out_dtype,
+                           uint32_t* status, hipStream_t stream) {
   constexpr int BM = 256, BN = 256;
   GemmArgs a{};
-  a.a_q = x_q;
-  a.a_s = x_s;
-  a.b_q = w_q;
-  a.b_s = w_s;
+  a.a_q = a_q;
+  a.a_s = a_s;
+  a.b_q = b_q;
+  a.b_s = b_s;
   a.N = N;
   a.K = K;
   a.R = R;
+  a.b_ld = b_ld;
+  a.b_estride = b_estride;
+  a.bs_estride = bs_estride;
+  a.bs_bstride = bs_bstride;
   a.splits = splits;
   a.E = E;
   a.out = out;
@@ -577,6 +590,25 @@ int launch_grouped_gemm_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R,
   return out_dtype == BSFP8_OUT_F32
              ? launch<kModeFprop, false, BM, BN, 128, 64, false, BSFP8_OUT_F32>(a, grid, stream)
              : launch<kModeFprop, false, BM, BN, 128, 64, false, BSFP8_OUT_BF16>(a, grid, stream);
+}
+
+int launch_grouped_gemm_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R, int64_t K, const uint8_t* w_q,
+                              const uint8_t* w_s, int64_t N, const int32_t* splits, int E, void* out, int out_dtype,
+                              uint32_t* status, hipStream_t stream) {
+  // W rowwise [E*N][K], scales [K/32][E*N]
+  return launch_mgrouped(x_q, x_s, R, K, w_q, w_s, N, K, N * K, N, (int64_t)E * N, splits, E, out, out_dtype, status,
+                         stream);
+}
+
+int launch_grouped_gemm_dgrad(const uint8_t* dy_q, const uint8_t* dy_s, int64_t R, int64_t n, const uint8_t* w_q,
+                              const void* w_s, int64_t k, const int32_t* splits, int E, void* out, int out_dtype,
+                              uint32_t* status, hipStream_t stream) {
+  // W colwise: group e's rows are its k output channels, each np = 128 * ceil(n / 128) bytes
+  // (n along the contraction, pad lanes 0), data at k * np * e; E8M0 (e, b, c) at
+  // k * np * e / 32 + b * k + c
+  const int64_t np = (n + 127) / 128 * 128;
+  return launch_mgrouped(dy_q, dy_s, R, n, w_q, (const uint8_t*)w_s, k, np, k * np, k * np / 32, k, splits, E, out,
+                         out_dtype, status, stream);
 }
 
 }  // namespace bsfp8

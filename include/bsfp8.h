@@ -168,6 +168,31 @@ int bsfp8_grouped_gemm_fprop(const uint8_t* x_row_q, const uint8_t* x_row_s, int
                              const int32_t* split_sizes, int32_t num_groups, void* out,
                              int out_dtype, uint32_t* status, void* stream);
 
+/* ----------------------------------------------------------------------------------------- */
+/* m-grouped data-gradient GEMM (the remaining GEMM of the expert backward beside wgrad and    */
+/* fprop: TE #3484 scope -- the token axis is a free dimension of everything but wgrad).      */
+/* MX recipe only.                                                                           */
+/* ----------------------------------------------------------------------------------------- */
+/*
+ * dy_row_q, dy_row_s  rowwise output of bsfp8_grouped_quantize for dy [capacity_rows][n]
+ * w_col_q, w_col_s    colwise output of bsfp8_grouped_quantize for the weight viewed as
+ *                     [num_groups * n][k] with split sizes n, ..., n (num_groups of them): the
+ *                     32-blocks run along n inside each expert, so expert e's matrix is
+ *                     transposed in the buffer -- output channel j, contraction index c at
+ *                     k*np*e + j*np + c with np = 128 * ceil(n / 128); E8M0 (e, b, j) at
+ *                     k*np*e/32 + b*k + j (bsfp8_colwise_data_bytes / _scale_bytes with
+ *                     capacity_rows = num_groups * n give the sizes)
+ * out                 [capacity_rows][k], fp32 or bf16 (round to nearest even from fp32):
+ *     out[off_e + t][j] = sum_c deq(dy)[off_e + t][c] * deq(W_e)[c][j]   for t < k_e
+ *   rows at or past sum(k_e) are not written.
+ * n and k must be multiples of 32, n at most 2^24 - 256, k at most 2^21 (BSFP8_ERR_SHAPE
+ * otherwise).  capacity_rows == 0 returns BSFP8_OK without touching any pointer.
+ */
+int bsfp8_grouped_gemm_dgrad(const uint8_t* dy_row_q, const uint8_t* dy_row_s, int64_t capacity_rows,
+                             int64_t n, const uint8_t* w_col_q, const void* w_col_s, int64_t k,
+                             const int32_t* split_sizes, int32_t num_groups, void* out,
+                             int out_dtype, uint32_t* status, void* stream);
+
 /* Static description of a return code. */
 const char* bsfp8_strerror(int code);
 

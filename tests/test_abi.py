@@ -125,6 +125,27 @@ def test_fprop_rejects_before_launch(kw, code):
     assert _f(**kw) == code
 
 
+def _d(**kw):
+    a = dict(yq=P, ys=P, R=1024, n=256, wq=P, ws=P, k=256, splits=P, E=4, out=P, dtype=bs.OUT_F32, status=P)
+    a.update(kw)
+    return bs.lib().bsfp8_grouped_gemm_dgrad(a["yq"], a["ys"], a["R"], a["n"], a["wq"], a["ws"], a["k"],
+                                             a["splits"], a["E"], a["out"], a["dtype"], a["status"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(E=0), -2), (dict(E=2000), -2), (dict(n=48), -4), (dict(k=-32), -4), (dict(k=(1 << 21) + 32), -4),
+    (dict(n=(1 << 24) - 224), -4), (dict(dtype=2), -7), (dict(R=-1), -4),
+    (dict(yq=None), -1), (dict(ws=None), -1), (dict(splits=None), -1), (dict(out=None), -1),
+    (dict(out=P + 2), -5), (dict(wq=P + 8), -5), (dict(ys=P + 1), -5),
+])
+def test_dgrad_rejects_before_launch(kw, code):
+    assert _d(**kw) == code
+
+
+def test_dgrad_zero_rows_returns_without_touching_pointers():
+    assert _d(R=0, yq=None, ys=None, wq=None, ws=None, splits=None, out=None) == 0
+
+
 def test_fprop_zero_rows_early_return():
     """TE PR #3224: a zero-row batch returns before any data pointer is used."""
     assert _f(R=0, xq=None, xs=None, wq=None, ws=None, splits=None, out=None) == 0
