@@ -60,7 +60,7 @@ def lib():
         L.bsfp8_rowwise_scale_bytes.argtypes = [_i64, _i64]
         L.bsfp8_grouped_quantize.restype = ctypes.c_int
         L.bsfp8_grouped_quantize.argtypes = [_vp, _i64, _i64, _vp, _i32, ctypes.c_int, ctypes.c_int,
-                                             ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp]
+                                             ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.bsfp8_grouped_gemm_wgrad.restype = ctypes.c_int
         L.bsfp8_grouped_gemm_wgrad.argtypes = [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i64, ctypes.c_int,
                                                _vp, ctypes.c_int, _vp, _vp]
@@ -148,9 +148,11 @@ def alloc_quantized(capacity_rows, cols, num_groups, recipe, which, device="cuda
 # ------------------------------------------------------------------------------------------
 
 def grouped_quantize(x, split_sizes, recipe, which, out, zero_amax_scale=1e-30, status=None, stream=None,
-                     capacity_rows=None, cols=None):
+                     capacity_rows=None, cols=None, noop_flag=None):
     """bsfp8_grouped_quantize on a bf16 [R, C] tensor; ``out`` holds the output tensors
-    (see alloc_quantized).  split_sizes: int32 device tensor, or None (rowwise, all rows live)."""
+    (see alloc_quantized), overwritten in place.  split_sizes: int32 device tensor, or None
+    (rowwise, all rows live).  noop_flag: None, or a float32 device scalar; when it holds a
+    nonzero value at run time the call leaves ``out`` (and ``status``) as they are."""
     if isinstance(x, torch.Tensor):
         R, C = x.shape if capacity_rows is None else (capacity_rows, cols)
     else:
@@ -158,7 +160,7 @@ def grouped_quantize(x, split_sizes, recipe, which, out, zero_amax_scale=1e-30, 
     E = 0 if split_sizes is None else int(split_sizes.numel())
     rc = lib().bsfp8_grouped_quantize(_ptr(x), R, C, _ptr(split_sizes), E, recipe, which, float(zero_amax_scale),
                                       _ptr(out.get("row_q")), _ptr(out.get("row_s")), _ptr(out.get("col_q")),
-                                      _ptr(out.get("col_s")), _ptr(status), _stream(stream))
+                                      _ptr(out.get("col_s")), _ptr(noop_flag), _ptr(status), _stream(stream))
     _check(rc, "grouped_quantize")
     return out
 

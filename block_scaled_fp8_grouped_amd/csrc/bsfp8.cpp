@@ -11,7 +11,7 @@
 namespace bsfp8 {
 int launch_grouped_quantize(const void* in, int64_t R, int64_t C, const int32_t* splits, int E, int recipe,
                             int which, float zas, uint8_t* row_q, uint8_t* row_s, uint8_t* col_q, void* col_s,
-                            uint32_t* status, hipStream_t stream);
+                            const float* noop_flag, uint32_t* status, hipStream_t stream);
 int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, const uint8_t* x_q, const void* x_s,
                               int64_t h, const int32_t* splits, int E, int64_t R, int recipe, float* out,
                               int accumulate, uint32_t* status, hipStream_t stream);
@@ -72,7 +72,8 @@ size_t bsfp8_rowwise_scale_bytes(int64_t rows, int64_t cols) {
 
 int bsfp8_grouped_quantize(const void* in_bf16, int64_t capacity_rows, int64_t cols, const int32_t* split_sizes,
                            int32_t num_groups, int recipe, int which, float zero_amax_scale, uint8_t* row_q,
-                           uint8_t* row_s, uint8_t* col_q, void* col_s, uint32_t* status, void* stream) {
+                           uint8_t* row_s, uint8_t* col_q, void* col_s, const float* noop_flag, uint32_t* status,
+                           void* stream) {
   if (!valid_recipe(recipe)) return BSFP8_ERR_RECIPE;
   if (which <= 0 || (which & ~(BSFP8_ROWWISE | BSFP8_COLWISE)) != 0) return BSFP8_ERR_ARGUMENT;
   if ((which & BSFP8_ROWWISE) && recipe != BSFP8_RECIPE_MX_1X32_E8M0) return BSFP8_ERR_LAYOUT;
@@ -85,14 +86,16 @@ int bsfp8_grouped_quantize(const void* in_bf16, int64_t capacity_rows, int64_t c
   if (in_bf16 == nullptr) return BSFP8_ERR_NULL_POINTER;
   if ((which & BSFP8_ROWWISE) && (row_q == nullptr || row_s == nullptr)) return BSFP8_ERR_NULL_POINTER;
   if ((which & BSFP8_COLWISE) && (col_q == nullptr || col_s == nullptr)) return BSFP8_ERR_NULL_POINTER;
-  if (!aligned16(in_bf16) || !aligned4(split_sizes) || !aligned4(status)) return BSFP8_ERR_ALIGNMENT;
+  if (!aligned16(in_bf16) || !aligned4(split_sizes) || !aligned4(noop_flag) || !aligned4(status))
+    return BSFP8_ERR_ALIGNMENT;
   if ((which & BSFP8_ROWWISE) && (!aligned16(row_q) || !aligned16(row_s))) return BSFP8_ERR_ALIGNMENT;
   if ((which & BSFP8_COLWISE) && (!aligned16(col_q) || !aligned16(col_s))) return BSFP8_ERR_ALIGNMENT;
   return bsfp8::launch_grouped_quantize(in_bf16, capacity_rows, cols, split_sizes, split_sizes ? num_groups : 0,
                                         recipe, which, zero_amax_scale, (which & BSFP8_ROWWISE) ? row_q : nullptr,
                                         (which & BSFP8_ROWWISE) ? row_s : nullptr,
                                         (which & BSFP8_COLWISE) ? col_q : nullptr,
-                                        (which & BSFP8_COLWISE) ? col_s : nullptr, status, (hipStream_t)stream);
+                                        (which & BSFP8_COLWISE) ? col_s : nullptr, noop_flag, status,
+                                        (hipStream_t)stream);
 }
 
 int bsfp8_grouped_gemm_wgrad(const uint8_t* dy_col_q, const void* dy_col_s, int64_t n, const uint8_t* x_col_q,

@@ -116,12 +116,20 @@ size_t bsfp8_rowwise_scale_bytes(int64_t rows, int64_t cols);
  *          PC : fp32 (e, b, c) at cols*P_e/128 + b*cols + c, b < Kp_e/128.
  *   Blocks restart at every group start; a partial block takes its amax over live rows only.
  *   Bytes of col_q / col_s past cols*sum(Kp_e) are not written.
+ * noop_flag       NULL, or a device fp32 scalar read by the kernels when they run (TE PR #3224,
+ *                 group_quantize output reuse: the noop flag of the FP8 block-scaling path).  A
+ *                 nonzero value makes the call a no-op on the device: no output byte and no status
+ *                 bit is written, so storage filled by an earlier call (a cached quantized weight)
+ *                 is reused as it stands.  Zero (or NULL) quantizes as usual, overwriting the
+ *                 caller's pre-allocated outputs in place.  The flag is read on the device, so one
+ *                 captured graph serves both the first microbatch (flag 0) and the rest (flag 1).
+ *                 4-byte aligned.
  * capacity_rows == 0 returns BSFP8_OK without touching any pointer.
  */
 int bsfp8_grouped_quantize(const void* in_bf16, int64_t capacity_rows, int64_t cols,
                            const int32_t* split_sizes, int32_t num_groups, int recipe, int which,
                            float zero_amax_scale, uint8_t* row_q, uint8_t* row_s, uint8_t* col_q,
-                           void* col_s, uint32_t* status, void* stream);
+                           void* col_s, const float* noop_flag, uint32_t* status, void* stream);
 
 /* ----------------------------------------------------------------------------------------- */
 /* k-grouped weight-gradient GEMM (DeepGEMM #365, k_grouped_fp8_gemm_nt_contiguous; TE #3484, */

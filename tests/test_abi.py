@@ -62,11 +62,11 @@ def test_size_queries():
 
 def _q(**kw):
     a = dict(inp=P, R=1024, C=256, splits=P, E=4, recipe=MX, which=bs.COLWISE, zas=1e-30, row_q=P, row_s=P,
-             col_q=P, col_s=P, status=P, stream=None)
+             col_q=P, col_s=P, noop=None, status=P, stream=None)
     a.update(kw)
     return bs.lib().bsfp8_grouped_quantize(a["inp"], a["R"], a["C"], a["splits"], a["E"], a["recipe"], a["which"],
-                                           a["zas"], a["row_q"], a["row_s"], a["col_q"], a["col_s"], a["status"],
-                                           a["stream"])
+                                           a["zas"], a["row_q"], a["row_s"], a["col_q"], a["col_s"], a["noop"],
+                                           a["status"], a["stream"])
 
 
 def _w(**kw):
@@ -94,6 +94,7 @@ def _f(**kw):
     (dict(inp=None), -1), (dict(col_q=None), -1), (dict(col_s=None), -1),
     (dict(which=bs.ROWWISE | bs.COLWISE, row_q=None), -1),
     (dict(inp=P + 8), -5), (dict(col_q=P + 4), -5), (dict(splits=P + 2), -5), (dict(status=P + 1), -5),
+    (dict(noop=P + 2), -5),
 ])
 def test_quantize_rejects_before_launch(kw, code):
     assert _q(**kw) == code
@@ -102,6 +103,7 @@ def test_quantize_rejects_before_launch(kw, code):
 def test_quantize_zero_rows_returns_without_touching_pointers():
     assert _q(R=0, inp=None, col_q=None, col_s=None) == 0
     assert _q(R=0, which=bs.ROWWISE, splits=None, inp=None, row_q=None, row_s=None) == 0
+    assert _q(R=0, inp=None, col_q=None, col_s=None, noop=P + 2) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
