@@ -110,6 +110,31 @@ def cpu_baseline(case, experts, channels):
     }
 
 
+def graph_leg(graph_step, flag, stream):
+    """Capture one step in a HIP graph; mean replay time with the weight quantize running (flag 0)
+    and skipped on the device (flag 1)."""
+    import torch
+    log("graph leg")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        graph_step()
+    graph_ms = {}
+    for name, fv in (("replay", 0.0), ("replay_cached_weight", 1.0)):
+        flag.fill_(fv)
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(3):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms[name] = g0.elapsed_time(g1) / 3
+    del graph
+    return graph_ms
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +143,7 @@ def main():
     ap.add_argument("--cpu-experts", type=int, default=2,
                     help="experts in the CPU-baseline sample (0 skips it)")
     ap.add_argument("--cpu-channels", type=int, default=2048, help="dy channels per sampled expert")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay leg")
     ap.add_argument("--calibrate-copy-gb", type=float, default=0.0,
                     help="after the timed region, run one device copy of this many GB (for counter "
                          "calibration against a kernel of known traffic)")
@@ -209,39 +235,6 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    # The same step captured once in a HIP graph and replayed: first with the weight quantize
-    # running (noop flag 0, the step above), then as a later microbatch that reuses the cached
-    # quantized weight (flag 1).  Replays accumulate into main_grad like eager steps.
-    log("graph leg")
-    flag = torch.zeros(1, dtype=torch.float32, device=dev)
-
-    def graph_step():
-        bs.grouped_quantize(case["x"], st, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, xq, status=status)
-        bs.grouped_quantize(case["dy"], st, bs.RECIPE_MX, bs.COLWISE, dq, status=status)
-        bs.grouped_quantize(w2, None, bs.RECIPE_MX, bs.ROWWISE, wq, noop_flag=flag)
-        bs.grouped_gemm_wgrad(dq, n, xq, h, st, R, bs.RECIPE_MX, mg, accumulate=True, status=status)
-        bs.grouped_gemm_fprop(xq, K, wq, N, st, R, fout, bs.OUT_BF16, status=status)
-
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        graph_step()
-    graph_ms = {}
-    for name, fv in (("replay", 0.0), ("replay_cached_weight", 1.0)):
-        flag.fill_(fv)
-        graph.replay()
-        torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
-        for _ in range(3):
-            graph.replay()
-        g1.record(stream)
-        torch.cuda.synchronize()
-        graph_ms[name] = g0.elapsed_time(g1) / 3
-    if int(status.item()) != 0:
-        raise RuntimeError(f"device status {int(status.item())}")
-    del graph
-
     dgrad_leg()
     dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(5)]
     for ev in dev_ev:
@@ -251,6 +244,24 @@ def main():
         raise RuntimeError(f"device status {int(status.item())}")
     dleg = [sum(ev[i].elapsed_time(ev[i + 1]) for ev in dev_ev) / len(dev_ev) for i in range(3)]
     del dx, dyr, wcq
+
+    # The same step captured once in a HIP graph and replayed: first with the weight quantize
+    # running (noop flag 0, the step above), then as a later microbatch that reuses the cached
+    # quantized weight (flag 1).  Replays accumulate into main_grad like eager steps.
+    graph_ms = None
+    flag = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def graph_step():
+        bs.grouped_quantize(case["x"], st, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, xq, status=status)
+        bs.grouped_quantize(case["dy"], st, bs.RECIPE_MX, bs.COLWISE, dq, status=status)
+        bs.grouped_quantize(w2, None, bs.RECIPE_MX, bs.ROWWISE, wq, noop_flag=flag)
+        bs.grouped_gemm_wgrad(dq, n, xq, h, st, R, bs.RECIPE_MX, mg, accumulate=True, status=status)
+        bs.grouped_gemm_fprop(xq, K, wq, N, st, R, fout, bs.OUT_BF16, status=status)
+
+    if not args.no_graph:
+        graph_ms = graph_leg(graph_step, flag, stream)
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
 
     wgrad_flop = 2.0 * n * h * T
     fprop_flop = 2.0 * T * K * N
@@ -315,10 +326,11 @@ def main():
             "dgrad": {"ms": round(dleg[2], 3), "TFLOP/s": round(2.0 * T * N * K / (dleg[2] / 1e3) / 1e12, 1)},
         },
     }
-    out["graph"] = {"ms_per_step": round(graph_ms["replay"], 3),
-                    "ms_per_step_cached_weight": round(graph_ms["replay_cached_weight"], 3),
-                    "note": "the step captured once and replayed; cached_weight: weight quantize "
-                            "skipped on the device by its noop flag"}
+    if graph_ms is not None:
+        out["graph"] = {"ms_per_step": round(graph_ms["replay"], 3),
+                        "ms_per_step_cached_weight": round(graph_ms["replay_cached_weight"], 3),
+                        "note": "the step captured once and replayed; cached_weight: weight quantize "
+                                "skipped on the device by its noop flag"}
     if args.calibrate_copy_gb > 0:
         nbytes = int(args.calibrate_copy_gb * 1e9) // 16 * 16
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)

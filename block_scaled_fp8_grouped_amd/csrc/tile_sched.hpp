@@ -9,7 +9,8 @@
 // operand panels into those runs:
 //   wgrad: per group, blocks of `gn` tile columns; inside a block, tile rows then columns
 //          (TM x gn tiles with gn = 32 / TM share all A panels and gn B panels).
-//   fprop: runs of `gm` m-tiles (rows of one group's tokens) times all TN weight tiles.
+//   fprop: runs of `gm` m-tiles (rows of the groups' tokens) crossing the TN weight tiles in
+//          blocks of `gn`; inside a block, m-tiles then weight tiles.
 // Plain C++ for the host-side bijection test and for gfx950.
 #pragma once
 
@@ -54,19 +55,26 @@ BSFP8_HD void wgrad_tile(int64_t L, int TM, int TN, int* e, int* tm, int* tn) {
   *tn = j * gn + q % w;
 }
 
-// fprop: m-tiles per run for TN weight tiles.
+// fprop: weight tiles per column block, and m-tiles per run, for TN weight tiles.  A run of gm
+// m-tiles crosses the TN weight tiles in blocks of gn, so the 32 workgroups of an XCD share
+// about gm A panels and gn B panels (4 + 8 for wide weights, rather than 1 + 32).
+BSFP8_HD int fprop_block_cols(int tn_count) { return tn_count < 8 ? tn_count : 8; }
+
 BSFP8_HD int fprop_run_mtiles(int tn_count) {
-  const int g = kCusPerXcd / tn_count;
+  const int g = kCusPerXcd / fprop_block_cols(tn_count);
   return g > 0 ? g : 1;
 }
 
 // fprop: logical tile L -> (global m-tile index mt, weight tile tn).
 BSFP8_HD void fprop_tile(int64_t L, int TN, int64_t* mt, int* tn) {
-  const int gm = fprop_run_mtiles(TN);
+  const int gn = fprop_block_cols(TN), gm = fprop_run_mtiles(TN);
   const int64_t run = L / ((int64_t)gm * TN);
-  const int w = (int)(L % ((int64_t)gm * TN));
-  *mt = run * gm + w / TN;
-  *tn = w % TN;
+  const int r = (int)(L % ((int64_t)gm * TN));
+  const int jb = r / (gm * gn);                         // column block
+  const int q = r - jb * gm * gn;
+  const int w = TN - jb * gn < gn ? TN - jb * gn : gn;  // width of this block
+  *mt = run * gm + q / w;
+  *tn = jb * gn + q % w;
 }
 
 }  // namespace bsfp8

@@ -83,7 +83,7 @@ int main() {
                          {7, 1, 3}, {1024, 1, 1}, {3, 40, 2}, {2, 33, 33}};
   for (auto& d : dims) check_wgrad(d[0], d[1], d[2]);
   for (int64_t MT : {1, 2, 3, 4, 5, 31, 33, 260, 4224})
-    for (int TN : {1, 2, 6, 8, 28, 40}) check_fprop(MT, TN);
+    for (int TN : {1, 2, 6, 8, 9, 12, 28, 40}) check_fprop(MT, TN);
   std::printf("tile order: %ld violations\n", g_fail);
   return g_fail == 0 ? 0 : 1;
 }
