@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 RECIPE_MX = 1  # MXFP8: e4m3 data, one E8M0 power-of-two scale per 32 elements
 RECIPE_PC = 2  # per channel: e4m3 data, one fp32 scale per 128 rows
+RECIPE_MX4 = 3  # MXFP4: e2m1 data packed two per byte, one E8M0 power-of-two scale per 32 elements
 ROWWISE = 1
 COLWISE = 2
 
@@ -53,6 +54,14 @@ def lib():
         L.oracle_e8m0_exponent.restype = ctypes.c_int
         L.oracle_e8m0_exponent.argtypes = [ctypes.c_float]
         L.oracle_e8m0_exponent_array.argtypes = [_vp, _vp, _i64]
+        L.oracle_e2m1_decode.restype = ctypes.c_double
+        L.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_encode.restype = ctypes.c_uint8
+        L.oracle_e2m1_encode.argtypes = [ctypes.c_float]
+        L.oracle_e2m1_encode_array.argtypes = [_vp, _vp, _i64]
+        L.oracle_e8m0_exponent_fp4.restype = ctypes.c_int
+        L.oracle_e8m0_exponent_fp4.argtypes = [ctypes.c_float]
+        L.oracle_e8m0_exponent_fp4_array.argtypes = [_vp, _vp, _i64]
         L.oracle_padded_rows.restype = _i64
         L.oracle_padded_rows.argtypes = [_vp, _i32]
         L.oracle_grouped_quantize.restype = ctypes.c_int
@@ -62,9 +71,11 @@ def lib():
         L.oracle_grouped_wgrad.argtypes = [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i64, ctypes.c_int,
                                            _vp, _i32, ctypes.c_int, _vp, _vp]
         L.oracle_grouped_fprop.restype = ctypes.c_int
-        L.oracle_grouped_fprop.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _vp]
+        L.oracle_grouped_fprop.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i32, ctypes.c_int, _vp, _i32,
+                                           _vp]
         L.oracle_grouped_dgrad.restype = ctypes.c_int
-        L.oracle_grouped_dgrad.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _vp]
+        L.oracle_grouped_dgrad.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i32, ctypes.c_int, _vp, _i32,
+                                           _vp]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_wgrad_unquantized.restype = ctypes.c_int
@@ -110,6 +121,28 @@ def e8m0_exponent(amax):
     return out
 
 
+def e2m1_encode(v):
+    """Nearest-even OCP FP4 E2M1 code (0..15) of every float32 in ``v`` (magnitudes >= 6 give 6)."""
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().oracle_e2m1_encode_array(_p(v), _p(out), v.size)
+    return out
+
+
+def e2m1_decode(q):
+    """Exact value (float64) of every e2m1 code (low 4 bits) in ``q``."""
+    q = _c(q, np.uint8)
+    return np.array([lib().oracle_e2m1_decode(int(c)) for c in q.ravel()], np.float64).reshape(q.shape)
+
+
+def e8m0_exponent_fp4(amax):
+    """MXFP4 block exponent e (int32) for every float32 block amax."""
+    a = _c(amax, np.float32)
+    out = np.empty(a.shape, np.int32)
+    lib().oracle_e8m0_exponent_fp4_array(_p(a), _p(out), a.size)
+    return out
+
+
 def padded_rows(splits):
     s = _c(splits, np.int32)
     return int(lib().oracle_padded_rows(_p(s), s.size))
@@ -122,6 +155,8 @@ def grouped_quantize(x_bits, splits, recipe, which, zero_amax_scale=1e-30):
       row_q uint8 [R, C] and row_s uint8 [C/32, R]   (rows not live are left 0)
       col_q uint8 [C * sum(Kp_e)] and col_s uint8 [C * sum(Kp_e) / 32] (MX) or
       float32 [C * sum(Kp_e) / 128] (per-channel).
+    MXFP4 (RECIPE_MX4) packs two e2m1 codes per byte: row_q is uint8 [R, C/2] and col_q has
+    C * sum(Kp_e) / 2 bytes; the scales are as for MX.
     ``splits`` may be None for rowwise-only quantization of a fully live buffer.
     """
     x = _c(x_bits, np.uint16)
@@ -130,14 +165,15 @@ def grouped_quantize(x_bits, splits, recipe, which, zero_amax_scale=1e-30):
     s = None if splits is None else _c(splits, np.int32)
     E = 0 if s is None else s.size
     row_q = row_s = col_q = col_s = None
+    per = 2 if recipe == RECIPE_MX4 else 1  # elements per data byte
     if which & ROWWISE:
-        row_q = np.zeros((R, C), np.uint8)
+        row_q = np.zeros((R, C // per), np.uint8)
         row_s = np.zeros((C // 32, R), np.uint8)
         out["row_q"], out["row_s"] = row_q, row_s
     if which & COLWISE:
         rows = padded_rows(s)
-        col_q = np.zeros(C * rows, np.uint8)
-        if recipe == RECIPE_MX:
+        col_q = np.zeros(C * rows // per, np.uint8)
+        if recipe != RECIPE_PC:
             col_s = np.zeros(C * rows // 32, np.uint8)
         else:
             col_s = np.zeros(C * rows // 128, np.float32)
@@ -171,39 +207,44 @@ def grouped_wgrad(dy_col_q, dy_col_s, n, x_col_q, x_col_s, h, splits, R, recipe,
     return out
 
 
-def grouped_fprop(x_row_q, x_row_s, w_q, w_s, N, splits, cols_sel=None):
+def grouped_fprop(x_row_q, x_row_s, w_q, w_s, N, splits, cols_sel=None, recipe=RECIPE_MX):
     """fp64 out[off_e + t][j] = sum_k x[off_e + t][k] W[e][j][k] over dequantized rowwise data.
 
-    x_row_q uint8 [R, K], x_row_s uint8 [K/32, R], w_q uint8 [E*N, K], w_s uint8 [K/32, E*N].
+    x_row_q uint8 [R, K], x_row_s uint8 [K/32, R], w_q uint8 [E*N, K], w_s uint8 [K/32, E*N]
+    (MXFP4: the data arrays are [R, K/2] and [E*N, K/2], two codes per byte).
     Returns float64 [R, len(cols_sel) or N]; rows not in any group hold NaN.
     """
     xq = _c(x_row_q, np.uint8)
     R, K = xq.shape
+    if recipe == RECIPE_MX4:
+        K *= 2
     s = _c(splits, np.int32)
     sel = None if cols_sel is None else _c(cols_sel, np.int32)
     ns = N if sel is None else sel.size
     out = np.full((R, ns), np.nan, np.float64)
     rc = lib().oracle_grouped_fprop(_p(xq), _p(_c(x_row_s, np.uint8)), R, K, _p(_c(w_q, np.uint8)),
-                                    _p(_c(w_s, np.uint8)), N, _p(s), s.size, _p(sel),
+                                    _p(_c(w_s, np.uint8)), N, _p(s), s.size, recipe, _p(sel),
                                     0 if sel is None else sel.size, _p(out))
     if rc != 0:
         raise ValueError(f"oracle_grouped_fprop failed ({rc})")
     return out
 
 
-def grouped_dgrad(dy_row_q, dy_row_s, w_col_q, w_col_s, k, splits, cols_sel=None):
+def grouped_dgrad(dy_row_q, dy_row_s, w_col_q, w_col_s, k, splits, cols_sel=None, recipe=RECIPE_MX):
     """fp64 out[off_e + t][j] = sum_c dy[off_e + t][c] W[e][c][j] over the dequantized rowwise dy
     [R, n] (scales [n/32, R]) and the colwise-quantized weight (grouped_quantize of W viewed as
     [E*n, k] with splits [n] * E).  Returns float64 [R, len(cols_sel) or k]; rows not in any group
-    hold NaN."""
+    hold NaN.  MXFP4: dy_row_q is [R, n/2] (two codes per byte)."""
     yq = _c(dy_row_q, np.uint8)
     R, n = yq.shape
+    if recipe == RECIPE_MX4:
+        n *= 2
     s = _c(splits, np.int32)
     sel = None if cols_sel is None else _c(cols_sel, np.int32)
     ns = k if sel is None else sel.size
     out = np.full((R, ns), np.nan, np.float64)
     rc = lib().oracle_grouped_dgrad(_p(yq), _p(_c(dy_row_s, np.uint8)), R, n, _p(_c(w_col_q, np.uint8)),
-                                    _p(_c(w_col_s, np.uint8)), k, _p(s), s.size, _p(sel),
+                                    _p(_c(w_col_s, np.uint8)), k, _p(s), s.size, recipe, _p(sel),
                                     0 if sel is None else sel.size, _p(out))
     if rc != 0:
         raise ValueError(f"oracle_grouped_dgrad failed ({rc})")

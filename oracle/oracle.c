@@ -23,6 +23,10 @@
  *    saturate to 448 (never reached by either recipe for finite input); the sign is kept.
  *  - MXFP8 1x32 scale: the smallest power of two 2^e, e in [-127, 127], with amax <= 448 * 2^e;
  *    amax == 0 gives e = -127 (byte 0).  Stored as the E8M0 byte e + 127.
+ *  - MXFP4 (the 4-bit member of the same block-scaled family, next to MXFP8): e2m1 is OCP FP4
+ *    E2M1 (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives); rounding to nearest, ties to
+ *    the even code; the scale is the smallest 2^e, e in [-127, 127], with amax <= 6 * 2^e.  Two
+ *    codes share a byte along the contiguous axis: element 2i in bits 3..0, 2i+1 in bits 7..4.
  *  - Scale blocks restart at every group start; a partial block takes its amax over live rows.
  *  - Rows at or past sum(split_sizes) are outside every group and are never read.
  *
@@ -34,6 +38,8 @@
  *  colwise PC128  : fp32 (e, b, c)  at C*P_e/128 + b*C + c,  b < Kp_e/128
  *  rowwise data   : byte (r, c)     at r*C + c
  *  rowwise MX     : E8M0 (r, b)     at b*R + r,              b < C/32
+ *  MXFP4          : the same element indices as MXFP8; element i of a data buffer is nibble
+ *                   i % 2 of byte i / 2 (so every data buffer has half the bytes)
  *
  * Parity unpinned: none of the functions below; every function has at least one test that pins
  * it to a value fixed by the pages, a library routine, exact arithmetic or brute force.
@@ -52,6 +58,7 @@
 
 #define RECIPE_MX 1  /* MXFP8: one E8M0 power-of-two scale per 32 elements */
 #define RECIPE_PC 2  /* per channel, one fp32 scale per 128 rows (the DeepGEMM reproducer's cast) */
+#define RECIPE_MX4 3 /* MXFP4: e2m1 elements, one E8M0 power-of-two scale per 32 elements */
 #define WHICH_ROW 1
 #define WHICH_COL 2
 
@@ -144,6 +151,87 @@ void oracle_e8m0_exponent_array(const float* amax, int32_t* out, int64_t n) {
   for (i = 0; i < n; ++i) out[i] = oracle_e8m0_exponent(amax[i]);
 }
 
+/* ------------------------------------------------------------------------------------------ */
+/* OCP FP4 E2M1 codec and the MXFP4 scale exponent.                                            */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Value of an e2m1 code (low 4 bits of q): sign bit 3, exponent bits 2..1 with bias 1, mantissa
+ * bit 0.  Exponent field 0 is subnormal (m * 2^-1); every code is finite. */
+double oracle_e2m1_decode(uint8_t q) {
+  int sign = (q >> 3) & 1;
+  int ef = (q >> 1) & 3;
+  int mf = q & 1;
+  double mag = ef == 0 ? 0.5 * mf : ldexp(1.0 + mf / 2.0, ef - 1);
+  return sign ? -mag : mag;
+}
+
+/* Nearest e2m1 code to v, by the same placement rule as the e4m3 encoder over the 8
+ * non-negative magnitudes (codes 0..7): closer neighbour wins, a tie goes to the code whose
+ * mantissa bit is 0; magnitudes >= 6 give 6 (the MXFP4 recipe never exceeds 6). */
+uint8_t oracle_e2m1_encode(float v) {
+  uint8_t sign = signbit(v) ? 0x8 : 0x0;
+  double a = fabs((double)v), dlo, dhi;
+  int lo, hi;
+  if (a >= 6.0) return sign | 7;
+  lo = 0;  /* invariant: mag(lo) <= a < mag(hi) */
+  hi = 7;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (oracle_e2m1_decode((uint8_t)mid) <= a)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  dlo = a - oracle_e2m1_decode((uint8_t)lo);
+  dhi = oracle_e2m1_decode((uint8_t)hi) - a;
+  if (dlo < dhi) return sign | (uint8_t)lo;
+  if (dhi < dlo) return sign | (uint8_t)hi;
+  return sign | (uint8_t)((lo & 1) ? hi : lo);
+}
+
+void oracle_e2m1_encode_array(const float* v, uint8_t* out, int64_t n) {
+  int64_t i;
+  for (i = 0; i < n; ++i) out[i] = oracle_e2m1_encode(v[i]);
+}
+
+/* MXFP4 scale exponent: smallest e in [-127, 127] with amax <= 6 * 2^e (amax == 0 -> -127);
+ * the same bisection as the MXFP8 rule with the e2m1 maximum. */
+int oracle_e8m0_exponent_fp4(float amax) {
+  int lo = -127, hi = 127;
+  if (!(amax > 0.0f)) return -127;
+  if ((double)amax <= ldexp(6.0, lo)) return lo;
+  if (!((double)amax <= ldexp(6.0, hi))) return hi; /* unreachable for finite bf16 input */
+  while (hi - lo > 1) {
+    int mid = lo + (hi - lo) / 2;
+    if ((double)amax <= ldexp(6.0, mid))
+      hi = mid;
+    else
+      lo = mid;
+  }
+  return hi;
+}
+
+void oracle_e8m0_exponent_fp4_array(const float* amax, int32_t* out, int64_t n) {
+  int64_t i;
+  for (i = 0; i < n; ++i) out[i] = oracle_e8m0_exponent_fp4(amax[i]);
+}
+
+/* Element i of a data buffer: an e4m3 byte, or nibble i % 2 of byte i / 2 for MXFP4. */
+static double elem_value(const uint8_t* q, int64_t i, int recipe) {
+  if (recipe == RECIPE_MX4) return oracle_e2m1_decode((uint8_t)((q[i / 2] >> (4 * (i % 2))) & 15));
+  return oracle_e4m3_decode(q[i]);
+}
+
+/* Stores code c (a byte, or a nibble for MXFP4) as element i of a data buffer. */
+static void elem_store(uint8_t* q, int64_t i, uint8_t c, int recipe) {
+  if (recipe == RECIPE_MX4) {
+    int sh = 4 * (int)(i % 2);
+    q[i / 2] = (uint8_t)((q[i / 2] & ~(15 << sh)) | ((c & 15) << sh));
+  } else {
+    q[i] = c;
+  }
+}
+
 /* bf16 bit pattern -> fp32 (exact: bf16 is the top half of an fp32). */
 static float bf16_to_f32(uint16_t h) {
   uint32_t u = (uint32_t)h << 16;
@@ -212,9 +300,9 @@ static float pc_block(const float* vals, int64_t nlive, float zero_amax_scale, u
   return sf;
 }
 
-/* MXFP8 cast of one block of up to 32 live elements: E8M0 exponent from the block amax, each
- * element scaled by 2^-e (exact) and converted.  Returns the exponent e. */
-static int mx_block(const float* vals, int64_t nlive, uint8_t* q) {
+/* MXFP8 / MXFP4 cast of one block of up to 32 live elements: E8M0 exponent from the block
+ * amax, each element scaled by 2^-e (exact) and converted to e4m3 or e2m1.  Returns e. */
+static int mx_block(const float* vals, int64_t nlive, int recipe, uint8_t* q) {
   float amax = 0.0f;
   int64_t i;
   int e;
@@ -222,10 +310,10 @@ static int mx_block(const float* vals, int64_t nlive, uint8_t* q) {
     float a = fabsf(vals[i]);
     if (a > amax) amax = a;
   }
-  e = oracle_e8m0_exponent(amax);
+  e = recipe == RECIPE_MX4 ? oracle_e8m0_exponent_fp4(amax) : oracle_e8m0_exponent(amax);
   for (i = 0; i < nlive; ++i) {
     double v = ldexp((double)vals[i], -e); /* exact power-of-two scaling */
-    q[i] = oracle_e4m3_encode((float)v);
+    q[i] = recipe == RECIPE_MX4 ? oracle_e2m1_encode((float)v) : oracle_e4m3_encode((float)v);
   }
   return e;
 }
@@ -233,8 +321,9 @@ static int mx_block(const float* vals, int64_t nlive, uint8_t* q) {
 /*
  * in      : bf16 [R][C] row-major (bit patterns); rows >= sum(split_sizes) are never read.
  * splits  : host array of E group sizes, or NULL (rowwise only: all R rows live).
- * row_q   : [R][C] e4m3 (rowwise, MX only);  row_s : E8M0 [C/32][R]
- * col_q   : C * sum(Kp_e) bytes;  col_s : E8M0 C*sum(Kp_e)/32 bytes (MX) or fp32 C*sum(Kp_e)/128
+ * row_q   : [R][C] e4m3 (rowwise, MX only; MXFP4: [R][C/2] packed e2m1);  row_s : E8M0 [C/32][R]
+ * col_q   : C * sum(Kp_e) bytes (MXFP4: half);  col_s : E8M0 C*sum(Kp_e)/32 bytes (MX, MXFP4)
+ *           or fp32 C*sum(Kp_e)/128 (per-channel)
  * Only live rows are written for the rowwise outputs; the colwise outputs are written in full.
  */
 int oracle_grouped_quantize(const uint16_t* in, int64_t R, int64_t C, const int32_t* splits,
@@ -244,8 +333,8 @@ int oracle_grouped_quantize(const uint16_t* in, int64_t R, int64_t C, const int3
   group_t all;
   int32_t ng, e;
   if (C <= 0 || C % 32 != 0 || R < 0) return ORACLE_EINVAL;
-  if (recipe != RECIPE_MX && recipe != RECIPE_PC) return ORACLE_EINVAL;
-  if ((which & WHICH_ROW) && recipe != RECIPE_MX) return ORACLE_EINVAL;
+  if (recipe != RECIPE_MX && recipe != RECIPE_PC && recipe != RECIPE_MX4) return ORACLE_EINVAL;
+  if ((which & WHICH_ROW) && recipe == RECIPE_PC) return ORACLE_EINVAL;
   if (splits == NULL) {
     if (which & WHICH_COL) return ORACLE_EINVAL;
     all.k = R; all.off = 0; all.kp = 128 * ((R + 127) / 128); all.p = 0;
@@ -271,8 +360,8 @@ int oracle_grouped_quantize(const uint16_t* in, int64_t R, int64_t C, const int3
         for (b = 0; b < C / 32; ++b) {
           int i, ex;
           for (i = 0; i < 32; ++i) vals[i] = bf16_to_f32(in[r * C + b * 32 + i]);
-          ex = mx_block(vals, 32, q);
-          for (i = 0; i < 32; ++i) row_q[r * C + b * 32 + i] = q[i];
+          ex = mx_block(vals, 32, recipe, q);
+          for (i = 0; i < 32; ++i) elem_store(row_q, r * C + b * 32 + i, q[i], recipe);
           row_s[b * R + r] = (uint8_t)(ex + 127);
         }
       }
@@ -282,7 +371,7 @@ int oracle_grouped_quantize(const uint16_t* in, int64_t R, int64_t C, const int3
   /* Colwise: per group, per channel, blocks of 32 (MX) or 128 (PC) rows starting at the group
    * start; written K-major (the token index contiguous) into the group's packed slot. */
   if (which & WHICH_COL) {
-    int64_t blk = recipe == RECIPE_MX ? 32 : 128;
+    int64_t blk = recipe == RECIPE_PC ? 128 : 32;
     for (e = 0; e < ng; ++e) {
       int64_t c;
       int64_t k = g[e].k, kp = g[e].kp, P = g[e].p, off = g[e].off;
@@ -291,21 +380,21 @@ int oracle_grouped_quantize(const uint16_t* in, int64_t R, int64_t C, const int3
         int64_t b, t;
         float vals[128];
         uint8_t q[128];
-        uint8_t* dst = col_q + C * P + c * kp;
+        int64_t base = C * P + c * kp; /* element index of the channel's first row */
         for (b = 0; b < kp / blk; ++b) {
           int64_t t0 = b * blk;
           int64_t nlive = k - t0;
           if (nlive > blk) nlive = blk;
           if (nlive < 0) nlive = 0;
           for (t = 0; t < nlive; ++t) vals[t] = bf16_to_f32(in[(off + t0 + t) * C + c]);
-          if (recipe == RECIPE_MX) {
-            int ex = mx_block(vals, nlive, q);
-            ((uint8_t*)col_s)[C * P / 32 + b * C + c] = (uint8_t)(ex + 127);
-          } else {
+          if (recipe == RECIPE_PC) {
             float sf = pc_block(vals, nlive, zero_amax_scale, q);
             ((float*)col_s)[C * P / 128 + b * C + c] = sf;
+          } else {
+            int ex = mx_block(vals, nlive, recipe, q);
+            ((uint8_t*)col_s)[C * P / 32 + b * C + c] = (uint8_t)(ex + 127);
           }
-          for (t = 0; t < blk; ++t) dst[t0 + t] = t < nlive ? q[t] : 0x00;
+          for (t = 0; t < blk; ++t) elem_store(col_q, base + t0 + t, t < nlive ? q[t] : 0x00, recipe);
         }
       }
     }
@@ -321,8 +410,8 @@ int oracle_grouped_quantize(const uint16_t* in, int64_t R, int64_t C, const int3
 /* Dequantized colwise element (e, t, c): dec(q) times its block scale. */
 static double col_value(const uint8_t* q, const void* s, int recipe, int64_t C, const group_t* ge,
                         int64_t t, int64_t c) {
-  double d = oracle_e4m3_decode(q[C * ge->p + c * ge->kp + t]);
-  if (recipe == RECIPE_MX) {
+  double d = elem_value(q, C * ge->p + c * ge->kp + t, recipe);
+  if (recipe != RECIPE_PC) {
     int byte = ((const uint8_t*)s)[C * ge->p / 32 + (t / 32) * C + c];
     return d * ldexp(1.0, byte - 127);
   }
@@ -348,7 +437,8 @@ int oracle_grouped_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, const
   group_t* g;
   int32_t e;
   int64_t ns = rows_sel ? n_sel : n;
-  if (E <= 0 || n <= 0 || h <= 0 || (recipe != RECIPE_MX && recipe != RECIPE_PC)) return ORACLE_EINVAL;
+  if (E <= 0 || n <= 0 || h <= 0 || (recipe != RECIPE_MX && recipe != RECIPE_PC && recipe != RECIPE_MX4))
+    return ORACLE_EINVAL;
   if (accumulate && !mg_in) return ORACLE_EINVAL;
   g = (group_t*)malloc(sizeof(group_t) * (size_t)E);
   if (!g) return ORACLE_ENOMEM;
@@ -396,18 +486,20 @@ int oracle_grouped_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, const
 /* ------------------------------------------------------------------------------------------ */
 
 /*
- * x_q [R][K], x_s E8M0 [K/32][R]; w_q [E*N][K], w_s E8M0 [K/32][E*N].
+ * x_q [R][K], x_s E8M0 [K/32][R]; w_q [E*N][K], w_s E8M0 [K/32][E*N] (recipe MX or MXFP4; the
+ * data element indices are those of the [R][K] / [E*N][K] matrices).
  * cols_sel : NULL for all N columns, else n_sel column indices j.  out : fp64 [R][n_sel].
  */
 int oracle_grouped_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R, int64_t K,
                          const uint8_t* w_q, const uint8_t* w_s, int64_t N,
-                         const int32_t* splits, int32_t E, const int32_t* cols_sel,
+                         const int32_t* splits, int32_t E, int recipe, const int32_t* cols_sel,
                          int32_t n_sel, double* out) {
   group_t* g;
   int32_t e;
   int64_t ns = cols_sel ? n_sel : N;
   int64_t WR = (int64_t)E * N; /* rows of the weight buffer */
-  if (E <= 0 || K <= 0 || K % 32 != 0 || N <= 0) return ORACLE_EINVAL;
+  if (E <= 0 || K <= 0 || K % 32 != 0 || N <= 0 || (recipe != RECIPE_MX && recipe != RECIPE_MX4))
+    return ORACLE_EINVAL;
   g = (group_t*)malloc(sizeof(group_t) * (size_t)E);
   if (!g) return ORACLE_ENOMEM;
   if (group_layout(splits, E, R, g) != ORACLE_OK) { free(g); return ORACLE_EINVAL; }
@@ -420,8 +512,7 @@ int oracle_grouped_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R, int6
     for (jj = 0; jj < ns; ++jj) {
       int64_t wr = (int64_t)e * N + (cols_sel ? cols_sel[jj] : jj);
       for (kk = 0; kk < K; ++kk)
-        w[jj * K + kk] = oracle_e4m3_decode(w_q[wr * K + kk]) *
-                         ldexp(1.0, (int)w_s[(kk / 32) * WR + wr] - 127);
+        w[jj * K + kk] = elem_value(w_q, wr * K + kk, recipe) * ldexp(1.0, (int)w_s[(kk / 32) * WR + wr] - 127);
     }
 #pragma omp parallel private(jj, kk)
     {
@@ -431,7 +522,7 @@ int oracle_grouped_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R, int6
         int64_t r = g[e].off + t;
         if (!xr) continue;
         for (kk = 0; kk < K; ++kk)
-          xr[kk] = oracle_e4m3_decode(x_q[r * K + kk]) * ldexp(1.0, (int)x_s[(kk / 32) * R + r] - 127);
+          xr[kk] = elem_value(x_q, r * K + kk, recipe) * ldexp(1.0, (int)x_s[(kk / 32) * R + r] - 127);
         for (jj = 0; jj < ns; ++jj) {
           double s = 0.0;
           for (kk = 0; kk < K; ++kk) s += xr[kk] * w[jj * K + kk];
@@ -458,17 +549,19 @@ int oracle_grouped_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R, int6
  * as E groups of n rows [E*n][k]: group e has P_e = e*np rows packed (np = 128 * ceil(n/128)), so
  * its byte (c, j) -- row c of the group, channel j -- sits at k*np*e + j*np + c and its E8M0
  * scale (b = c/32, j) at k*np*e/32 + b*k + j (the colwise layout above with C = k).
+ * Recipe MX or MXFP4 (element indices as above; MXFP4 packs two per byte).
  * cols_sel : NULL for all k columns, else n_sel column indices j.  out : fp64 [R][n_sel].
  */
 int oracle_grouped_dgrad(const uint8_t* dy_q, const uint8_t* dy_s, int64_t R, int64_t n,
                          const uint8_t* w_q, const uint8_t* w_s, int64_t k,
-                         const int32_t* splits, int32_t E, const int32_t* cols_sel,
+                         const int32_t* splits, int32_t E, int recipe, const int32_t* cols_sel,
                          int32_t n_sel, double* out) {
   group_t* g;
   int32_t e;
   int64_t ns = cols_sel ? n_sel : k;
   int64_t np = 128 * ((n + 127) / 128);
-  if (E <= 0 || n <= 0 || n % 32 != 0 || k <= 0 || k % 32 != 0) return ORACLE_EINVAL;
+  if (E <= 0 || n <= 0 || n % 32 != 0 || k <= 0 || k % 32 != 0 || (recipe != RECIPE_MX && recipe != RECIPE_MX4))
+    return ORACLE_EINVAL;
   g = (group_t*)malloc(sizeof(group_t) * (size_t)E);
   if (!g) return ORACLE_ENOMEM;
   if (group_layout(splits, E, R, g) != ORACLE_OK) { free(g); return ORACLE_EINVAL; }
@@ -481,7 +574,7 @@ int oracle_grouped_dgrad(const uint8_t* dy_q, const uint8_t* dy_s, int64_t R, in
     for (jj = 0; jj < ns; ++jj) {
       int64_t j = cols_sel ? cols_sel[jj] : jj;
       for (c = 0; c < n; ++c)
-        w[jj * n + c] = oracle_e4m3_decode(w_q[k * np * e + j * np + c]) *
+        w[jj * n + c] = elem_value(w_q, k * np * e + j * np + c, recipe) *
                         ldexp(1.0, (int)w_s[k * np * e / 32 + (c / 32) * k + j] - 127);
     }
 #pragma omp parallel private(jj, c)
@@ -492,7 +585,7 @@ int oracle_grouped_dgrad(const uint8_t* dy_q, const uint8_t* dy_s, int64_t R, in
         int64_t r = g[e].off + t;
         if (!yr) continue;
         for (c = 0; c < n; ++c)
-          yr[c] = oracle_e4m3_decode(dy_q[r * n + c]) * ldexp(1.0, (int)dy_s[(c / 32) * R + r] - 127);
+          yr[c] = elem_value(dy_q, r * n + c, recipe) * ldexp(1.0, (int)dy_s[(c / 32) * R + r] - 127);
         for (jj = 0; jj < ns; ++jj) {
           double s = 0.0;
           for (c = 0; c < n; ++c) s += yr[c] * w[jj * n + c];
