@@ -41,6 +41,7 @@ if ROOT not in sys.path:
 METRIC = "grouped FP8 wgrad TFLOP/s (useful FLOPs) and % of FP8 MFMA peak, 1 GPU"
 PEAK_BF16_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (the instruction the GEMMs run on)
 PEAK_FP8_MFMA_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_FP4_MFMA_TFLOPS = 10100.0   # MI355X dense fp4 MFMA (the MXFP4 GEMMs run on it)
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wgrad_moe128_traffic.json")
 
@@ -135,6 +136,48 @@ def graph_leg(graph_step, flag, stream):
     return graph_ms
 
 
+def mxfp4_leg(bs, W, case, st, R, n, h, K, N, E, mg, status, stream):
+    """Quantize x (row+col), dy (col), W (row) to MXFP4, wgrad into main_grad, fprop bf16: mean
+    per-kernel times over 3 steps after one warmup step."""
+    import torch
+    log("mxfp4 leg")
+    M4 = bs.RECIPE_MX4
+    xq = bs.alloc_quantized(R, h, E, M4, bs.COLWISE | bs.ROWWISE)
+    dq = bs.alloc_quantized(R, n, E, M4, bs.COLWISE)
+    wq = bs.alloc_quantized(E * N, K, 1, M4, bs.ROWWISE)
+    fout = torch.empty(R, N, dtype=torch.bfloat16, device="cuda")
+    w2 = case["W"].view(E * N, K)
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        bs.grouped_quantize(case["x"], st, M4, bs.COLWISE | bs.ROWWISE, xq, status=status)
+        mark(1)
+        bs.grouped_quantize(case["dy"], st, M4, bs.COLWISE, dq, status=status)
+        mark(2)
+        bs.grouped_quantize(w2, None, M4, bs.ROWWISE, wq)
+        mark(3)
+        bs.grouped_gemm_wgrad(dq, n, xq, h, st, R, M4, mg, accumulate=True, status=status)
+        mark(4)
+        bs.grouped_gemm_fprop(xq, K, wq, N, st, R, fout, bs.OUT_BF16, status=status, recipe=M4)
+        mark(5)
+
+    step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(3)]
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    names = ["quantize_x", "quantize_dy", "quantize_w", "wgrad", "fprop"]
+    ms = {nm: sum(ev[i].elapsed_time(ev[i + 1]) for ev in evs) / len(evs) for i, nm in enumerate(names)}
+    ms["step"] = sum(ev[0].elapsed_time(ev[5]) for ev in evs) / len(evs)
+    del xq, dq, wq, fout
+    return ms
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +187,7 @@ def main():
                     help="experts in the CPU-baseline sample (0 skips it)")
     ap.add_argument("--cpu-channels", type=int, default=2048, help="dy channels per sampled expert")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay leg")
+    ap.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4 leg")
     ap.add_argument("--calibrate-copy-gb", type=float, default=0.0,
                     help="after the timed region, run one device copy of this many GB (for counter "
                          "calibration against a kernel of known traffic)")
@@ -263,6 +307,12 @@ def main():
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())}")
 
+    # The same step with the MXFP4 recipe (e2m1 operands on the scaled fp4 MFMA), timed on its own
+    # after the MXFP8 step; not part of `value`.
+    mx4 = None
+    if not args.no_mxfp4:
+        mx4 = mxfp4_leg(bs, W, case, st, R, n, h, K, N, E, mg, status, stream)
+
     wgrad_flop = 2.0 * n * h * T
     fprop_flop = 2.0 * T * K * N
     # algorithmic HBM bytes: bf16 read once, e4m3 + E8M0 written once per requested layout
@@ -326,6 +376,17 @@ def main():
             "dgrad": {"ms": round(dleg[2], 3), "TFLOP/s": round(2.0 * T * N * K / (dleg[2] / 1e3) / 1e12, 1)},
         },
     }
+    if mx4 is not None:
+        T4 = 2.0 * n * h * T
+        out["mxfp4"] = {
+            "ms_per_step": round(mx4["step"], 3),
+            "wgrad_TFLOP/s_of_step": round(T4 / (mx4["step"] / 1e3) / 1e12, 2),
+            "legs_ms": {k: round(v, 3) for k, v in mx4.items() if k != "step"},
+            "wgrad_TFLOP/s": round(T4 / (mx4["wgrad"] / 1e3) / 1e12, 1),
+            "fprop_TFLOP/s": round(2.0 * T * K * N / (mx4["fprop"] / 1e3) / 1e12, 1),
+            "wgrad_frac_of_fp4_peak": round(T4 / (mx4["wgrad"] / 1e3) / 1e12 / PEAK_FP4_MFMA_TFLOPS, 4),
+            "note": "the same step with the MXFP4 recipe (e2m1 + E8M0, scaled fp4 MFMA); not part of value",
+        }
     if graph_ms is not None:
         out["graph"] = {"ms_per_step": round(graph_ms["replay"], 3),
                         "ms_per_step_cached_weight": round(graph_ms["replay_cached_weight"], 3),

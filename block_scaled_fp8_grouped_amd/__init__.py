@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libbsfp8.so")
 
 RECIPE_MX = 1  # BSFP8_RECIPE_MX_1X32_E8M0
 RECIPE_PC = 2  # BSFP8_RECIPE_PER_CHANNEL_128_F32
+RECIPE_MX4 = 3  # BSFP8_RECIPE_MXFP4_1X32_E8M0
 ROWWISE = 1
 COLWISE = 2
 OUT_F32 = 0
@@ -51,11 +52,11 @@ def lib():
         L.bsfp8_colwise_rows_bound.restype = _i64
         L.bsfp8_colwise_rows_bound.argtypes = [_i64, _i32]
         L.bsfp8_colwise_data_bytes.restype = _sz
-        L.bsfp8_colwise_data_bytes.argtypes = [_i64, _i64, _i32]
+        L.bsfp8_colwise_data_bytes.argtypes = [_i64, _i64, _i32, ctypes.c_int]
         L.bsfp8_colwise_scale_bytes.restype = _sz
         L.bsfp8_colwise_scale_bytes.argtypes = [_i64, _i64, _i32, ctypes.c_int]
         L.bsfp8_rowwise_data_bytes.restype = _sz
-        L.bsfp8_rowwise_data_bytes.argtypes = [_i64, _i64]
+        L.bsfp8_rowwise_data_bytes.argtypes = [_i64, _i64, ctypes.c_int]
         L.bsfp8_rowwise_scale_bytes.restype = _sz
         L.bsfp8_rowwise_scale_bytes.argtypes = [_i64, _i64]
         L.bsfp8_grouped_quantize.restype = ctypes.c_int
@@ -65,10 +66,10 @@ def lib():
         L.bsfp8_grouped_gemm_wgrad.argtypes = [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i64, ctypes.c_int,
                                                _vp, ctypes.c_int, _vp, _vp]
         L.bsfp8_grouped_gemm_fprop.restype = ctypes.c_int
-        L.bsfp8_grouped_gemm_fprop.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i32, _vp,
+        L.bsfp8_grouped_gemm_fprop.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i32, ctypes.c_int, _vp,
                                                ctypes.c_int, _vp, _vp]
         L.bsfp8_grouped_gemm_dgrad.restype = ctypes.c_int
-        L.bsfp8_grouped_gemm_dgrad.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i32, _vp,
+        L.bsfp8_grouped_gemm_dgrad.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i32, ctypes.c_int, _vp,
                                                ctypes.c_int, _vp, _vp]
         L.bsfp8_strerror.restype = ctypes.c_char_p
         L.bsfp8_strerror.argtypes = [ctypes.c_int]
@@ -107,16 +108,16 @@ def colwise_rows_bound(capacity_rows, num_groups):
     return int(lib().bsfp8_colwise_rows_bound(capacity_rows, num_groups))
 
 
-def colwise_data_bytes(capacity_rows, cols, num_groups):
-    return int(lib().bsfp8_colwise_data_bytes(capacity_rows, cols, num_groups))
+def colwise_data_bytes(capacity_rows, cols, num_groups, recipe=RECIPE_MX):
+    return int(lib().bsfp8_colwise_data_bytes(capacity_rows, cols, num_groups, recipe))
 
 
 def colwise_scale_bytes(capacity_rows, cols, num_groups, recipe):
     return int(lib().bsfp8_colwise_scale_bytes(capacity_rows, cols, num_groups, recipe))
 
 
-def rowwise_data_bytes(rows, cols):
-    return int(lib().bsfp8_rowwise_data_bytes(rows, cols))
+def rowwise_data_bytes(rows, cols, recipe=RECIPE_MX):
+    return int(lib().bsfp8_rowwise_data_bytes(rows, cols, recipe))
 
 
 def rowwise_scale_bytes(rows, cols):
@@ -126,17 +127,19 @@ def rowwise_scale_bytes(rows, cols):
 def alloc_quantized(capacity_rows, cols, num_groups, recipe, which, device="cuda"):
     """Output tensors for grouped_quantize, sized by the library's size queries.
 
-    Returns a dict with row_q uint8 [R, C], row_s uint8 [C/32, R], col_q uint8 [bytes],
-    col_s uint8 [bytes] (MX) or float32 [bytes/4] (per-channel), for the requested layouts."""
+    Returns a dict with row_q uint8 [R, C] (MXFP4: [R, C/2]), row_s uint8 [C/32, R], col_q uint8
+    [bytes], col_s uint8 [bytes] (MX recipes) or float32 [bytes/4] (per-channel), for the
+    requested layouts."""
     out = {}
     if which & ROWWISE:
-        out["row_q"] = torch.empty((capacity_rows, cols), dtype=torch.uint8, device=device)
+        per = 2 if recipe == RECIPE_MX4 else 1
+        out["row_q"] = torch.empty((capacity_rows, cols // per), dtype=torch.uint8, device=device)
         out["row_s"] = torch.empty((cols // 32, capacity_rows), dtype=torch.uint8, device=device)
     if which & COLWISE:
-        out["col_q"] = torch.empty(colwise_data_bytes(capacity_rows, cols, num_groups), dtype=torch.uint8,
+        out["col_q"] = torch.empty(colwise_data_bytes(capacity_rows, cols, num_groups, recipe), dtype=torch.uint8,
                                    device=device)
         nb = colwise_scale_bytes(capacity_rows, cols, num_groups, recipe)
-        if recipe == RECIPE_MX:
+        if recipe != RECIPE_PC:
             out["col_s"] = torch.empty(nb, dtype=torch.uint8, device=device)
         else:
             out["col_s"] = torch.empty(nb // 4, dtype=torch.float32, device=device)
@@ -178,26 +181,27 @@ def grouped_gemm_wgrad(dy_q, n, x_q, h, split_sizes, capacity_rows, recipe, out,
 
 
 def grouped_gemm_fprop(x_q, k, w_q, n, split_sizes, capacity_rows, out, out_dtype=OUT_F32, status=None,
-                       stream=None):
+                       stream=None, recipe=RECIPE_MX):
     """bsfp8_grouped_gemm_fprop: x_q is the rowwise dict of x [R, k], w_q the rowwise dict of the
-    weight [E*n, k]; out is [R, n] fp32 or bf16 (rows past sum(split_sizes) untouched)."""
+    weight [E*n, k], both of ``recipe`` (MX or MX4); out is [R, n] fp32 or bf16 (rows past
+    sum(split_sizes) untouched)."""
     E = int(split_sizes.numel())
     rc = lib().bsfp8_grouped_gemm_fprop(_ptr(x_q["row_q"]), _ptr(x_q["row_s"]), capacity_rows, k,
-                                        _ptr(w_q["row_q"]), _ptr(w_q["row_s"]), n, _ptr(split_sizes), E,
+                                        _ptr(w_q["row_q"]), _ptr(w_q["row_s"]), n, _ptr(split_sizes), E, recipe,
                                         _ptr(out), out_dtype, _ptr(status), _stream(stream))
     _check(rc, "grouped_gemm_fprop")
     return out
 
 
 def grouped_gemm_dgrad(dy_q, n, w_q, k, split_sizes, capacity_rows, out, out_dtype=OUT_F32, status=None,
-                       stream=None):
+                       stream=None, recipe=RECIPE_MX):
     """bsfp8_grouped_gemm_dgrad: dy_q is the rowwise dict of dy [R, n]; w_q the colwise dict of the
     weight viewed as [E*n, k] quantized with split sizes [n] * E (blocks of 32 along n inside each
     expert); out is [R, k] fp32 or bf16: out[off_e + t] = dy[off_e + t] @ W_e (rows past
     sum(split_sizes) untouched)."""
     E = int(split_sizes.numel())
     rc = lib().bsfp8_grouped_gemm_dgrad(_ptr(dy_q["row_q"]), _ptr(dy_q["row_s"]), capacity_rows, n,
-                                        _ptr(w_q["col_q"]), _ptr(w_q["col_s"]), k, _ptr(split_sizes), E,
+                                        _ptr(w_q["col_q"]), _ptr(w_q["col_s"]), k, _ptr(split_sizes), E, recipe,
                                         _ptr(out), out_dtype, _ptr(status), _stream(stream))
     _check(rc, "grouped_gemm_dgrad")
     return out

@@ -16,18 +16,24 @@ int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, 
                               int64_t h, const int32_t* splits, int E, int64_t R, int recipe, float* out,
                               int accumulate, uint32_t* status, hipStream_t stream);
 int launch_grouped_gemm_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R, int64_t K, const uint8_t* w_q,
-                              const uint8_t* w_s, int64_t N, const int32_t* splits, int E, void* out, int out_dtype,
-                              uint32_t* status, hipStream_t stream);
+                              const uint8_t* w_s, int64_t N, const int32_t* splits, int E, int recipe, void* out,
+                              int out_dtype, uint32_t* status, hipStream_t stream);
 int launch_grouped_gemm_dgrad(const uint8_t* dy_q, const uint8_t* dy_s, int64_t R, int64_t n, const uint8_t* w_q,
-                              const void* w_s, int64_t k, const int32_t* splits, int E, void* out, int out_dtype,
-                              uint32_t* status, hipStream_t stream);
+                              const void* w_s, int64_t k, const int32_t* splits, int E, int recipe, void* out,
+                              int out_dtype, uint32_t* status, hipStream_t stream);
 }  // namespace bsfp8
 
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
-bool valid_recipe(int r) { return r == BSFP8_RECIPE_MX_1X32_E8M0 || r == BSFP8_RECIPE_PER_CHANNEL_128_F32; }
+bool valid_recipe(int r) {
+  return r == BSFP8_RECIPE_MX_1X32_E8M0 || r == BSFP8_RECIPE_PER_CHANNEL_128_F32 || r == BSFP8_RECIPE_MXFP4_1X32_E8M0;
+}
+// recipes with E8M0 block scales (both layouts; the only ones the m-grouped GEMMs take)
+bool mx_recipe(int r) { return r == BSFP8_RECIPE_MX_1X32_E8M0 || r == BSFP8_RECIPE_MXFP4_1X32_E8M0; }
+// data elements per byte
+int64_t per_byte(int r) { return r == BSFP8_RECIPE_MXFP4_1X32_E8M0 ? 2 : 1; }
 bool valid_groups(int32_t e) { return e > 0 && e <= BSFP8_MAX_GROUPS; }
 // dims must be positive multiples of 32 and small enough that byte offsets fit in int64
 bool valid_dim(int64_t d) { return d > 0 && d % 32 == 0 && d <= (int64_t(1) << 40); }
@@ -48,21 +54,21 @@ int64_t bsfp8_colwise_rows_bound(int64_t capacity_rows, int32_t num_groups) {
   return 128 * ((capacity_rows + 127 * (int64_t)num_groups) / 128);
 }
 
-size_t bsfp8_colwise_data_bytes(int64_t capacity_rows, int64_t cols, int32_t num_groups) {
-  if (!valid_dim(cols)) return 0;
-  return (size_t)bsfp8_colwise_rows_bound(capacity_rows, num_groups) * (size_t)cols;
+size_t bsfp8_colwise_data_bytes(int64_t capacity_rows, int64_t cols, int32_t num_groups, int recipe) {
+  if (!valid_dim(cols) || !valid_recipe(recipe)) return 0;
+  return (size_t)bsfp8_colwise_rows_bound(capacity_rows, num_groups) * (size_t)(cols / per_byte(recipe));
 }
 
 size_t bsfp8_colwise_scale_bytes(int64_t capacity_rows, int64_t cols, int32_t num_groups, int recipe) {
   if (!valid_dim(cols) || !valid_recipe(recipe)) return 0;
   const size_t rows = (size_t)bsfp8_colwise_rows_bound(capacity_rows, num_groups);
-  if (recipe == BSFP8_RECIPE_MX_1X32_E8M0) return rows / 32 * (size_t)cols;
+  if (mx_recipe(recipe)) return rows / 32 * (size_t)cols;
   return rows / 128 * (size_t)cols * sizeof(float);
 }
 
-size_t bsfp8_rowwise_data_bytes(int64_t rows, int64_t cols) {
-  if (rows < 0 || !valid_dim(cols)) return 0;
-  return (size_t)rows * (size_t)cols;
+size_t bsfp8_rowwise_data_bytes(int64_t rows, int64_t cols, int recipe) {
+  if (rows < 0 || !valid_dim(cols) || !mx_recipe(recipe)) return 0;
+  return (size_t)rows * (size_t)(cols / per_byte(recipe));
 }
 
 size_t bsfp8_rowwise_scale_bytes(int64_t rows, int64_t cols) {
@@ -76,7 +82,7 @@ int bsfp8_grouped_quantize(const void* in_bf16, int64_t capacity_rows, int64_t c
                            void* stream) {
   if (!valid_recipe(recipe)) return BSFP8_ERR_RECIPE;
   if (which <= 0 || (which & ~(BSFP8_ROWWISE | BSFP8_COLWISE)) != 0) return BSFP8_ERR_ARGUMENT;
-  if ((which & BSFP8_ROWWISE) && recipe != BSFP8_RECIPE_MX_1X32_E8M0) return BSFP8_ERR_LAYOUT;
+  if ((which & BSFP8_ROWWISE) && !mx_recipe(recipe)) return BSFP8_ERR_LAYOUT;
   if (capacity_rows < 0 || !valid_dim(cols)) return BSFP8_ERR_SHAPE;
   if (recipe == BSFP8_RECIPE_PER_CHANNEL_128_F32 && !(isfinite(zero_amax_scale) && zero_amax_scale >= 0.0f))
     return BSFP8_ERR_ARGUMENT;
@@ -120,7 +126,9 @@ int bsfp8_grouped_gemm_wgrad(const uint8_t* dy_col_q, const void* dy_col_s, int6
 
 int bsfp8_grouped_gemm_fprop(const uint8_t* x_row_q, const uint8_t* x_row_s, int64_t capacity_rows, int64_t k,
                              const uint8_t* w_q, const uint8_t* w_s, int64_t n, const int32_t* split_sizes,
-                             int32_t num_groups, void* out, int out_dtype, uint32_t* status, void* stream) {
+                             int32_t num_groups, int recipe, void* out, int out_dtype, uint32_t* status,
+                             void* stream) {
+  if (!mx_recipe(recipe)) return BSFP8_ERR_RECIPE;
   if (!valid_groups(num_groups)) return BSFP8_ERR_NUM_GROUPS;
   if (!valid_dim(k) || !valid_dim(n) || capacity_rows < 0 || k > kMaxKExtent || n > kMaxOutCols)
     return BSFP8_ERR_SHAPE;
@@ -133,12 +141,14 @@ int bsfp8_grouped_gemm_fprop(const uint8_t* x_row_q, const uint8_t* x_row_s, int
       !aligned4(split_sizes) || !aligned4(status))
     return BSFP8_ERR_ALIGNMENT;
   return bsfp8::launch_grouped_gemm_fprop(x_row_q, x_row_s, capacity_rows, k, w_q, w_s, n, split_sizes, num_groups,
-                                          out, out_dtype, status, (hipStream_t)stream);
+                                          recipe, out, out_dtype, status, (hipStream_t)stream);
 }
 
 int bsfp8_grouped_gemm_dgrad(const uint8_t* dy_row_q, const uint8_t* dy_row_s, int64_t capacity_rows, int64_t n,
                              const uint8_t* w_col_q, const void* w_col_s, int64_t k, const int32_t* split_sizes,
-                             int32_t num_groups, void* out, int out_dtype, uint32_t* status, void* stream) {
+                             int32_t num_groups, int recipe, void* out, int out_dtype, uint32_t* status,
+                             void* stream) {
+  if (!mx_recipe(recipe)) return BSFP8_ERR_RECIPE;
   if (!valid_groups(num_groups)) return BSFP8_ERR_NUM_GROUPS;
   // the weight rows are n rounded up to 128: that padded length bounds the 32-bit tile offsets
   if (!valid_dim(n) || !valid_dim(k) || capacity_rows < 0 || n + 127 > kMaxKExtent || k > kMaxOutCols)
@@ -152,7 +162,7 @@ int bsfp8_grouped_gemm_dgrad(const uint8_t* dy_row_q, const uint8_t* dy_row_s, i
       !aligned4(split_sizes) || !aligned4(status))
     return BSFP8_ERR_ALIGNMENT;
   return bsfp8::launch_grouped_gemm_dgrad(dy_row_q, dy_row_s, capacity_rows, n, w_col_q, w_col_s, k, split_sizes,
-                                          num_groups, out, out_dtype, status, (hipStream_t)stream);
+                                          num_groups, recipe, out, out_dtype, status, (hipStream_t)stream);
 }
 
 const char* bsfp8_strerror(int code) {
@@ -163,7 +173,7 @@ const char* bsfp8_strerror(int code) {
     case BSFP8_ERR_RECIPE: return "unknown recipe";
     case BSFP8_ERR_SHAPE: return "a dimension is negative, not a multiple of 32, or too large";
     case BSFP8_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
-    case BSFP8_ERR_LAYOUT: return "rowwise layout needs the MX 1x32 E8M0 recipe";
+    case BSFP8_ERR_LAYOUT: return "rowwise layout needs an MX 1x32 E8M0 recipe (MXFP8 or MXFP4)";
     case BSFP8_ERR_ARGUMENT: return "invalid argument";
     case BSFP8_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown error code";

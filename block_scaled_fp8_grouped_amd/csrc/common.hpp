@@ -42,7 +42,19 @@ __device__ __forceinline__ int e8m0_exponent(float amax) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// 2^-e as an fp32 (exact; e in [-127, 120]).
+// MXFP4 block exponent: smallest e with amax <= 6 * 2^e, clamped to [-127, 127].
+// amax = 1.m * 2^u; 6 = 1.5 * 2^2, so e = u - 2 when 1.m <= 1.5, else u - 1.  fp32 subnormals
+// (and 0) give -127; for finite amax the result is at most 126.
+__device__ __forceinline__ int e8m0_exponent_fp4(float amax) {
+  const uint32_t bits = __float_as_uint(amax);
+  const int ef = (int)((bits >> 23) & 0xffu);
+  if (ef == 0) return -127;
+  const int u = ef - 127;
+  int e = u - 2 + ((bits & 0x7fffffu) > 0x400000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// 2^-e as an fp32 (exact; e in [-127, 126]).
 __device__ __forceinline__ float exp2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
 
 // Two fp32 -> two e4m3 codes in the low 16 bits (round to nearest even, sign kept).
@@ -54,6 +66,17 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
+}
+
+// Eight fp32 -> eight e2m1 codes packed in a dword, element i in bits 4i..4i+3 (round to
+// nearest even, sign kept, magnitudes above 6 saturate; unit conversion scale).
+__device__ __forceinline__ uint32_t e2m1x8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
+                                           float a7) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a0, a1, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a2, a3, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a4, a5, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a6, a7, 1.0f, 3);
+  return w;
 }
 
 // bf16 halves of a dword -> fp32 (exact).

@@ -16,6 +16,12 @@
 // and cannot meet a 1e-5 bound; the bf16 MFMA on the same values is within fp32 rounding.
 // Per-channel recipe (fp32 scales per 128 rows): unit-scale widening, one partial sum p per
 // 128-row K step, folded as acc = fma(p, sa_i * sb_j, acc) in K order.
+// MXFP4 recipe (e2m1, two per byte; TE #3484 additional context: a 4-bit block-scaled quantizer
+// on the same grouped paths): the operands go to the scaled MFMA as they are
+// (v_mfma_scale_f32_32x32x64_f8f6f4 in its fp4 x fp4 form, the E8M0 block scales applied by the
+// instruction).  A lane's 16-byte chunk is exactly one 32-element scale block, and every partial
+// sum of e2m1 products inside a block is a small multiple of 1/4, so the instruction's inner
+// sums are exact and the result is fp32-accumulated like the bf16 path.
 //
 // Tiling.  Workgroup tile BM x BN, K step 128, each wave owning a WM x WN block of 32 x 32
 // fragments.  MX recipe: 256 x 256 with 8 waves of 128 x 64 (two waves per SIMD, 128 fp32
@@ -99,28 +105,35 @@ __device__ __forceinline__ v8bf widen8(int d0, int d1, float scale) {
   return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-template <int MODE, bool PC, int BM, int BN, int WM, int WN>
+template <int MODE, bool PC, bool F4, int BM, int BN, int WM, int WN>
 struct GemmShape {
-  static constexpr int BK = 128;
+  static constexpr int BK = 128;                    // bytes of a row per K step
+  static constexpr int SBLK = F4 ? 8 : 4;           // E8M0 scale blocks per K step (MX recipes)
+  static constexpr int BLK_BYTES = BK / SBLK;       // bytes of one scale block
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int NW = WAVES_M * WAVES_N, NT = NW * 64;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  // LDS stage: A rows, B rows, then scales (MX: [4 blocks][rows] E8M0 bytes as they arrive, and
-  // the same decoded to fp32 [4 blocks][rows]; PC: one fp32 per row)
-  static constexpr int A_OFF = 0, B_OFF = BM * BK, SA_OFF = (BM + BN) * BK, SB_OFF = SA_OFF + BM * 4;
-  static constexpr int SAF_OFF = SB_OFF + BN * 4, SBF_OFF = SAF_OFF + 16 * BM;
-  static constexpr int STAGE = PC ? SB_OFF + BN * 4 : SBF_OFF + 16 * BN;
+  // LDS stage: A rows, B rows, then scales (MX: [SBLK blocks][rows] E8M0 bytes as they arrive,
+  // and for MXFP8 the same decoded to fp32 [4 blocks][rows]; PC: one fp32 per row)
+  static constexpr int A_OFF = 0, B_OFF = BM * BK, SA_OFF = (BM + BN) * BK;
+  static constexpr int SB_OFF = SA_OFF + (PC ? BM * 4 : SBLK * BM);
+  static constexpr int SAF_OFF = SB_OFF + (PC ? BN * 4 : SBLK * BN), SBF_OFF = SAF_OFF + 16 * BM;
+  static constexpr int STAGE = (PC || F4) ? SAF_OFF : SBF_OFF + 16 * BN;
   static constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;  // 1 KB DMA instructions per wave
   static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
   static_assert(A_INS * 8 * NW == BM && B_INS * 8 * NW == BN, "DMA loader shape");
   static_assert(2 * STAGE + (int)sizeof(GroupScanSmem<NT>) <= 160 * 1024, "LDS budget");
 };
 
-// KTAIL (fprop only): K is not a multiple of 128, so the last K step runs past it.
-template <int MODE, bool PC, int BM, int BN, int WM, int WN, bool ACCUM, int OUT, bool KTAIL>
+// KTAIL (MXFP8 fprop only): K is not a multiple of 128, so the last K step runs past it.  MXFP4
+// (F4) decides per group at run time whether its last K step is such a tail step.
+template <int MODE, bool PC, bool F4, int BM, int BN, int WM, int WN, bool ACCUM, int OUT, bool KTAIL>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kernel(GemmArgs args) {
-  using S = GemmShape<MODE, PC, BM, BN, WM, WN>;
+  using S = GemmShape<MODE, PC, F4, BM, BN, WM, WN>;
   constexpr int NT = S::NT, NW = S::NW, BK = S::BK, FM = S::FM, FN = S::FN;
+  constexpr int SBLK = S::SBLK, BLK_BYTES = S::BLK_BYTES;
+  constexpr int EPB = F4 ? 2 : 1;  // elements per data byte
+  static_assert(!(PC && F4) && !(KTAIL && F4), "recipe flags");
   __shared__ GroupScanSmem<NT> gsm;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::STAGE];
 
@@ -166,10 +179,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
       }
       return;
     }
-    lda = ldb = gi.kp;
-    kext = gi.kp;
-    a_data = args.a_q + args.M * gi.p;
-    b_data = args.b_q + args.N * gi.p;
+    lda = ldb = gi.kp / EPB;
+    kext = gi.kp / EPB;
+    a_data = args.a_q + args.M * gi.p / EPB;
+    b_data = args.b_q + args.N * gi.p / EPB;
     a_valid = args.M;
     b_valid = args.N;
     if constexpr (PC) {
@@ -212,7 +225,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   auto dma4 = [&](const void* g, uint8_t* l) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
   };
-  constexpr int FA_ROWS = 4 * BM / NT;  // fprop: A-scale bytes (rows) each thread stages per K step
+  constexpr int FA_ROWS = SBLK * BM / NT;  // fprop: A-scale bytes (rows) each thread stages per K step
   uint8_t fa_b[FA_ROWS];                 // fprop: those bytes, held in registers until settle
   uint32_t a_off[S::A_INS], b_off[S::B_INS];
 #pragma unroll
@@ -223,14 +236,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
     const uint32_t k0 = (uint32_t)kk * BK;
     if constexpr (MODE == kModeFprop) {
       // A scales first: waiting for these register loads (in settle) then does not wait for
-      // the DMAs behind them.  Thread t -> block t / (NT / 4) of this K step, rows
-      // FA_ROWS * (t % (NT / 4)) and the next FA_ROWS - 1 (t / (NT / 4) = wave / (NW / 4),
-      // t % (NT / 4) = (wave % (NW / 4)) * 64 + lane: the block index comes from the scalar wave
-      // index, so the buffer resource below is wave-uniform).
-      static_assert(FA_ROWS == 2 || FA_ROWS == 4, "fprop A-scale staging shape");
-      const int blk = wave / (NW / 4), r0 = FA_ROWS * ((wave % (NW / 4)) * 64 + lane);
-      const int64_t kb = (int64_t)kk * 4 + blk;
-      if (kb * 32 < kext) {
+      // the DMAs behind them.  Thread t -> block t / (NT / SBLK) of this K step, rows
+      // FA_ROWS * (t % (NT / SBLK)) and the next FA_ROWS - 1 (t / (NT / SBLK) = wave / (NW / SBLK),
+      // t % (NT / SBLK) = (wave % (NW / SBLK)) * 64 + lane: the block index comes from the scalar
+      // wave index, so the buffer resource below is wave-uniform).
+      static_assert((FA_ROWS == 2 || FA_ROWS == 4) && NW % SBLK == 0, "fprop A-scale staging shape");
+      const int blk = wave / (NW / SBLK), r0 = FA_ROWS * ((wave % (NW / SBLK)) * 64 + lane);
+      const int64_t kb = (int64_t)kk * SBLK + blk;
+      if (kb * BLK_BYTES < kext) {
         // the group's scale bytes of this block through a buffer resource spanning its valid
         // rows: rows past them read as 0 (their products are never stored)
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -268,7 +281,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
       }
     } else {
       // E8M0 block rows [blk][row]: 4 rows of 4 bytes per lane, 256 bytes per instruction
-      constexpr int SA_INS = 4 * BM / 256, SB_INS = 4 * BN / 256;
+      constexpr int SA_INS = SBLK * BM / 256, SB_INS = SBLK * BN / 256;
       static_assert((SA_INS + SB_INS) % NW == 0, "MX scale loader shape");
 #pragma unroll
       for (int u = 0; u < (SA_INS + SB_INS) / NW; ++u) {
@@ -277,11 +290,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
         const int vv = is_a ? v : v - SA_INS;
         const int per = (is_a ? BM : BN) / 256;
         const int blk = vv / per, part = vv % per;
-        const int64_t kb = (int64_t)kk * 4 + blk;
+        const int64_t kb = (int64_t)kk * SBLK + blk;
         uint8_t* dst = base + (is_a ? S::SA_OFF + blk * BM : S::SB_OFF + blk * BN) + part * 256;
         if (MODE == kModeFprop && is_a) {
-          // rows of a group start anywhere: four single-byte loads per thread instead (below)
-        } else if (MODE == kModeFprop && kb * 32 >= kext) {
+          // rows of a group start anywhere: single-byte loads per thread instead (above)
+        } else if ((MODE == kModeFprop || F4) && kb * BLK_BYTES >= kext) {
           *(uint32_t*)(dst + 4 * lane) = 0x7f7f7f7fu;  // past K: unit scales over zero data
         } else {
           // valid rows are a multiple of 32 here, so a group of 4 is all valid or all past
@@ -296,8 +309,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   // bytes its own scale DMA (or tail store) wrote -- visible to it after its own wait -- and the
   // fprop A scales come from the register-staged bytes.
   auto settle = [&](uint8_t* base) {
-    if constexpr (!PC) {
-      constexpr int SA_INS = 4 * BM / 256, SB_INS = 4 * BN / 256, PER = (SA_INS + SB_INS) / NW;
+    if constexpr (F4) {
+      // MXFP4: the MFMA takes the E8M0 bytes as they are; only the fprop A scales, staged in
+      // registers, are written to their [blk][row] place
+      if constexpr (MODE == kModeFprop) {
+        uint8_t* f = base + S::SA_OFF + (wave / (NW / SBLK)) * BM + FA_ROWS * ((wave % (NW / SBLK)) * 64 + lane);
+#pragma unroll
+        for (int i = 0; i < FA_ROWS; ++i) f[i] = fa_b[i];
+      }
+    } else if constexpr (!PC) {
+      constexpr int SA_INS = SBLK * BM / 256, SB_INS = SBLK * BN / 256, PER = (SA_INS + SB_INS) / NW;
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
         const int v = wave * PER + u;
@@ -415,26 +436,104 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
     }
   };
 
+  // MXFP4 K step: the same chunks as above go to the scaled MFMA without widening.  MFMA u of the
+  // step (K elements [64u, 64u + 64), chunks 2u and 2u + 1) takes chunk 2u + h of each lane's row,
+  // one whole E8M0 block, with that block's scale byte; for the half s = u / 2 these are the
+  // chunks 4s + h and 4s + 2 + h read above.
+  // Per-fragment LDS bases of the MXFP4 step.  Chunk c = 4s + 2u + h of a row sits at
+  // row * BK + ((c ^ swz(row)) << 4) = base ^ ((4s + 2u) << 4) with base = row * BK + ((h ^ swz(row))
+  // << 4) (4s + 2u is even and row * BK has no bits below 128); its E8M0 byte at
+  // SA_OFF + (h * BM + row) + (4s + 2u) * BM.  Six bases per operand stay live, not 24 addresses.
+  uint32_t a4b[FM], a4s[FM], b4b[FN], b4s[FN];
+  if constexpr (F4) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm * WM + i * 32 + l32;
+      a4b[i] = (uint32_t)(S::A_OFF + row * BK + ((h ^ swz(row)) << 4));
+      a4s[i] = (uint32_t)(S::SA_OFF + h * BM + row);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn * WN + j * 32 + l32;
+      b4b[j] = (uint32_t)(S::B_OFF + row * BK + ((h ^ swz(row)) << 4));
+      b4s[j] = (uint32_t)(S::SB_OFF + h * BN + row);
+    }
+  }
+  auto step4 = [&](auto tail_tag, int kk, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const int64_t k0 = (int64_t)kk * BK;
+    auto chunk = [&](uint32_t off, int c) {
+      const v4i v = *(const v4i*)(cur + off);
+      if constexpr (TAIL) return k0 + 16 * c < kext ? v : v4i{0, 0, 0, 0};
+      else return v;
+    };
+    auto op = [](v4i v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1); };
+    // opaque per step: the chunk addresses are formed where they are used (one XOR each)
+    // instead of being hoisted out of the K loop into 24 live registers
+#pragma unroll
+    for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(a4b[i]), "+v"(a4s[i]));
+#pragma unroll
+    for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(b4b[j]), "+v"(b4s[j]));
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int ce = 4 * s + 2 * u;  // the chunk index without h
+        v8i af[FM], bf[FN];
+        int as[FM], bs[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          af[i] = op(chunk(a4b[i] ^ (uint32_t)(ce << 4), ce + h));
+          as[i] = cur[a4s[i] + ce * BM];
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          bf[j] = op(chunk(b4b[j] ^ (uint32_t)(ce << 4), ce + h));
+          bs[j] = cur[b4s[j] + ce * BN];
+        }
+        if (s == 0 && u == 1 && kk + 1 < nk) issue(kk + 1, nxt);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0, as[i], 0,
+                                                                         bs[j]);
+      }
+      // the second half's reads stay below the first half's MFMAs: both halves' fragments
+      // would not fit beside the accumulators
+      if (s == 0) __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto run_step = [&](auto tail_tag, int kk, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+    if constexpr (F4) step4(tail_tag, kk, cur, nxt);
+    else step(tail_tag, kk, cur, nxt);
+  };
+
   issue(0, smem);
   wait_dma();
   settle(smem);
   __syncthreads();
-  // fprop K not a multiple of 128: the last step is the tail step
-  static_assert(!KTAIL || MODE == kModeFprop, "only fprop has a K tail");
-  const int nfull = KTAIL ? nk - 1 : nk;
+  // the last step runs past kext (MXFP8 fprop with K not a multiple of 128; MXFP4 when the
+  // group's K bytes are not a multiple of 128): it is the tail step
+  static_assert(!KTAIL || MODE == kModeFprop, "only fprop has a static K tail");
+  bool tail = KTAIL;
+  if constexpr (F4) tail = kext % BK != 0;
+  const int nfull = tail ? nk - 1 : nk;
   for (int kk = 0; kk < nfull; ++kk) {
     uint8_t* cur = smem + (kk & 1) * S::STAGE;
     uint8_t* nxt = smem + ((kk & 1) ^ 1) * S::STAGE;
-    step(BoolC<false>(), kk, cur, nxt);
+    run_step(BoolC<false>(), kk, cur, nxt);
     if (kk + 1 < nk) {
       wait_dma();
       settle(nxt);
     }
     __syncthreads();
   }
-  if constexpr (KTAIL) {  // the tail step (its loads were issued by the step before)
-    step(BoolC<true>(), nfull, smem + (nfull & 1) * S::STAGE, smem + ((nfull & 1) ^ 1) * S::STAGE);
-    __syncthreads();
+  if constexpr (KTAIL || F4) {
+    if (tail) {  // the tail step (its loads were issued by the step before)
+      run_step(BoolC<true>(), nfull, smem + (nfull & 1) * S::STAGE, smem + ((nfull & 1) ^ 1) * S::STAGE);
+      __syncthreads();
+    }
   }
 
   // ---------------- epilogue ----------------
@@ -510,10 +609,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
 // Launchers
 // ------------------------------------------------------------------------------------------
 
-template <int MODE, bool PC, int BM, int BN, int WM, int WN, bool ACCUM, int OUT, bool KTAIL = false>
+template <int MODE, bool PC, bool F4, int BM, int BN, int WM, int WN, bool ACCUM, int OUT, bool KTAIL = false>
 static int launch(const GemmArgs& a, dim3 grid, hipStream_t stream) {
-  using S = GemmShape<MODE, PC, BM, BN, WM, WN>;
-  hipLaunchKernelGGL((grouped_gemm_kernel<MODE, PC, BM, BN, WM, WN, ACCUM, OUT, KTAIL>), grid, dim3(S::NT), 0, stream, a);
+  using S = GemmShape<MODE, PC, F4, BM, BN, WM, WN>;
+  hipLaunchKernelGGL((grouped_gemm_kernel<MODE, PC, F4, BM, BN, WM, WN, ACCUM, OUT, KTAIL>), grid, dim3(S::NT), 0,
+                     stream, a);
   return hipGetLastError() == hipSuccess ? BSFP8_OK : BSFP8_ERR_LAUNCH;
 }
 
@@ -532,15 +632,18 @@ int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, 
   a.E = E;
   a.out = out;
   a.status = status;
-  if (recipe == BSFP8_RECIPE_MX_1X32_E8M0) {
+  if (recipe == BSFP8_RECIPE_MX_1X32_E8M0 || recipe == BSFP8_RECIPE_MXFP4_1X32_E8M0) {
     constexpr int BM = 256, BN = 256;
     a.tiles_m = (int)((n + BM - 1) / BM);
     a.tiles_n = (int)((h + BN - 1) / BN);
     a.tiles = (int64_t)E * a.tiles_m * a.tiles_n;
     if (xcd_launch_size(a.tiles) > 0x7fffffff) return BSFP8_ERR_SHAPE;
     dim3 grid((unsigned)xcd_launch_size(a.tiles));
-    return accumulate ? launch<kModeWgrad, false, BM, BN, 128, 64, true, 0>(a, grid, stream)
-                      : launch<kModeWgrad, false, BM, BN, 128, 64, false, 0>(a, grid, stream);
+    if (recipe == BSFP8_RECIPE_MXFP4_1X32_E8M0)
+      return accumulate ? launch<kModeWgrad, false, true, BM, BN, 128, 64, true, 0>(a, grid, stream)
+                        : launch<kModeWgrad, false, true, BM, BN, 128, 64, false, 0>(a, grid, stream);
+    return accumulate ? launch<kModeWgrad, false, false, BM, BN, 128, 64, true, 0>(a, grid, stream)
+                      : launch<kModeWgrad, false, false, BM, BN, 128, 64, false, 0>(a, grid, stream);
   }
   constexpr int BM = 128, BN = 128;
   a.tiles_m = (int)((n + BM - 1) / BM);
@@ -548,13 +651,14 @@ int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, 
   a.tiles = (int64_t)E * a.tiles_m * a.tiles_n;
   if (xcd_launch_size(a.tiles) > 0x7fffffff) return BSFP8_ERR_SHAPE;
   dim3 grid((unsigned)xcd_launch_size(a.tiles));
-  return accumulate ? launch<kModeWgrad, true, BM, BN, 64, 64, true, 0>(a, grid, stream)
-                    : launch<kModeWgrad, true, BM, BN, 64, 64, false, 0>(a, grid, stream);
+  return accumulate ? launch<kModeWgrad, true, false, BM, BN, 64, 64, true, 0>(a, grid, stream)
+                    : launch<kModeWgrad, true, false, BM, BN, 64, 64, false, 0>(a, grid, stream);
 }
 
 // m-grouped GEMM: out[off_e + t][j] = sum_c A[off_e + t][c] B_e[j][c] over the rowwise A
-// [R][K] and a per-group B described by its row length and strides (see GemmArgs).
-static int launch_mgrouped(const uint8_t* a_q, const uint8_t* a_s, int64_t R, int64_t K, const uint8_t* b_q,
+// [R][K] and a per-group B described by its row length and strides (see GemmArgs).  K, b_ld and
+// b_estride are in bytes (K elements / 2 for MXFP4); the scale strides count E8M0 bytes.
+static int launch_mgrouped(bool f4, const uint8_t* a_q, const uint8_t* a_s, int64_t R, int64_t K, const uint8_t* b_q,
                            const uint8_t* b_s, int64_t N, int64_t b_ld, int64_t b_estride, int64_t bs_estride,
                            int64_t bs_bstride, const int32_t* splits, int E, void* out, int out_dtype,
                            uint32_t* status, hipStream_t stream) {
@@ -583,32 +687,39 @@ static int launch_mgrouped(const uint8_t* a_q, const uint8_t* a_s, int64_t R, in
   a.tiles = (mt + gm - 1) / gm * gm * a.tiles_n;
   if (xcd_launch_size(a.tiles) > 0x7fffffff) return BSFP8_ERR_SHAPE;
   dim3 grid((unsigned)xcd_launch_size(a.tiles));
+  if (f4)
+    return out_dtype == BSFP8_OUT_F32
+               ? launch<kModeFprop, false, true, BM, BN, 128, 64, false, BSFP8_OUT_F32>(a, grid, stream)
+               : launch<kModeFprop, false, true, BM, BN, 128, 64, false, BSFP8_OUT_BF16>(a, grid, stream);
   if (K % 128 != 0)
     return out_dtype == BSFP8_OUT_F32
-               ? launch<kModeFprop, false, BM, BN, 128, 64, false, BSFP8_OUT_F32, true>(a, grid, stream)
-               : launch<kModeFprop, false, BM, BN, 128, 64, false, BSFP8_OUT_BF16, true>(a, grid, stream);
+               ? launch<kModeFprop, false, false, BM, BN, 128, 64, false, BSFP8_OUT_F32, true>(a, grid, stream)
+               : launch<kModeFprop, false, false, BM, BN, 128, 64, false, BSFP8_OUT_BF16, true>(a, grid, stream);
   return out_dtype == BSFP8_OUT_F32
-             ? launch<kModeFprop, false, BM, BN, 128, 64, false, BSFP8_OUT_F32>(a, grid, stream)
-             : launch<kModeFprop, false, BM, BN, 128, 64, false, BSFP8_OUT_BF16>(a, grid, stream);
+             ? launch<kModeFprop, false, false, BM, BN, 128, 64, false, BSFP8_OUT_F32>(a, grid, stream)
+             : launch<kModeFprop, false, false, BM, BN, 128, 64, false, BSFP8_OUT_BF16>(a, grid, stream);
 }
 
 int launch_grouped_gemm_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R, int64_t K, const uint8_t* w_q,
-                              const uint8_t* w_s, int64_t N, const int32_t* splits, int E, void* out, int out_dtype,
-                              uint32_t* status, hipStream_t stream) {
+                              const uint8_t* w_s, int64_t N, const int32_t* splits, int E, int recipe, void* out,
+                              int out_dtype, uint32_t* status, hipStream_t stream) {
   // W rowwise [E*N][K], scales [K/32][E*N]
-  return launch_mgrouped(x_q, x_s, R, K, w_q, w_s, N, K, N * K, N, (int64_t)E * N, splits, E, out, out_dtype, status,
-                         stream);
+  const bool f4 = recipe == BSFP8_RECIPE_MXFP4_1X32_E8M0;
+  const int64_t kb = f4 ? K / 2 : K;  // bytes of a row
+  return launch_mgrouped(f4, x_q, x_s, R, kb, w_q, w_s, N, kb, N * kb, N, (int64_t)E * N, splits, E, out, out_dtype,
+                         status, stream);
 }
 
 int launch_grouped_gemm_dgrad(const uint8_t* dy_q, const uint8_t* dy_s, int64_t R, int64_t n, const uint8_t* w_q,
-                              const void* w_s, int64_t k, const int32_t* splits, int E, void* out, int out_dtype,
-                              uint32_t* status, hipStream_t stream) {
-  // W colwise: group e's rows are its k output channels, each np = 128 * ceil(n / 128) bytes
-  // (n along the contraction, pad lanes 0), data at k * np * e; E8M0 (e, b, c) at
+                              const void* w_s, int64_t k, const int32_t* splits, int E, int recipe, void* out,
+                              int out_dtype, uint32_t* status, hipStream_t stream) {
+  // W colwise: group e's rows are its k output channels, each np = 128 * ceil(n / 128) elements
+  // (n along the contraction, pad lanes 0), data at element k * np * e; E8M0 (e, b, c) at
   // k * np * e / 32 + b * k + c
-  const int64_t np = (n + 127) / 128 * 128;
-  return launch_mgrouped(dy_q, dy_s, R, n, w_q, (const uint8_t*)w_s, k, np, k * np, k * np / 32, k, splits, E, out,
-                         out_dtype, status, stream);
+  const bool f4 = recipe == BSFP8_RECIPE_MXFP4_1X32_E8M0;
+  const int64_t np = (n + 127) / 128 * 128, epb = f4 ? 2 : 1;
+  return launch_mgrouped(f4, dy_q, dy_s, R, n / epb, w_q, (const uint8_t*)w_s, k, np / epb, k * np / epb, k * np / 32,
+                         k, splits, E, out, out_dtype, status, stream);
 }
 
 }  // namespace bsfp8

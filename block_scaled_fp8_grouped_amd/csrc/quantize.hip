@@ -1,6 +1,9 @@
 // Grouped quantize: bf16 -> e4m3 with MXFP8 1x32 E8M0 scales or per-channel 128-row fp32
 // scales (DeepGEMM #365 reproducer: per-channel cast and K-major pack; TE #3484: MXFP8 block
-// scaling over a padded token buffer; TE PR #3224: columnwise scales strided per group member).
+// scaling over a padded token buffer; TE PR #3224: columnwise scales strided per group member),
+// or bf16 -> e2m1 with MXFP4 1x32 E8M0 scales (TE #3484 additional context: the same gated
+// grouped paths take a 4-bit block-scaled quantizer), two codes per byte along the contiguous
+// axis.
 //
 // One workgroup (4 waves) walks 8 consecutive 128-row tiles of one 128-channel column: the
 // split sizes are scanned once for the first tile and later tiles step forward through the
@@ -124,9 +127,11 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
       }
       float s0, s1;
       uint32_t sbits = 0;
-      if constexpr (RECIPE == BSFP8_RECIPE_MX_1X32_E8M0) {
-        const int e0 = e8m0_exponent(__uint_as_float(m0 << 16));
-        const int e1 = e8m0_exponent(__uint_as_float(m1 << 16));
+      if constexpr (RECIPE != BSFP8_RECIPE_PER_CHANNEL_128_F32) {
+        constexpr bool F4 = RECIPE == BSFP8_RECIPE_MXFP4_1X32_E8M0;
+        const float a0 = __uint_as_float(m0 << 16), a1 = __uint_as_float(m1 << 16);
+        const int e0 = F4 ? e8m0_exponent_fp4(a0) : e8m0_exponent(a0);
+        const int e1 = F4 ? e8m0_exponent_fp4(a1) : e8m0_exponent(a1);
         s0 = exp2_neg(e0);
         s1 = exp2_neg(e1);
         sbits = (uint32_t)(e0 + 127) | ((uint32_t)(e1 + 127) << 8);
@@ -154,24 +159,43 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
           *(float2*)((float*)col_s + C * P / 128 + jblk * C + c0 + c) = sv;
         }
       }
-      v4i q0[2], q1[2];
+      if constexpr (RECIPE == BSFP8_RECIPE_MXFP4_1X32_E8M0) {
+        // 32 tokens of each channel -> 16 bytes, token 2j in the low nibble of byte j
+        v4i q0, q1;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t lo = e4m3x4(bf16_lo(w[4 * i]) * s0, bf16_lo(w[4 * i + 1]) * s0, bf16_lo(w[4 * i + 2]) * s0,
-                                   bf16_lo(w[4 * i + 3]) * s0);
-        const uint32_t hi = e4m3x4(bf16_hi(w[4 * i]) * s1, bf16_hi(w[4 * i + 1]) * s1, bf16_hi(w[4 * i + 2]) * s1,
-                                   bf16_hi(w[4 * i + 3]) * s1);
-        q0[i >> 2][i & 3] = (int)lo;
-        q1[i >> 2][i & 3] = (int)hi;
-      }
-      if (c0 + c < C) {
-        uint8_t* dst = col_q + C * P + (c0 + c) * kp + kQRows * jblk + 32 * wave;
-        *(v4i*)dst = q0[0];
-        *(v4i*)(dst + 16) = q0[1];
-        *(v4i*)(dst + kp) = q1[0];
-        *(v4i*)(dst + kp + 16) = q1[1];
-        if constexpr (RECIPE == BSFP8_RECIPE_MX_1X32_E8M0) {
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t* wi = w + 8 * i;
+          q0[i] = (int)e2m1x8(bf16_lo(wi[0]) * s0, bf16_lo(wi[1]) * s0, bf16_lo(wi[2]) * s0, bf16_lo(wi[3]) * s0,
+                              bf16_lo(wi[4]) * s0, bf16_lo(wi[5]) * s0, bf16_lo(wi[6]) * s0, bf16_lo(wi[7]) * s0);
+          q1[i] = (int)e2m1x8(bf16_hi(wi[0]) * s1, bf16_hi(wi[1]) * s1, bf16_hi(wi[2]) * s1, bf16_hi(wi[3]) * s1,
+                              bf16_hi(wi[4]) * s1, bf16_hi(wi[5]) * s1, bf16_hi(wi[6]) * s1, bf16_hi(wi[7]) * s1);
+        }
+        if (c0 + c < C) {
+          uint8_t* dst = col_q + (C * P + (c0 + c) * kp) / 2 + kQRows / 2 * jblk + 16 * wave;
+          *(v4i*)dst = q0;
+          *(v4i*)(dst + kp / 2) = q1;
           *(uint16_t*)((uint8_t*)col_s + C * P / 32 + (4 * jblk + wave) * C + c0 + c) = (uint16_t)sbits;
+        }
+      } else {
+        v4i q0[2], q1[2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t lo = e4m3x4(bf16_lo(w[4 * i]) * s0, bf16_lo(w[4 * i + 1]) * s0, bf16_lo(w[4 * i + 2]) * s0,
+                                     bf16_lo(w[4 * i + 3]) * s0);
+          const uint32_t hi = e4m3x4(bf16_hi(w[4 * i]) * s1, bf16_hi(w[4 * i + 1]) * s1, bf16_hi(w[4 * i + 2]) * s1,
+                                     bf16_hi(w[4 * i + 3]) * s1);
+          q0[i >> 2][i & 3] = (int)lo;
+          q1[i >> 2][i & 3] = (int)hi;
+        }
+        if (c0 + c < C) {
+          uint8_t* dst = col_q + C * P + (c0 + c) * kp + kQRows * jblk + 32 * wave;
+          *(v4i*)dst = q0[0];
+          *(v4i*)(dst + 16) = q0[1];
+          *(v4i*)(dst + kp) = q1[0];
+          *(v4i*)(dst + kp + 16) = q1[1];
+          if constexpr (RECIPE == BSFP8_RECIPE_MX_1X32_E8M0) {
+            *(uint16_t*)((uint8_t*)col_s + C * P / 32 + (4 * jblk + wave) * C + c0 + c) = (uint16_t)sbits;
+          }
         }
       }
     }
@@ -188,12 +212,21 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
         for (int i = 0; i < 4; ++i) m = max(m, max((uint32_t)v[i] & 0x7fffu, ((uint32_t)v[i] >> 16) & 0x7fffu));
         m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
         m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
-        const int e = e8m0_exponent(__uint_as_float(m << 16));
+        const float amax = __uint_as_float(m << 16);
+        const int e = RECIPE == BSFP8_RECIPE_MXFP4_1X32_E8M0 ? e8m0_exponent_fp4(amax) : e8m0_exponent(amax);
         const float s = exp2_neg(e);
-        v2i q;
-        q[0] = (int)e4m3x4(bf16_lo(v[0]) * s, bf16_hi(v[0]) * s, bf16_lo(v[1]) * s, bf16_hi(v[1]) * s);
-        q[1] = (int)e4m3x4(bf16_lo(v[2]) * s, bf16_hi(v[2]) * s, bf16_lo(v[3]) * s, bf16_hi(v[3]) * s);
-        if (r < nlive && ch * 8 < ncols) *(v2i*)(row_q + (row0 + r) * C + c0 + ch * 8) = q;
+        if (r < nlive && ch * 8 < ncols) {
+          if constexpr (RECIPE == BSFP8_RECIPE_MXFP4_1X32_E8M0) {  // 8 codes -> 4 bytes
+            *(uint32_t*)(row_q + ((row0 + r) * C + c0 + ch * 8) / 2) =
+                e2m1x8(bf16_lo(v[0]) * s, bf16_hi(v[0]) * s, bf16_lo(v[1]) * s, bf16_hi(v[1]) * s,
+                       bf16_lo(v[2]) * s, bf16_hi(v[2]) * s, bf16_lo(v[3]) * s, bf16_hi(v[3]) * s);
+          } else {
+            v2i q;
+            q[0] = (int)e4m3x4(bf16_lo(v[0]) * s, bf16_hi(v[0]) * s, bf16_lo(v[1]) * s, bf16_hi(v[1]) * s);
+            q[1] = (int)e4m3x4(bf16_lo(v[2]) * s, bf16_hi(v[2]) * s, bf16_lo(v[3]) * s, bf16_hi(v[3]) * s);
+            *(v2i*)(row_q + (row0 + r) * C + c0 + ch * 8) = q;
+          }
+        }
         if ((ch & 3) == 0) rs_tile[ch >> 2][r] = (uint8_t)(e + 127);
       }
       __syncthreads();
@@ -235,6 +268,16 @@ int launch_grouped_quantize(const void* in, int64_t R, int64_t C, const int32_t*
                          x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status);
     else
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MX_1X32_E8M0, false, true>), grid, block, 0, stream,
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status);
+  } else if (recipe == BSFP8_RECIPE_MXFP4_1X32_E8M0) {
+    if (row && col)
+      hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MXFP4_1X32_E8M0, true, true>), grid, block, 0, stream,
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status);
+    else if (row)
+      hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MXFP4_1X32_E8M0, true, false>), grid, block, 0, stream,
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status);
+    else
+      hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MXFP4_1X32_E8M0, false, true>), grid, block, 0, stream,
                          x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status);
   } else {
     hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_PER_CHANNEL_128_F32, false, true>), grid, block, 0,

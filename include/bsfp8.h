@@ -45,6 +45,7 @@ extern "C" {
 /* Quantization recipes. */
 #define BSFP8_RECIPE_MX_1X32_E8M0 1       /* e4m3 data, one E8M0 power-of-two scale per 32 values */
 #define BSFP8_RECIPE_PER_CHANNEL_128_F32 2 /* e4m3 data, one fp32 scale per channel per 128 rows */
+#define BSFP8_RECIPE_MXFP4_1X32_E8M0 3     /* e2m1 data (two per byte), one E8M0 scale per 32 values */
 
 /* Layout selection bits for bsfp8_grouped_quantize. */
 #define BSFP8_ROWWISE 1 /* blocks along a row (channels); used by the forward GEMM */
@@ -77,23 +78,25 @@ extern "C" {
 
 /* Upper bound of sum(Kp_e) over all valid split sizes: 128 * floor((R + 127 * E) / 128). */
 int64_t bsfp8_colwise_rows_bound(int64_t capacity_rows, int32_t num_groups);
-/* Bytes of a colwise e4m3 buffer: cols * bsfp8_colwise_rows_bound(R, E). */
-size_t bsfp8_colwise_data_bytes(int64_t capacity_rows, int64_t cols, int32_t num_groups);
-/* Bytes of a colwise scale buffer: rows_bound * cols / 32 (MX) or rows_bound * cols / 128 * 4. */
+/* Bytes of a colwise data buffer: cols * bsfp8_colwise_rows_bound(R, E) (half that for MXFP4). */
+size_t bsfp8_colwise_data_bytes(int64_t capacity_rows, int64_t cols, int32_t num_groups, int recipe);
+/* Bytes of a colwise scale buffer: rows_bound * cols / 32 (MX, MXFP4) or rows_bound * cols / 128 * 4. */
 size_t bsfp8_colwise_scale_bytes(int64_t capacity_rows, int64_t cols, int32_t num_groups, int recipe);
-/* Bytes of rowwise e4m3 data (rows * cols) and of its E8M0 scales (rows * cols / 32). */
-size_t bsfp8_rowwise_data_bytes(int64_t rows, int64_t cols);
+/* Bytes of rowwise data (rows * cols for MXFP8, rows * cols / 2 for MXFP4; 0 for the
+ * per-channel recipe, which has no rowwise layout) and of its E8M0 scales (rows * cols / 32). */
+size_t bsfp8_rowwise_data_bytes(int64_t rows, int64_t cols, int recipe);
 size_t bsfp8_rowwise_scale_bytes(int64_t rows, int64_t cols);
 
 /* ----------------------------------------------------------------------------------------- */
-/* Grouped quantize: bf16 -> e4m3 with block scales (DeepGEMM #365 reproducer, per-channel    */
-/* cast; TE #3484 MXFP8 block scaling; TE PR #3224, per-member columnwise scale strides).     */
+/* Grouped quantize: bf16 -> e4m3 / e2m1 with block scales (DeepGEMM #365 reproducer,         */
+/* per-channel cast; TE #3484 MXFP8 block scaling, and the 4-bit quantizer its additional     */
+/* context says the same gated paths accept; TE PR #3224, per-member columnwise scale strides). */
 /* ----------------------------------------------------------------------------------------- */
 /*
  * in_bf16         [capacity_rows][cols] bf16, row-major.
  * split_sizes     device int32[num_groups]; may be NULL only when which == BSFP8_ROWWISE,
  *                 meaning that all capacity_rows rows are live (e.g. a weight [E*N][K]).
- * which           BSFP8_ROWWISE, BSFP8_COLWISE or both (rowwise needs the MX recipe).
+ * which           BSFP8_ROWWISE, BSFP8_COLWISE or both (rowwise needs an MX recipe).
  * zero_amax_scale per-channel recipe only: the scale used when a block's amax is 0 (the
  *                 reproducer's sf_val, default 1e-30); must be finite and >= 0.
  *
@@ -104,8 +107,13 @@ size_t bsfp8_rowwise_scale_bytes(int64_t rows, int64_t cols);
  *   sf = fp32(amax / 448); sf == 0 becomes zero_amax_scale; sf = max(sf, 1e-30);
  *   each value v becomes e4m3(fp32(v * fp32(1 / sf))); the fp32 sf is stored.
  * e4m3 is OCP E4M3FN, round to nearest even, sign kept (both recipes keep |v| <= 448).
+ * MXFP4 1x32 E8M0 (both layouts): as MXFP8 with 6 in place of 448 (e is the smallest integer in
+ *   [-127, 127] with amax <= 6 * 2^e) and each value becoming e2m1(v * 2^-e): OCP FP4 E2M1
+ *   (0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives), round to nearest even, sign kept.  The codes of
+ *   elements 2i and 2i + 1 along the contiguous axis share a byte, 2i in bits 3..0.
  *
- * Outputs (all caller-allocated; only the requested ones may be non-NULL):
+ * Outputs (all caller-allocated; only the requested ones may be non-NULL).  The offsets below
+ * count data elements; for MXFP4 element i is a nibble of byte i / 2 (see above).
  *   row_q  [capacity_rows][cols] e4m3: row r, column c at r*cols + c      (live rows only)
  *   row_s  [cols/32][capacity_rows] E8M0: row r, block b at b*capacity_rows + r (live rows only)
  *   col_q  bsfp8_colwise_data_bytes(): group e, row t < Kp_e, column c at
@@ -134,6 +142,7 @@ int bsfp8_grouped_quantize(const void* in_bf16, int64_t capacity_rows, int64_t c
 /* ----------------------------------------------------------------------------------------- */
 /* k-grouped weight-gradient GEMM (DeepGEMM #365, k_grouped_fp8_gemm_nt_contiguous; TE #3484, */
 /* accumulate into an fp32 main_grad; the contraction runs over each group's tokens only).    */
+/* All three recipes.                                                                         */
 /* ----------------------------------------------------------------------------------------- */
 /*
  * dy_col_q, dy_col_s  colwise output of bsfp8_grouped_quantize for dy [capacity_rows][n]
@@ -147,6 +156,8 @@ int bsfp8_grouped_quantize(const void* in_bf16, int64_t capacity_rows, int64_t c
  *   accumulate in fp32.
  * Per-channel recipe: each 128-row block's unit-scale partial sum p is folded in as
  *   acc = fma(p, sdy_i * sx_j, acc) in block order.
+ * MXFP4 recipe: the scaled fp4 MFMA takes the codes and E8M0 scales as they are (its sums of
+ *   e2m1 products within a block are exact); products accumulate in fp32.
  * n and h must be multiples of 32, h at most 2^21; capacity_rows + 127 must stay below
  * 2^24 - 128 (BSFP8_ERR_SHAPE otherwise): the kernels address an operand tile and a 128-row
  * output block with 32-bit offsets.
@@ -158,10 +169,11 @@ int bsfp8_grouped_gemm_wgrad(const uint8_t* dy_col_q, const void* dy_col_s, int6
 
 /* ----------------------------------------------------------------------------------------- */
 /* m-grouped forward GEMM (TE PR #3224, grouped GEMM over a single grouped weight; the token   */
-/* axis is a free dimension).  MX recipe only.                                                */
+/* axis is a free dimension).  recipe: BSFP8_RECIPE_MX_1X32_E8M0 or BSFP8_RECIPE_MXFP4_1X32_E8M0. */
 /* ----------------------------------------------------------------------------------------- */
 /*
  * x_row_q, x_row_s  rowwise output of bsfp8_grouped_quantize for x [capacity_rows][k]
+ *                   (the same recipe as the weight's)
  * w_q, w_s          rowwise output for the weight [num_groups * n][k] (split_sizes NULL):
  *                   expert e's row j is buffer row e*n + j; scales [k/32][num_groups * n]
  * out               [capacity_rows][n], fp32 or bf16 (round to nearest even from fp32):
@@ -173,13 +185,13 @@ int bsfp8_grouped_gemm_wgrad(const uint8_t* dy_col_q, const void* dy_col_s, int6
  */
 int bsfp8_grouped_gemm_fprop(const uint8_t* x_row_q, const uint8_t* x_row_s, int64_t capacity_rows,
                              int64_t k, const uint8_t* w_q, const uint8_t* w_s, int64_t n,
-                             const int32_t* split_sizes, int32_t num_groups, void* out,
+                             const int32_t* split_sizes, int32_t num_groups, int recipe, void* out,
                              int out_dtype, uint32_t* status, void* stream);
 
 /* ----------------------------------------------------------------------------------------- */
 /* m-grouped data-gradient GEMM (the remaining GEMM of the expert backward beside wgrad and    */
 /* fprop: TE #3484 scope -- the token axis is a free dimension of everything but wgrad).      */
-/* MX recipe only.                                                                           */
+/* recipe: BSFP8_RECIPE_MX_1X32_E8M0 or BSFP8_RECIPE_MXFP4_1X32_E8M0.                        */
 /* ----------------------------------------------------------------------------------------- */
 /*
  * dy_row_q, dy_row_s  rowwise output of bsfp8_grouped_quantize for dy [capacity_rows][n]
@@ -187,7 +199,7 @@ int bsfp8_grouped_gemm_fprop(const uint8_t* x_row_q, const uint8_t* x_row_s, int
  *                     [num_groups * n][k] with split sizes n, ..., n (num_groups of them): the
  *                     32-blocks run along n inside each expert, so expert e's matrix is
  *                     transposed in the buffer -- output channel j, contraction index c at
- *                     k*np*e + j*np + c with np = 128 * ceil(n / 128); E8M0 (e, b, j) at
+ *                     element k*np*e + j*np + c with np = 128 * ceil(n / 128); E8M0 (e, b, j) at
  *                     k*np*e/32 + b*k + j (bsfp8_colwise_data_bytes / _scale_bytes with
  *                     capacity_rows = num_groups * n give the sizes)
  * out                 [capacity_rows][k], fp32 or bf16 (round to nearest even from fp32):
@@ -198,7 +210,7 @@ int bsfp8_grouped_gemm_fprop(const uint8_t* x_row_q, const uint8_t* x_row_s, int
  */
 int bsfp8_grouped_gemm_dgrad(const uint8_t* dy_row_q, const uint8_t* dy_row_s, int64_t capacity_rows,
                              int64_t n, const uint8_t* w_col_q, const void* w_col_s, int64_t k,
-                             const int32_t* split_sizes, int32_t num_groups, void* out,
+                             const int32_t* split_sizes, int32_t num_groups, int recipe, void* out,
                              int out_dtype, uint32_t* status, void* stream);
 
 /* Static description of a return code. */

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HDR = os.path.join(ROOT, "include", "bsfp8.h")
 
 P = 1 << 20  # a fake, 16-byte-aligned device address; never dereferenced by these calls
-MX, PC = bs.RECIPE_MX, bs.RECIPE_PC
+MX, PC, MX4 = bs.RECIPE_MX, bs.RECIPE_PC, bs.RECIPE_MX4
 
 
 def _declared():
@@ -39,6 +39,7 @@ def test_every_declared_symbol_is_exported():
 def test_binding_constants_match_header():
     c = _hdr_consts()
     assert c["BSFP8_RECIPE_MX_1X32_E8M0"] == bs.RECIPE_MX and c["BSFP8_RECIPE_PER_CHANNEL_128_F32"] == bs.RECIPE_PC
+    assert c["BSFP8_RECIPE_MXFP4_1X32_E8M0"] == bs.RECIPE_MX4
     assert c["BSFP8_ROWWISE"] == bs.ROWWISE and c["BSFP8_COLWISE"] == bs.COLWISE
     assert c["BSFP8_OUT_F32"] == bs.OUT_F32 and c["BSFP8_OUT_BF16"] == bs.OUT_BF16
     assert c["BSFP8_MAX_GROUPS"] == bs.MAX_GROUPS
@@ -49,15 +50,19 @@ def test_size_queries():
         rb = 128 * ((R + 127 * E) // 128)
         assert bs.colwise_rows_bound(R, E) == rb
         assert bs.colwise_data_bytes(R, 256, E) == rb * 256
+        assert bs.colwise_data_bytes(R, 256, E, PC) == rb * 256
+        assert bs.colwise_data_bytes(R, 256, E, MX4) == rb * 128
         assert bs.colwise_scale_bytes(R, 256, E, MX) == rb // 32 * 256
+        assert bs.colwise_scale_bytes(R, 256, E, MX4) == rb // 32 * 256
         assert bs.colwise_scale_bytes(R, 256, E, PC) == rb // 128 * 256 * 4
     # the bound covers the worst case of any valid split
     for R, E in [(1000, 7), (129, 2), (1, 1)]:
         worst = sum(128 * ((k + 127) // 128) for k in [R - (E - 1)] + [1] * (E - 1))
         assert worst <= bs.colwise_rows_bound(R, E)
     assert bs.rowwise_data_bytes(10, 64) == 640 and bs.rowwise_scale_bytes(10, 64) == 20
+    assert bs.rowwise_data_bytes(10, 64, MX4) == 320 and bs.rowwise_data_bytes(10, 64, PC) == 0
     assert bs.colwise_data_bytes(10, 33, 1) == 0 and bs.colwise_rows_bound(10, 0) == 0
-    assert bs.colwise_scale_bytes(10, 64, 1, 7) == 0
+    assert bs.colwise_scale_bytes(10, 64, 1, 7) == 0 and bs.colwise_data_bytes(10, 64, 1, 7) == 0
 
 
 def _q(**kw):
@@ -77,16 +82,18 @@ def _w(**kw):
 
 
 def _f(**kw):
-    a = dict(xq=P, xs=P, R=1024, k=256, wq=P, ws=P, n=256, splits=P, E=4, out=P, dtype=bs.OUT_F32, status=P)
+    a = dict(xq=P, xs=P, R=1024, k=256, wq=P, ws=P, n=256, splits=P, E=4, recipe=MX, out=P, dtype=bs.OUT_F32,
+             status=P)
     a.update(kw)
     return bs.lib().bsfp8_grouped_gemm_fprop(a["xq"], a["xs"], a["R"], a["k"], a["wq"], a["ws"], a["n"],
-                                             a["splits"], a["E"], a["out"], a["dtype"], a["status"], None)
+                                             a["splits"], a["E"], a["recipe"], a["out"], a["dtype"], a["status"],
+                                             None)
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(recipe=0), -3), (dict(recipe=3), -3),
+    (dict(recipe=0), -3), (dict(recipe=4), -3),
     (dict(which=0), -7), (dict(which=4), -7),
-    (dict(which=bs.ROWWISE, recipe=PC), -6),
+    (dict(which=bs.ROWWISE, recipe=PC), -6), (dict(which=bs.ROWWISE | bs.COLWISE, recipe=PC), -6),
     (dict(C=33), -4), (dict(C=0), -4), (dict(R=-1), -4),
     (dict(recipe=PC, zas=float("nan")), -7), (dict(recipe=PC, zas=-1.0), -7), (dict(recipe=PC, zas=float("inf")), -7),
     (dict(splits=None), -1),
@@ -119,7 +126,7 @@ def test_wgrad_rejects_before_launch(kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(E=0), -2), (dict(k=48), -4), (dict(n=-32), -4), (dict(dtype=2), -7), (dict(k=1 << 24), -4),
-    (dict(n=(1 << 21) + 32), -4),
+    (dict(n=(1 << 21) + 32), -4), (dict(recipe=PC), -3), (dict(recipe=0), -3), (dict(recipe=4), -3),
     (dict(xq=None), -1), (dict(ws=None), -1), (dict(splits=None), -1), (dict(out=None), -1),
     (dict(out=P + 2), -5), (dict(wq=P + 8), -5),
 ])
@@ -128,15 +135,17 @@ def test_fprop_rejects_before_launch(kw, code):
 
 
 def _d(**kw):
-    a = dict(yq=P, ys=P, R=1024, n=256, wq=P, ws=P, k=256, splits=P, E=4, out=P, dtype=bs.OUT_F32, status=P)
+    a = dict(yq=P, ys=P, R=1024, n=256, wq=P, ws=P, k=256, splits=P, E=4, recipe=MX, out=P, dtype=bs.OUT_F32,
+             status=P)
     a.update(kw)
     return bs.lib().bsfp8_grouped_gemm_dgrad(a["yq"], a["ys"], a["R"], a["n"], a["wq"], a["ws"], a["k"],
-                                             a["splits"], a["E"], a["out"], a["dtype"], a["status"], None)
+                                             a["splits"], a["E"], a["recipe"], a["out"], a["dtype"], a["status"],
+                                             None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(E=0), -2), (dict(E=2000), -2), (dict(n=48), -4), (dict(k=-32), -4), (dict(k=(1 << 21) + 32), -4),
-    (dict(n=(1 << 24) - 224), -4), (dict(dtype=2), -7), (dict(R=-1), -4),
+    (dict(n=(1 << 24) - 224), -4), (dict(dtype=2), -7), (dict(R=-1), -4), (dict(recipe=PC), -3),
     (dict(yq=None), -1), (dict(ws=None), -1), (dict(splits=None), -1), (dict(out=None), -1),
     (dict(out=P + 2), -5), (dict(wq=P + 8), -5), (dict(ys=P + 1), -5),
 ])
