@@ -208,6 +208,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
     b_valid = args.N;
   }
   const int nk = (int)((kext + BK - 1) / BK);
+  const int64_t nblk = (kext + BLK_BYTES - 1) / BLK_BYTES;  // scale blocks along K
 
   // ---------------- loads of one K step, straight into LDS ----------------
   // One DMA instruction moves 64 lanes x 16 bytes = 8 rows x 128 bytes; lane l fills LDS slot
@@ -243,7 +244,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
       static_assert((FA_ROWS == 2 || FA_ROWS == 4) && NW % SBLK == 0, "fprop A-scale staging shape");
       const int blk = wave / (NW / SBLK), r0 = FA_ROWS * ((wave % (NW / SBLK)) * 64 + lane);
       const int64_t kb = (int64_t)kk * SBLK + blk;
-      if (kb * BLK_BYTES < kext) {
+      if constexpr (F4) {
+        // no branch: a block past kext loads the last valid one; settle() puts unit scales there
+        const int64_t kbc = kb < nblk ? kb : nblk - 1;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a_sc + kbc * a_sld + a_row0), (short)0, a_last + 1, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < FA_ROWS; ++i) fa_b[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, r0 + i, 0, 0);
+      } else if (kb * BLK_BYTES < kext) {
         // the group's scale bytes of this block through a buffer resource spanning its valid
         // rows: rows past them read as 0 (their products are never stored)
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -294,7 +302,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
         uint8_t* dst = base + (is_a ? S::SA_OFF + blk * BM : S::SB_OFF + blk * BN) + part * 256;
         if (MODE == kModeFprop && is_a) {
           // rows of a group start anywhere: single-byte loads per thread instead (above)
-        } else if ((MODE == kModeFprop || F4) && kb * BLK_BYTES >= kext) {
+        } else if (F4) {
+          // no branch: a block past kext loads the last valid one; settle() puts unit scales there
+          const int64_t kbc = kb < nblk ? kb : nblk - 1;
+          const int r4 = scale_dma_row(part, lane, is_a ? a_last : b_last);
+          dma4((is_a ? a_sc + a_row0 : b_sc + b_row0) + kbc * (is_a ? a_sld : b_sld) + r4, dst);
+        } else if (MODE == kModeFprop && kb * BLK_BYTES >= kext) {
           *(uint32_t*)(dst + 4 * lane) = 0x7f7f7f7fu;  // past K: unit scales over zero data
         } else {
           // valid rows are a multiple of 32 here, so a group of 4 is all valid or all past
@@ -308,14 +321,45 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   // the fragment reads take fp32 scales with no per-read decode.  Each wave decodes the 256
   // bytes its own scale DMA (or tail store) wrote -- visible to it after its own wait -- and the
   // fprop A scales come from the register-staged bytes.
-  auto settle = [&](uint8_t* base) {
+  auto settle = [&](uint8_t* base, int kk) {
     if constexpr (F4) {
-      // MXFP4: the MFMA takes the E8M0 bytes as they are; only the fprop A scales, staged in
-      // registers, are written to their [blk][row] place
+      // MXFP4: the MFMA takes the E8M0 bytes as they are.  The fprop A scales, staged in
+      // registers, are written to their [blk][row] place, and blocks past kext (a tail step)
+      // get unit scales over their zero data, in the 256-byte pieces this wave's DMA filled.
+      constexpr int SA_INS = SBLK * BM / 256, SB_INS = SBLK * BN / 256, PER = (SA_INS + SB_INS) / NW;
       if constexpr (MODE == kModeFprop) {
-        uint8_t* f = base + S::SA_OFF + (wave / (NW / SBLK)) * BM + FA_ROWS * ((wave % (NW / SBLK)) * 64 + lane);
+        const int blk = wave / (NW / SBLK);
+        const bool valid = ((int64_t)kk * SBLK + blk) * BLK_BYTES < kext;
+        uint8_t* f = base + S::SA_OFF + blk * BM + FA_ROWS * ((wave % (NW / SBLK)) * 64 + lane);
 #pragma unroll
-        for (int i = 0; i < FA_ROWS; ++i) f[i] = fa_b[i];
+        for (int i = 0; i < FA_ROWS; ++i) f[i] = valid ? fa_b[i] : (uint8_t)0x7f;
+      }
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int v = wave * PER + u;
+        const bool is_a = v < SA_INS;
+        if (MODE == kModeFprop && is_a) continue;
+        const int vv = is_a ? v : v - SA_INS;
+        const int per = (is_a ? BM : BN) / 256;
+        const int blk = vv / per, part = vv % per;
+        if (((int64_t)kk * SBLK + blk) * BLK_BYTES >= kext)
+          *(uint32_t*)(base + (is_a ? S::SA_OFF + blk * BM : S::SB_OFF + blk * BN) + part * 256 + 4 * lane) =
+              0x7f7f7f7fu;
+      }
+      // a tail step: the 16-byte chunks this wave's data DMA put past kext (bytes of the next
+      // row, or zeros past the operand) become zeros, so the step needs no masking
+      const int64_t k0 = (int64_t)kk * BK;
+      if (k0 + BK > kext) {
+#pragma unroll
+        for (int u = 0; u < S::A_INS; ++u) {
+          const int g = wave * S::A_INS + u;
+          if (k0 + dma_chunk(g, lane) >= kext) *(v4i*)(base + S::A_OFF + g * 1024 + 16 * lane) = v4i{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < S::B_INS; ++u) {
+          const int g = wave * S::B_INS + u;
+          if (k0 + dma_chunk(g, lane) >= kext) *(v4i*)(base + S::B_OFF + g * 1024 + 16 * lane) = v4i{0, 0, 0, 0};
+        }
       }
     } else if constexpr (!PC) {
       constexpr int SA_INS = SBLK * BM / 256, SB_INS = SBLK * BN / 256, PER = (SA_INS + SB_INS) / NW;
@@ -459,14 +503,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
       b4s[j] = (uint32_t)(S::SB_OFF + h * BN + row);
     }
   }
-  auto step4 = [&](auto tail_tag, int kk, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
-    constexpr bool TAIL = decltype(tail_tag)::value;
-    const int64_t k0 = (int64_t)kk * BK;
-    auto chunk = [&](uint32_t off, int c) {
-      const v4i v = *(const v4i*)(cur + off);
-      if constexpr (TAIL) return k0 + 16 * c < kext ? v : v4i{0, 0, 0, 0};
-      else return v;
-    };
+  // The step is one basic block with no branch: it always issues the next step's loads (after
+  // the last step they fetch clamped, in-range addresses into the idle stage and are waited for
+  // before the epilogue), and a tail step needs no masking because settle() zeroed its chunks
+  // past kext.  So the scheduler can interleave each chunk group's reads with the MFMAs of the
+  // group before.
+  auto step4 = [&](int kk, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+    auto chunk = [&](uint32_t off, int) { return *(const v4i*)(cur + off); };
     auto op = [](v4i v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1); };
     // opaque per step: the chunk addresses are formed where they are used (one XOR each)
     // instead of being hoisted out of the K loop into 24 live registers
@@ -474,64 +517,83 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
     for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(a4b[i]), "+v"(a4s[i]));
 #pragma unroll
     for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(b4b[j]), "+v"(b4s[j]));
+    // chunk group g = 2s + u (chunk 4s + 2u + h of each row): its fragments and scale bytes
+    v4i af[2][FM], bf[2][FN];
+    int as[2][FM], bs[2][FN];
+    auto rd = [&](int g, int buf) {
+      const int ce = 2 * g;  // the chunk index without h
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int ce = 4 * s + 2 * u;  // the chunk index without h
-        v8i af[FM], bf[FN];
-        int as[FM], bs[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          af[i] = op(chunk(a4b[i] ^ (uint32_t)(ce << 4), ce + h));
-          as[i] = cur[a4s[i] + ce * BM];
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          bf[j] = op(chunk(b4b[j] ^ (uint32_t)(ce << 4), ce + h));
-          bs[j] = cur[b4s[j] + ce * BN];
-        }
-        if (s == 0 && u == 1 && kk + 1 < nk) issue(kk + 1, nxt);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0, as[i], 0,
-                                                                         bs[j]);
+      for (int i = 0; i < FM; ++i) {
+        af[buf][i] = chunk(a4b[i] ^ (uint32_t)(ce << 4), ce + h);
+        as[buf][i] = cur[a4s[i] + ce * BM];
       }
-      // the second half's reads stay below the first half's MFMAs: both halves' fragments
-      // would not fit beside the accumulators
-      if (s == 0) __builtin_amdgcn_sched_barrier(0);
-    }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        bf[buf][j] = chunk(b4b[j] ^ (uint32_t)(ce << 4), ce + h);
+        bs[buf][j] = cur[b4s[j] + ce * BN];
+      }
+    };
+    auto mm = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op(af[buf][i]), op(bf[buf][j]), acc[i][j], 4, 4,
+                                                                       0, as[buf][i], 0, bs[buf][j]);
+    };
+    // software pipeline over the 4 groups: group g + 1's reads go out beside group g's MFMAs;
+    // the scheduling fences keep each phase's reads from being hoisted further up (two groups'
+    // fragments fit beside the accumulators, four do not)
+    rd(0, 0);
+    issue(kk + 1, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    rd(1, 1);
+    mm(0);
+    __builtin_amdgcn_sched_barrier(0);
+    rd(2, 0);
+    mm(1);
+    __builtin_amdgcn_sched_barrier(0);
+    rd(3, 1);
+    mm(0);
+    __builtin_amdgcn_sched_barrier(0);
+    mm(1);
+    // the MFMAs stay in this step: sunk below the DMA wait and barrier that follow, they would
+    // keep all four groups' fragments live at once
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(acc[i][j]));
   };
-  auto run_step = [&](auto tail_tag, int kk, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
-    if constexpr (F4) step4(tail_tag, kk, cur, nxt);
-    else step(tail_tag, kk, cur, nxt);
-  };
-
   issue(0, smem);
   wait_dma();
-  settle(smem);
+  settle(smem, 0);
   __syncthreads();
   // the last step runs past kext (MXFP8 fprop with K not a multiple of 128; MXFP4 when the
   // group's K bytes are not a multiple of 128): it is the tail step
   static_assert(!KTAIL || MODE == kModeFprop, "only fprop has a static K tail");
-  bool tail = KTAIL;
-  if constexpr (F4) tail = kext % BK != 0;
-  const int nfull = tail ? nk - 1 : nk;
-  for (int kk = 0; kk < nfull; ++kk) {
-    uint8_t* cur = smem + (kk & 1) * S::STAGE;
-    uint8_t* nxt = smem + ((kk & 1) ^ 1) * S::STAGE;
-    run_step(BoolC<false>(), kk, cur, nxt);
-    if (kk + 1 < nk) {
-      wait_dma();
-      settle(nxt);
+  if constexpr (F4) {
+    for (int kk = 0; kk < nk; ++kk) {
+      uint8_t* cur = smem + (kk & 1) * S::STAGE;
+      uint8_t* nxt = smem + ((kk & 1) ^ 1) * S::STAGE;
+      step4(kk, cur, nxt);
+      wait_dma();  // after the last step: the surplus loads have landed before LDS is reused
+      if (kk + 1 < nk) settle(nxt, kk + 1);
+      __syncthreads();
     }
-    __syncthreads();
-  }
-  if constexpr (KTAIL || F4) {
-    if (tail) {  // the tail step (its loads were issued by the step before)
-      run_step(BoolC<true>(), nfull, smem + (nfull & 1) * S::STAGE, smem + ((nfull & 1) ^ 1) * S::STAGE);
+  } else {
+    const int nfull = KTAIL ? nk - 1 : nk;
+    for (int kk = 0; kk < nfull; ++kk) {
+      uint8_t* cur = smem + (kk & 1) * S::STAGE;
+      uint8_t* nxt = smem + ((kk & 1) ^ 1) * S::STAGE;
+      step(BoolC<false>(), kk, cur, nxt);
+      if (kk + 1 < nk) {
+        wait_dma();
+        settle(nxt, kk + 1);
+      }
+      __syncthreads();
+    }
+    if constexpr (KTAIL) {  // the tail step (its loads were issued by the step before)
+      step(BoolC<true>(), nfull, smem + (nfull & 1) * S::STAGE, smem + ((nfull & 1) ^ 1) * S::STAGE);
       __syncthreads();
     }
   }
