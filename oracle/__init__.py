@@ -67,6 +67,10 @@ def lib():
         L.oracle_grouped_quantize.restype = ctypes.c_int
         L.oracle_grouped_quantize.argtypes = [_vp, _i64, _i64, _vp, _i32, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_float, _vp, _vp, _vp, _vp]
+        L.oracle_act_values.argtypes = [ctypes.c_int, _vp, _vp, _vp, _i64, _vp]
+        L.oracle_grouped_act_quantize.restype = ctypes.c_int
+        L.oracle_grouped_act_quantize.argtypes = [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _vp, _i32, ctypes.c_int,
+                                                  ctypes.c_int, _vp, _vp, _vp, _vp]
         L.oracle_grouped_wgrad.restype = ctypes.c_int
         L.oracle_grouped_wgrad.argtypes = [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i64, ctypes.c_int,
                                            _vp, _i32, ctypes.c_int, _vp, _vp]
@@ -182,6 +186,49 @@ def grouped_quantize(x_bits, splits, recipe, which, zero_amax_scale=1e-30):
                                        _p(row_q), _p(row_s), _p(col_q), _p(col_s))
     if rc != 0:
         raise ValueError(f"oracle_grouped_quantize failed ({rc})")
+    return out
+
+
+ACT_SRELU_FWD = 1  # y = p * relu(h)^2
+ACT_SRELU_BWD = 2  # g = dy * p * 2 relu(h)
+
+
+def act_values(act, h_bits, p, dy_bits=None):
+    """The fp32 activation values (act 1: (r r) p; act 2: ((2 r) p) dy; r = max(h, 0)) of bf16
+    h (and dy) with float32 p, element by element (all arrays of one shape)."""
+    h = _c(h_bits, np.uint16)
+    pp = _c(p, np.float32)
+    d = None if dy_bits is None else _c(dy_bits, np.uint16)
+    out = np.empty(h.shape, np.float32)
+    lib().oracle_act_values(act, _p(h), _p(pp), _p(d), h.size, _p(out))
+    return out
+
+
+def grouped_act_quantize(act, h_bits, probs, dy_bits, splits, recipe, which):
+    """Scaled squared ReLU (act 1) or its gradient (act 2) in fp32 on the live rows of the bf16
+    [R, C] buffer(s), then the grouped quantize of those values (MX recipes).  probs: float32 [R]
+    or None (p = 1).  Returns the same dict as grouped_quantize."""
+    h = _c(h_bits, np.uint16)
+    R, C = h.shape
+    s = _c(splits, np.int32)
+    p = None if probs is None else _c(probs, np.float32)
+    d = None if dy_bits is None else _c(dy_bits, np.uint16)
+    per = 2 if recipe == RECIPE_MX4 else 1
+    out = {}
+    row_q = row_s = col_q = col_s = None
+    if which & ROWWISE:
+        row_q = np.zeros((R, C // per), np.uint8)
+        row_s = np.zeros((C // 32, R), np.uint8)
+        out["row_q"], out["row_s"] = row_q, row_s
+    if which & COLWISE:
+        rows = padded_rows(s)
+        col_q = np.zeros(C * rows // per, np.uint8)
+        col_s = np.zeros(C * rows // 32, np.uint8)
+        out["col_q"], out["col_s"] = col_q, col_s
+    rc = lib().oracle_grouped_act_quantize(act, _p(h), _p(p), _p(d), R, C, _p(s), s.size, recipe, which,
+                                           _p(row_q), _p(row_s), _p(col_q), _p(col_s))
+    if rc != 0:
+        raise ValueError(f"oracle_grouped_act_quantize failed ({rc})")
     return out
 
 

@@ -326,9 +326,15 @@ static int mx_block(const float* vals, int64_t nlive, int recipe, uint8_t* q) {
  *           or fp32 C*sum(Kp_e)/128 (per-channel)
  * Only live rows are written for the rowwise outputs; the colwise outputs are written in full.
  */
-int oracle_grouped_quantize(const uint16_t* in, int64_t R, int64_t C, const int32_t* splits,
-                            int32_t E, int recipe, int which, float zero_amax_scale,
-                            uint8_t* row_q, uint8_t* row_s, uint8_t* col_q, void* col_s) {
+/* Element (r, c) of the quantizer's input: a bf16 buffer, or fp32 values computed beforehand. */
+static float in_value(const uint16_t* in_bf16, const float* in_f32, int64_t C, int64_t r, int64_t c) {
+  return in_f32 ? in_f32[r * C + c] : bf16_to_f32(in_bf16[r * C + c]);
+}
+
+static int quantize_values(const uint16_t* in, const float* in_f32, int64_t R, int64_t C,
+                           const int32_t* splits, int32_t E, int recipe, int which,
+                           float zero_amax_scale, uint8_t* row_q, uint8_t* row_s, uint8_t* col_q,
+                           void* col_s) {
   group_t* g;
   group_t all;
   int32_t ng, e;
@@ -359,7 +365,7 @@ int oracle_grouped_quantize(const uint16_t* in, int64_t R, int64_t C, const int3
         uint8_t q[32];
         for (b = 0; b < C / 32; ++b) {
           int i, ex;
-          for (i = 0; i < 32; ++i) vals[i] = bf16_to_f32(in[r * C + b * 32 + i]);
+          for (i = 0; i < 32; ++i) vals[i] = in_value(in, in_f32, C, r, b * 32 + i);
           ex = mx_block(vals, 32, recipe, q);
           for (i = 0; i < 32; ++i) elem_store(row_q, r * C + b * 32 + i, q[i], recipe);
           row_s[b * R + r] = (uint8_t)(ex + 127);
@@ -386,7 +392,7 @@ int oracle_grouped_quantize(const uint16_t* in, int64_t R, int64_t C, const int3
           int64_t nlive = k - t0;
           if (nlive > blk) nlive = blk;
           if (nlive < 0) nlive = 0;
-          for (t = 0; t < nlive; ++t) vals[t] = bf16_to_f32(in[(off + t0 + t) * C + c]);
+          for (t = 0; t < nlive; ++t) vals[t] = in_value(in, in_f32, C, off + t0 + t, c);
           if (recipe == RECIPE_PC) {
             float sf = pc_block(vals, nlive, zero_amax_scale, q);
             ((float*)col_s)[C * P / 128 + b * C + c] = sf;
@@ -401,6 +407,69 @@ int oracle_grouped_quantize(const uint16_t* in, int64_t R, int64_t C, const int3
   }
   if (splits != NULL) free(g);
   return ORACLE_OK;
+}
+
+int oracle_grouped_quantize(const uint16_t* in, int64_t R, int64_t C, const int32_t* splits,
+                            int32_t E, int recipe, int which, float zero_amax_scale,
+                            uint8_t* row_q, uint8_t* row_s, uint8_t* col_q, void* col_s) {
+  return quantize_values(in, NULL, R, C, splits, E, recipe, which, zero_amax_scale, row_q, row_s, col_q, col_s);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Activation fused with the quantize: the ScaledSReLU step between fc1 and fc2 of the         */
+/* TransformerEngine #3484 reproducer (fc1 -> ScaledSReLU -> fc2, per-token probs).            */
+/* ------------------------------------------------------------------------------------------ */
+
+/*
+ * Squared ReLU scaled by the token's routing probability, and its gradient, in fp32 (each
+ * product rounded to fp32, in this order; r is +0 for h <= 0, including -0):
+ *   act 1 (forward)  : r = max(h, 0);  y = (r * r) * p
+ *   act 2 (backward) : r = max(h, 0);  g = ((2 * r) * p) * dy
+ * h and dy are bf16 [R][C]; probs fp32 [R] (NULL means p = 1).  The fp32 values of the live rows
+ * are then quantized exactly like a bf16 input (MX recipes; per-channel is not offered).
+ */
+static float act_value(int act, float hv, float p, float d) {
+  float r = hv > 0.0f ? hv : 0.0f;
+  if (act == 1) {
+    float r2 = r * r;
+    return r2 * p;
+  } else {
+    float tp = (2.0f * r) * p;
+    return tp * d;
+  }
+}
+
+/* The activation values themselves, element by element (h, dy bf16; p fp32 per element). */
+void oracle_act_values(int act, const uint16_t* h, const float* p, const uint16_t* dy, int64_t n, float* out) {
+  int64_t i;
+  for (i = 0; i < n; ++i) out[i] = act_value(act, bf16_to_f32(h[i]), p[i], dy ? bf16_to_f32(dy[i]) : 0.0f);
+}
+
+int oracle_grouped_act_quantize(int act, const uint16_t* h, const float* probs, const uint16_t* dy,
+                                int64_t R, int64_t C, const int32_t* splits, int32_t E, int recipe,
+                                int which, uint8_t* row_q, uint8_t* row_s, uint8_t* col_q, void* col_s) {
+  float* y;
+  group_t* g;
+  int32_t e;
+  int rc;
+  if ((act != 1 && act != 2) || (act == 2 && dy == NULL) || recipe == RECIPE_PC) return ORACLE_EINVAL;
+  if (C <= 0 || C % 32 != 0 || R < 0 || splits == NULL || E <= 0) return ORACLE_EINVAL;
+  g = (group_t*)malloc(sizeof(group_t) * (size_t)E);
+  y = (float*)calloc((size_t)(R > 0 ? R : 1) * (size_t)C, sizeof(float));
+  if (!g || !y) { free(g); free(y); return ORACLE_ENOMEM; }
+  if (group_layout(splits, E, R, g) != ORACLE_OK) { free(g); free(y); return ORACLE_EINVAL; }
+  for (e = 0; e < E; ++e) {
+    int64_t t, c;
+    for (t = g[e].off; t < g[e].off + g[e].k; ++t) { /* live rows only */
+      float p = probs ? probs[t] : 1.0f;
+      for (c = 0; c < C; ++c)
+        y[t * C + c] = act_value(act, bf16_to_f32(h[t * C + c]), p, act == 2 ? bf16_to_f32(dy[t * C + c]) : 0.0f);
+    }
+  }
+  rc = quantize_values(NULL, y, R, C, splits, E, recipe, which, 0.0f, row_q, row_s, col_q, col_s);
+  free(g);
+  free(y);
+  return rc;
 }
 
 /* ------------------------------------------------------------------------------------------ */
