@@ -23,6 +23,8 @@ RECIPE_PC = 2  # BSFP8_RECIPE_PER_CHANNEL_128_F32
 RECIPE_MX4 = 3  # BSFP8_RECIPE_MXFP4_1X32_E8M0
 ROWWISE = 1
 COLWISE = 2
+ACT_SRELU = 1  # BSFP8_ACT_SRELU: y = p * max(h, 0)^2
+ACT_SRELU_GRAD = 2  # BSFP8_ACT_SRELU_GRAD: g = dy * p * 2 max(h, 0)
 OUT_F32 = 0
 OUT_BF16 = 1
 STATUS_NEGATIVE_SPLIT = 1
@@ -62,6 +64,9 @@ def lib():
         L.bsfp8_grouped_quantize.restype = ctypes.c_int
         L.bsfp8_grouped_quantize.argtypes = [_vp, _i64, _i64, _vp, _i32, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.bsfp8_grouped_act_quantize.restype = ctypes.c_int
+        L.bsfp8_grouped_act_quantize.argtypes = [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _vp, _i32, ctypes.c_int,
+                                                 ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]
         L.bsfp8_grouped_gemm_wgrad.restype = ctypes.c_int
         L.bsfp8_grouped_gemm_wgrad.argtypes = [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i64, ctypes.c_int,
                                                _vp, ctypes.c_int, _vp, _vp]
@@ -165,6 +170,21 @@ def grouped_quantize(x, split_sizes, recipe, which, out, zero_amax_scale=1e-30, 
                                       _ptr(out.get("row_q")), _ptr(out.get("row_s")), _ptr(out.get("col_q")),
                                       _ptr(out.get("col_s")), _ptr(noop_flag), _ptr(status), _stream(stream))
     _check(rc, "grouped_quantize")
+    return out
+
+
+def grouped_act_quantize(activation, h, split_sizes, recipe, which, out, probs=None, dy=None, status=None,
+                         stream=None):
+    """bsfp8_grouped_act_quantize: the scaled squared ReLU (ACT_SRELU) of the bf16 [R, C] tensor
+    h, or its gradient (ACT_SRELU_GRAD, with the bf16 gradient dy), times the float32 per-row
+    probs (None: 1), quantized into ``out`` (see alloc_quantized) with an MX recipe."""
+    R, C = h.shape
+    E = int(split_sizes.numel())
+    rc = lib().bsfp8_grouped_act_quantize(activation, _ptr(h), _ptr(probs), _ptr(dy), R, C, _ptr(split_sizes), E,
+                                          recipe, which, _ptr(out.get("row_q")), _ptr(out.get("row_s")),
+                                          _ptr(out.get("col_q")), _ptr(out.get("col_s")), _ptr(status),
+                                          _stream(stream))
+    _check(rc, "grouped_act_quantize")
     return out
 
 

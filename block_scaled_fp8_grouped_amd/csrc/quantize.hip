@@ -34,11 +34,35 @@ struct QTile {
   int nlive;     // live rows of the tile (<= 128)
 };
 
-template <int RECIPE, bool ROW, bool COL>
+// Inputs of the activation fused in front of the quantizer (ACT != 0): the routing probability of
+// each token row (NULL: 1) and, for the gradient, the incoming bf16 gradient.
+struct ActArgs {
+  const float* probs;
+  const uint16_t* dy;
+};
+
+// The scaled squared ReLU between fc1 and fc2 (TE #3484 reproducer, fc1 -> ScaledSReLU -> fc2),
+// in fp32 with each product rounded in this order; r is +0 for h <= 0 (also for h = -0):
+//   ACT 1: y = (r * r) * p          ACT 2 (its gradient): g = ((2 * r) * p) * dy
+template <int ACT>
+__device__ __forceinline__ float act_value(float h, float p, float d) {
+  const float r = h > 0.0f ? h : 0.0f;
+  if constexpr (ACT == 1) {
+    const float r2 = r * r;
+    return r2 * p;
+  } else {
+    const float tp = (2.0f * r) * p;
+    return tp * d;
+  }
+}
+
+template <int RECIPE, bool ROW, bool COL, int ACT = 0>
 __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
     const uint16_t* __restrict__ in, int64_t R, int64_t C, const int32_t* __restrict__ splits, int E,
     float zero_amax_scale, uint8_t* __restrict__ row_q, uint8_t* __restrict__ row_s,
-    uint8_t* __restrict__ col_q, void* __restrict__ col_s, const float* noop_flag, uint32_t* status) {
+    uint8_t* __restrict__ col_q, void* __restrict__ col_s, const float* noop_flag, uint32_t* status,
+    ActArgs act) {
+  static_assert(ACT == 0 || RECIPE != BSFP8_RECIPE_PER_CHANNEL_128_F32, "the fused activation takes MX recipes");
   // a set flag turns the whole call into a no-op: the outputs (and the status word) keep what
   // they hold, which lets a captured graph skip re-quantizing a cached weight
   if (noop_flag != nullptr && *noop_flag != 0.0f) return;
@@ -46,6 +70,8 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t tile[kQRows][kQCols / 2];  // bf16 pairs
   __shared__ float pc_amax[4][kQCols];
   __shared__ uint8_t rs_tile[kQCols / 32][kQRows];
+  __shared__ __attribute__((aligned(16))) uint32_t tile_dy[ACT == 2 ? kQRows : 1][kQCols / 2];  // gradient
+  __shared__ float prow[ACT != 0 ? kQRows : 1];  // the tile rows' probabilities (0 past the live rows)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -90,6 +116,8 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
 
   // this thread's share of a tile: 16 lanes per row, 8 channels (16 bytes) each
   v4i pre[kQRows / 16];
+  v4i pre_dy[ACT == 2 ? kQRows / 16 : 1];
+  float pre_p = 0.0f;
   auto load_tile = [&](const QTile& q) {
 #pragma unroll
     for (int pass = 0; pass < kQRows / 16; ++pass) {
@@ -97,6 +125,14 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
       const int ch = tid & 15;
       pre[pass] = v4i{0, 0, 0, 0};
       if (r < q.nlive && ch * 8 < ncols) pre[pass] = *(const v4i*)(in + (q.row0 + r) * C + c0 + ch * 8);
+      if constexpr (ACT == 2) {
+        pre_dy[pass] = v4i{0, 0, 0, 0};
+        if (r < q.nlive && ch * 8 < ncols) pre_dy[pass] = *(const v4i*)(act.dy + (q.row0 + r) * C + c0 + ch * 8);
+      }
+    }
+    if constexpr (ACT != 0) {
+      pre_p = 0.0f;
+      if (tid < q.nlive) pre_p = act.probs != nullptr ? act.probs[q.row0 + tid] : 1.0f;
     }
   };
 
@@ -105,7 +141,13 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
   load_tile(cur);
   for (int t = 0; t < kQTilesPerWG; ++t) {
 #pragma unroll
-    for (int pass = 0; pass < kQRows / 16; ++pass) *(v4i*)&tile[pass * 16 + (tid >> 4)][(tid & 15) * 4] = pre[pass];
+    for (int pass = 0; pass < kQRows / 16; ++pass) {
+      *(v4i*)&tile[pass * 16 + (tid >> 4)][(tid & 15) * 4] = pre[pass];
+      if constexpr (ACT == 2) *(v4i*)&tile_dy[pass * 16 + (tid >> 4)][(tid & 15) * 4] = pre_dy[pass];
+    }
+    if constexpr (ACT != 0) {
+      if (tid < kQRows) prow[tid] = pre_p;
+    }
     __syncthreads();
     // the next tile's loads are in flight while this one is quantized
     QTile nxt;
@@ -114,7 +156,55 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
     const int64_t row0 = cur.row0, P = cur.p, kp = cur.kp, jblk = cur.jblk;
     const int nlive = cur.nlive;
 
-    if constexpr (COL) {
+    if constexpr (COL && ACT != 0) {
+      // ---- colwise with the activation: the same split, on the fp32 activation values ----
+      constexpr bool F4 = RECIPE == BSFP8_RECIPE_MXFP4_1X32_E8M0;
+      const int c = 2 * lane;
+      float y0[32], y1[32];
+      uint32_t m0 = 0, m1 = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int r = wave * 32 + i;
+        const uint32_t hw = tile[r][lane], dw = ACT == 2 ? tile_dy[r][lane] : 0u;
+        const float p = prow[r];
+        y0[i] = act_value<ACT>(bf16_lo(hw), p, bf16_lo(dw));
+        y1[i] = act_value<ACT>(bf16_hi(hw), p, bf16_hi(dw));
+        m0 = max(m0, __float_as_uint(y0[i]) & 0x7fffffffu);
+        m1 = max(m1, __float_as_uint(y1[i]) & 0x7fffffffu);
+      }
+      const int e0 = F4 ? e8m0_exponent_fp4(__uint_as_float(m0)) : e8m0_exponent(__uint_as_float(m0));
+      const int e1 = F4 ? e8m0_exponent_fp4(__uint_as_float(m1)) : e8m0_exponent(__uint_as_float(m1));
+      const float s0 = exp2_neg(e0), s1 = exp2_neg(e1);
+      const uint32_t sbits = (uint32_t)(e0 + 127) | ((uint32_t)(e1 + 127) << 8);
+      if (c0 + c < C) {
+        if constexpr (F4) {
+          v4i q0, q1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float* a = y0 + 8 * i;
+            const float* b = y1 + 8 * i;
+            q0[i] = (int)e2m1x8(a[0] * s0, a[1] * s0, a[2] * s0, a[3] * s0, a[4] * s0, a[5] * s0, a[6] * s0, a[7] * s0);
+            q1[i] = (int)e2m1x8(b[0] * s1, b[1] * s1, b[2] * s1, b[3] * s1, b[4] * s1, b[5] * s1, b[6] * s1, b[7] * s1);
+          }
+          uint8_t* dst = col_q + (C * P + (c0 + c) * kp) / 2 + kQRows / 2 * jblk + 16 * wave;
+          *(v4i*)dst = q0;
+          *(v4i*)(dst + kp / 2) = q1;
+        } else {
+          v4i q0[2], q1[2];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            q0[i >> 2][i & 3] = (int)e4m3x4(y0[4 * i] * s0, y0[4 * i + 1] * s0, y0[4 * i + 2] * s0, y0[4 * i + 3] * s0);
+            q1[i >> 2][i & 3] = (int)e4m3x4(y1[4 * i] * s1, y1[4 * i + 1] * s1, y1[4 * i + 2] * s1, y1[4 * i + 3] * s1);
+          }
+          uint8_t* dst = col_q + C * P + (c0 + c) * kp + kQRows * jblk + 32 * wave;
+          *(v4i*)dst = q0[0];
+          *(v4i*)(dst + 16) = q0[1];
+          *(v4i*)(dst + kp) = q1[0];
+          *(v4i*)(dst + kp + 16) = q1[1];
+        }
+        *(uint16_t*)((uint8_t*)col_s + C * P / 32 + (4 * jblk + wave) * C + c0 + c) = (uint16_t)sbits;
+      }
+    } else if constexpr (COL) {
       // ---- colwise: wave -> 32 tokens, lane -> channel pair ----
       const int c = 2 * lane;
       uint32_t w[32];
@@ -208,22 +298,38 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
         const int ch = tid & 15;
         const v4i v = *(const v4i*)&tile[r][ch * 4];
         uint32_t m = 0;
+        float yv[8];  // the values this lane quantizes (bf16 inputs, or the activation's fp32 values)
+        if constexpr (ACT != 0) {
+          const v4i vd = ACT == 2 ? *(const v4i*)&tile_dy[r][ch * 4] : v4i{0, 0, 0, 0};
+          const float p = prow[r];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = max(m, max((uint32_t)v[i] & 0x7fffu, ((uint32_t)v[i] >> 16) & 0x7fffu));
+          for (int i = 0; i < 4; ++i) {
+            yv[2 * i] = act_value<ACT>(bf16_lo((uint32_t)v[i]), p, bf16_lo((uint32_t)vd[i]));
+            yv[2 * i + 1] = act_value<ACT>(bf16_hi((uint32_t)v[i]), p, bf16_hi((uint32_t)vd[i]));
+            m = max(m, max(__float_as_uint(yv[2 * i]) & 0x7fffffffu, __float_as_uint(yv[2 * i + 1]) & 0x7fffffffu));
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            yv[2 * i] = bf16_lo((uint32_t)v[i]);
+            yv[2 * i + 1] = bf16_hi((uint32_t)v[i]);
+            m = max(m, max((uint32_t)v[i] & 0x7fffu, ((uint32_t)v[i] >> 16) & 0x7fffu));
+          }
+          m <<= 16;  // the bf16 magnitude's fp32 bits
+        }
         m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
         m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
-        const float amax = __uint_as_float(m << 16);
+        const float amax = __uint_as_float(m);
         const int e = RECIPE == BSFP8_RECIPE_MXFP4_1X32_E8M0 ? e8m0_exponent_fp4(amax) : e8m0_exponent(amax);
         const float s = exp2_neg(e);
         if (r < nlive && ch * 8 < ncols) {
           if constexpr (RECIPE == BSFP8_RECIPE_MXFP4_1X32_E8M0) {  // 8 codes -> 4 bytes
-            *(uint32_t*)(row_q + ((row0 + r) * C + c0 + ch * 8) / 2) =
-                e2m1x8(bf16_lo(v[0]) * s, bf16_hi(v[0]) * s, bf16_lo(v[1]) * s, bf16_hi(v[1]) * s,
-                       bf16_lo(v[2]) * s, bf16_hi(v[2]) * s, bf16_lo(v[3]) * s, bf16_hi(v[3]) * s);
+            *(uint32_t*)(row_q + ((row0 + r) * C + c0 + ch * 8) / 2) = e2m1x8(
+                yv[0] * s, yv[1] * s, yv[2] * s, yv[3] * s, yv[4] * s, yv[5] * s, yv[6] * s, yv[7] * s);
           } else {
             v2i q;
-            q[0] = (int)e4m3x4(bf16_lo(v[0]) * s, bf16_hi(v[0]) * s, bf16_lo(v[1]) * s, bf16_hi(v[1]) * s);
-            q[1] = (int)e4m3x4(bf16_lo(v[2]) * s, bf16_hi(v[2]) * s, bf16_lo(v[3]) * s, bf16_hi(v[3]) * s);
+            q[0] = (int)e4m3x4(yv[0] * s, yv[1] * s, yv[2] * s, yv[3] * s);
+            q[1] = (int)e4m3x4(yv[4] * s, yv[5] * s, yv[6] * s, yv[7] * s);
             *(v2i*)(row_q + (row0 + r) * C + c0 + ch * 8) = q;
           }
         }
@@ -262,26 +368,70 @@ int launch_grouped_quantize(const void* in, int64_t R, int64_t C, const int32_t*
   if (recipe == BSFP8_RECIPE_MX_1X32_E8M0) {
     if (row && col)
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MX_1X32_E8M0, true, true>), grid, block, 0, stream, x,
-                         R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status);
+                         R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{});
     else if (row)
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MX_1X32_E8M0, true, false>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status);
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{});
     else
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MX_1X32_E8M0, false, true>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status);
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{});
   } else if (recipe == BSFP8_RECIPE_MXFP4_1X32_E8M0) {
     if (row && col)
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MXFP4_1X32_E8M0, true, true>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status);
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{});
     else if (row)
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MXFP4_1X32_E8M0, true, false>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status);
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{});
     else
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MXFP4_1X32_E8M0, false, true>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status);
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{});
   } else {
     hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_PER_CHANNEL_128_F32, false, true>), grid, block, 0,
-                       stream, x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status);
+                       stream, x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{});
+  }
+  return hipGetLastError() == hipSuccess ? BSFP8_OK : BSFP8_ERR_LAUNCH;
+}
+
+template <int RECIPE, int ACT>
+static void launch_act(dim3 grid, dim3 block, hipStream_t stream, bool row, bool col, const uint16_t* x, int64_t R,
+                       int64_t C, const int32_t* splits, int E, uint8_t* row_q, uint8_t* row_s, uint8_t* col_q,
+                       void* col_s, uint32_t* status, ActArgs a) {
+  if (row && col)
+    hipLaunchKernelGGL((grouped_quantize_kernel<RECIPE, true, true, ACT>), grid, block, 0, stream, x, R, C, splits, E,
+                       0.0f, row_q, row_s, col_q, col_s, nullptr, status, a);
+  else if (row)
+    hipLaunchKernelGGL((grouped_quantize_kernel<RECIPE, true, false, ACT>), grid, block, 0, stream, x, R, C, splits, E,
+                       0.0f, row_q, row_s, col_q, col_s, nullptr, status, a);
+  else
+    hipLaunchKernelGGL((grouped_quantize_kernel<RECIPE, false, true, ACT>), grid, block, 0, stream, x, R, C, splits, E,
+                       0.0f, row_q, row_s, col_q, col_s, nullptr, status, a);
+}
+
+int launch_grouped_act_quantize(int act, const void* h, const float* probs, const void* dy, int64_t R, int64_t C,
+                                const int32_t* splits, int E, int recipe, int which, uint8_t* row_q, uint8_t* row_s,
+                                uint8_t* col_q, void* col_s, uint32_t* status, hipStream_t stream) {
+  const int64_t gx = (quantize_row_tiles(R, E, true) + kQTilesPerWG - 1) / kQTilesPerWG;
+  const int64_t gy = (C + kQCols - 1) / kQCols;
+  if (gx <= 0 || gy <= 0) return BSFP8_OK;
+  if (gx * gy > 0x7fffffff) return BSFP8_ERR_SHAPE;
+  dim3 grid((unsigned)(gx * gy)), block(kQThreads);
+  const uint16_t* x = (const uint16_t*)h;
+  const bool row = (which & BSFP8_ROWWISE) != 0, col = (which & BSFP8_COLWISE) != 0;
+  const ActArgs a{probs, (const uint16_t*)dy};
+  if (recipe == BSFP8_RECIPE_MX_1X32_E8M0) {
+    if (act == BSFP8_ACT_SRELU)
+      launch_act<BSFP8_RECIPE_MX_1X32_E8M0, 1>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q,
+                                               col_s, status, a);
+    else
+      launch_act<BSFP8_RECIPE_MX_1X32_E8M0, 2>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q,
+                                               col_s, status, a);
+  } else {
+    if (act == BSFP8_ACT_SRELU)
+      launch_act<BSFP8_RECIPE_MXFP4_1X32_E8M0, 1>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s,
+                                                  col_q, col_s, status, a);
+    else
+      launch_act<BSFP8_RECIPE_MXFP4_1X32_E8M0, 2>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s,
+                                                  col_q, col_s, status, a);
   }
   return hipGetLastError() == hipSuccess ? BSFP8_OK : BSFP8_ERR_LAUNCH;
 }

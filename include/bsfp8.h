@@ -51,6 +51,10 @@ extern "C" {
 #define BSFP8_ROWWISE 1 /* blocks along a row (channels); used by the forward GEMM */
 #define BSFP8_COLWISE 2 /* blocks along the token axis within each group; used by wgrad */
 
+/* Activations of bsfp8_grouped_act_quantize. */
+#define BSFP8_ACT_SRELU 1      /* y = p * max(h, 0)^2 (scaled squared ReLU) */
+#define BSFP8_ACT_SRELU_GRAD 2 /* g = dy * p * 2 max(h, 0) (its gradient with respect to h) */
+
 /* Output element types of bsfp8_grouped_gemm_fprop. */
 #define BSFP8_OUT_F32 0
 #define BSFP8_OUT_BF16 1
@@ -138,6 +142,33 @@ int bsfp8_grouped_quantize(const void* in_bf16, int64_t capacity_rows, int64_t c
                            const int32_t* split_sizes, int32_t num_groups, int recipe, int which,
                            float zero_amax_scale, uint8_t* row_q, uint8_t* row_s, uint8_t* col_q,
                            void* col_s, const float* noop_flag, uint32_t* status, void* stream);
+
+/* ----------------------------------------------------------------------------------------- */
+/* Activation fused with the grouped quantize (TE #3484 reproducer: fc1 -> ScaledSReLU -> fc2   */
+/* with per-token probs; the activation's formula is the usual scaled squared ReLU).          */
+/* ----------------------------------------------------------------------------------------- */
+/*
+ * h_bf16      [capacity_rows][cols] bf16: fc1's output (forward) or fc1's output saved for the
+ *             backward (BSFP8_ACT_SRELU_GRAD).
+ * probs       device fp32 [capacity_rows]: the token's routing probability p, or NULL for p = 1.
+ * dy_bf16     [capacity_rows][cols] bf16, the gradient arriving at the activation's output
+ *             (BSFP8_ACT_SRELU_GRAD only; NULL otherwise).
+ * activation  BSFP8_ACT_SRELU:      y = (r * r) * p
+ *             BSFP8_ACT_SRELU_GRAD: g = ((2 * r) * p) * dy
+ *             with r = h for h > 0 and +0 otherwise, every product rounded to fp32 in this order
+ *             (no fused multiply-add).  The fp32 values of the live rows are quantized as
+ *             bsfp8_grouped_quantize quantizes a bf16 input, for recipe
+ *             BSFP8_RECIPE_MX_1X32_E8M0 or BSFP8_RECIPE_MXFP4_1X32_E8M0, into the same layouts
+ *             (rowwise for the next GEMM's forward, colwise for its weight gradient).
+ * split_sizes is required; rows at or past sum(split_sizes) (of h, dy and probs) are never read.
+ * Outputs, status and errors as bsfp8_grouped_quantize; capacity_rows == 0 returns BSFP8_OK
+ * without touching any pointer.
+ */
+int bsfp8_grouped_act_quantize(int activation, const void* h_bf16, const float* probs,
+                               const void* dy_bf16, int64_t capacity_rows, int64_t cols,
+                               const int32_t* split_sizes, int32_t num_groups, int recipe, int which,
+                               uint8_t* row_q, uint8_t* row_s, uint8_t* col_q, void* col_s,
+                               uint32_t* status, void* stream);
 
 /* ----------------------------------------------------------------------------------------- */
 /* k-grouped weight-gradient GEMM (DeepGEMM #365, k_grouped_fp8_gemm_nt_contiguous; TE #3484, */

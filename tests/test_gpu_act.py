@@ -1,0 +1,116 @@
+"""The activation fused with the grouped quantize (the ScaledSReLU step between fc1 and fc2 in the
+TransformerEngine #3484 reproducer, and its gradient) on the GPU vs the CPU oracle: quantized
+bytes and scales bit-exact (both sides compute the activation in fp32 with the same rounding
+order, then take every quantization decision on the same fp32 value).
+
+Ragged groups, both layouts, MXFP8 and MXFP4, with and without probs (negative ones too),
+garbage padding (NaN/Inf in h, dy and probs past the live rows), signed zeros, the device status
+word, and the 32-expert MoE shape at full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_grouped_amd as bs
+import oracle
+import workloads as W
+from gpu_util import DEV, assert_quant_matches, flush, poisoned_quant_outputs
+
+pytestmark = pytest.mark.gpu
+RAGGED = [[0, 1, 31, 32, 33, 127, 128, 129, 256], [300, 0, 45, 1, 200], [1000], [0, 0, 5]]
+
+
+def _inputs(R, C, splits, seed, negative_probs=False):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    h = W.randn_bf16((R, C), g, DEV, scale=2.0)
+    dy = W.randn_bf16((R, C), g, DEV, scale=0.5)
+    p = torch.rand(R, generator=g, device=DEV)
+    if negative_probs:
+        p = p - 0.5
+    T = sum(splits)
+    rng = np.random.default_rng(seed)
+    for t in (h, dy):
+        bits = rng.integers(0, 1 << 16, size=(R - T, C), dtype=np.uint16)
+        t[T:] = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    p[T:] = float("nan")
+    return h, dy, p
+
+
+def _check(act, h, dy, p, splits, recipe, which, label):
+    R, C = h.shape
+    st = W.splits_tensor(splits, DEV)
+    out = poisoned_quant_outputs(R, C, len(splits), recipe, which)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bs.grouped_act_quantize(act, h, st, recipe, which, out, probs=p, dy=dy if act == bs.ACT_SRELU_GRAD else None,
+                            status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ref = oracle.grouped_act_quantize(act, W.bf16_bits(h), None if p is None else p.cpu().numpy(),
+                                      W.bf16_bits(dy) if act == bs.ACT_SRELU_GRAD else None, splits,
+                                      recipe, which)
+    assert_quant_matches(out, ref, splits, R, which, label)
+
+
+@pytest.mark.parametrize("act", [bs.ACT_SRELU, bs.ACT_SRELU_GRAD])
+@pytest.mark.parametrize("recipe", [bs.RECIPE_MX, bs.RECIPE_MX4])
+@pytest.mark.parametrize("splits", RAGGED)
+@pytest.mark.parametrize("C", [32, 160, 512])
+def test_act_quantize_parity(act, recipe, splits, C):
+    flush(f"act={act} recipe={recipe} C={C} splits={splits}")
+    T = sum(splits)
+    h, dy, p = _inputs(T + 37, C, splits, seed=C + T + act, negative_probs=(C == 160))
+    _check(act, h, dy, p, splits, recipe, bs.ROWWISE | bs.COLWISE, f"act{act} r{recipe} C={C}")
+
+
+@pytest.mark.parametrize("which", [bs.ROWWISE, bs.COLWISE])
+@pytest.mark.parametrize("act", [bs.ACT_SRELU, bs.ACT_SRELU_GRAD])
+def test_act_quantize_single_layout_and_no_probs(which, act):
+    flush(f"act={act} which={which} no probs")
+    splits = [130, 0, 257, 31]
+    h, dy, _ = _inputs(sum(splits) + 20, 288, splits, seed=7)
+    _check(act, h, dy, None, splits, bs.RECIPE_MX, which, f"act{act} which{which}")
+
+
+def test_act_quantize_signed_zeros_and_negative_inputs():
+    flush("act signed zeros")
+    splits = [64]
+    C = 64
+    g = torch.Generator(device=DEV).manual_seed(2)
+    h = W.randn_bf16((64, C), g, DEV)
+    h[:, :8] = -0.0
+    h[:, 8:16] = 0.0
+    h[:4] = -h[:4].abs()
+    dy = W.randn_bf16((64, C), g, DEV)
+    p = torch.linspace(-1, 1, 64, device=DEV)
+    for act in (bs.ACT_SRELU, bs.ACT_SRELU_GRAD):
+        _check(act, h, dy, p, splits, bs.RECIPE_MX, bs.ROWWISE | bs.COLWISE, f"zeros act{act}")
+
+
+def test_act_quantize_status_bits_and_no_writes():
+    flush("act status")
+    R, C = 300, 64
+    h, dy, p = _inputs(R, C, [R], seed=3)
+    for splits, bit in (([100, -5, 50], bs.STATUS_NEGATIVE_SPLIT), ([200, 200], bs.STATUS_EXCEEDS_CAPACITY)):
+        st = W.splits_tensor(splits, DEV)
+        out = poisoned_quant_outputs(R, C, len(splits), bs.RECIPE_MX, bs.ROWWISE | bs.COLWISE)
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        bs.grouped_act_quantize(bs.ACT_SRELU, h, st, bs.RECIPE_MX, bs.ROWWISE | bs.COLWISE, out, probs=p,
+                                status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) & bit
+        for t in out.values():
+            assert (t.view(torch.uint8) == 0xFF).all()
+
+
+def test_act_quantize_moe32_shape():
+    """fc1's output of the 32-expert layer (65,536 routed rows, ffn 1536, Zipf routing with empty
+    experts, garbage padding): forward activation + both MXFP8 layouts, all bytes."""
+    flush("act moe32")
+    case = W.moe32_zipf(DEV, with_weight=False)
+    splits, R = case["splits"], case["R"]
+    T = case["T"]
+    g = torch.Generator(device=DEV).manual_seed(40)
+    h = case["dy"]  # any [R, 1536] bf16 buffer of this shape and padding serves as fc1's output
+    p = torch.rand(R, generator=g, device=DEV)
+    _check(bs.ACT_SRELU, h, None, p, splits, bs.RECIPE_MX, bs.ROWWISE | bs.COLWISE, "moe32")
+    assert T < R
