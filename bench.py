@@ -307,6 +307,30 @@ def main():
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())}")
 
+    # The activation between fc1 and fc2 fused with the quantize: fc1's output here is a
+    # [T, ffn] bf16 buffer (the dy buffer of this workload serves, same shape and distribution),
+    # probs one fp32 per row; forward (y = p relu(h)^2) and gradient (g = dy p 2 relu(h)) into both
+    # MXFP8 layouts.  Timed on their own; not part of `value`.
+    log("activation + quantize leg")
+    aq = bs.alloc_quantized(R, n, E, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, dev)
+    probs = torch.rand(R, device=dev, generator=torch.Generator(device=dev).manual_seed(77))
+    act_ms = {}
+    for name, act in (("act_srelu_quantize", bs.ACT_SRELU), ("act_srelu_grad_quantize", bs.ACT_SRELU_GRAD)):
+        def run_act():
+            bs.grouped_act_quantize(act, case["dy"], st, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, aq, probs=probs,
+                                    dy=case["dy"] if act == bs.ACT_SRELU_GRAD else None, status=status)
+        run_act()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(5):
+            run_act()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        act_ms[name] = a0.elapsed_time(a1) / 5
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    del aq, probs
+
     # The same step with the MXFP4 recipe (e2m1 operands on the scaled fp4 MFMA), timed on its own
     # after the MXFP8 step; not part of `value`.
     mx4 = None
@@ -322,6 +346,8 @@ def main():
     bytes_w = E * N * K * (2 + 1 + 1 / 32)
     wgrad_bytes = (n + h) * kp_rows * (1 + 1 / 32) + 2 * 4.0 * n * h * sum(1 for k in splits if k)
     fprop_bytes = T * K * (1 + 1 / 32) + E * N * K * (1 + 1 / 32) + T * N * 2
+    # fused activation + quantize of [T, n]: read h (and dy) and probs, write both MXFP8 layouts
+    bytes_act = T * n * 2 + 4 * T + (T + kp_rows) * n * (1 + 1 / 32)
 
     wg_s = leg_ms["wgrad"] / 1e3
     achieved = wgrad_flop / wg_s / 1e12
@@ -368,6 +394,12 @@ def main():
             "fprop": {"ms": round(leg_ms["fprop"], 3),
                       "TFLOP/s": round(fprop_flop / (leg_ms["fprop"] / 1e3) / 1e12, 1),
                       "algorithmic_GB": round(fprop_bytes / 1e9, 2)},
+            # outside the step: the activation fused with the quantize of fc1's output
+            "act_srelu_quantize": {"ms": round(act_ms["act_srelu_quantize"], 3),
+                                   "GB/s": round(bytes_act / (act_ms["act_srelu_quantize"] / 1e3) / 1e9, 1)},
+            "act_srelu_grad_quantize": {"ms": round(act_ms["act_srelu_grad_quantize"], 3),
+                                        "GB/s": round((bytes_act + 2 * T * n)
+                                                      / (act_ms["act_srelu_grad_quantize"] / 1e3) / 1e9, 1)},
             # outside the step: the data-gradient GEMM and its quantize passes
             "quantize_dy_row": {"ms": round(dleg[0], 3),
                                 "GB/s": round(T * n * (2 + 1 + 1 / 32) / (dleg[0] / 1e3) / 1e9, 1)},
