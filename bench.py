@@ -289,6 +289,37 @@ def main():
     dleg = [sum(ev[i].elapsed_time(ev[i + 1]) for ev in dev_ev) / len(dev_ev) for i in range(3)]
     del dx, dyr, wcq
 
+    # The activation between fc1 and fc2 fused with the quantize: fc1's output here is a
+    # [T, ffn] bf16 buffer (the dy buffer of this workload serves, same shape and distribution),
+    # probs one fp32 per row; forward (y = p relu(h)^2) and gradient (g = dy p 2 relu(h)) into both
+    # MXFP8 layouts.  Timed on their own; not part of `value`.
+    log("activation + quantize leg")
+    aq = bs.alloc_quantized(R, n, E, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, dev)
+    probs = torch.rand(R, device=dev, generator=torch.Generator(device=dev).manual_seed(77))
+    g_act = W.randn_bf16((R, n), torch.Generator(device=dev).manual_seed(78), dev)  # the gradient at y
+    act_ms = {}
+    for name, act in (("act_srelu_quantize", bs.ACT_SRELU), ("act_srelu_grad_quantize", bs.ACT_SRELU_GRAD)):
+        def run_act():
+            bs.grouped_act_quantize(act, case["dy"], st, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, aq, probs=probs,
+                                    dy=g_act if act == bs.ACT_SRELU_GRAD else None, status=status)
+        run_act()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(5):
+            run_act()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        act_ms[name] = a0.elapsed_time(a1) / 5
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    del aq, probs, g_act
+
+    # The same step with the MXFP4 recipe (e2m1 operands on the scaled fp4 MFMA), timed on its own
+    # after the MXFP8 step; not part of `value`.
+    mx4 = None
+    if not args.no_mxfp4:
+        mx4 = mxfp4_leg(bs, W, case, st, R, n, h, K, N, E, mg, status, stream)
+
     # The same step captured once in a HIP graph and replayed: first with the weight quantize
     # running (noop flag 0, the step above), then as a later microbatch that reuses the cached
     # quantized weight (flag 1).  Replays accumulate into main_grad like eager steps.
@@ -306,36 +337,6 @@ def main():
         graph_ms = graph_leg(graph_step, flag, stream)
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())}")
-
-    # The activation between fc1 and fc2 fused with the quantize: fc1's output here is a
-    # [T, ffn] bf16 buffer (the dy buffer of this workload serves, same shape and distribution),
-    # probs one fp32 per row; forward (y = p relu(h)^2) and gradient (g = dy p 2 relu(h)) into both
-    # MXFP8 layouts.  Timed on their own; not part of `value`.
-    log("activation + quantize leg")
-    aq = bs.alloc_quantized(R, n, E, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, dev)
-    probs = torch.rand(R, device=dev, generator=torch.Generator(device=dev).manual_seed(77))
-    act_ms = {}
-    for name, act in (("act_srelu_quantize", bs.ACT_SRELU), ("act_srelu_grad_quantize", bs.ACT_SRELU_GRAD)):
-        def run_act():
-            bs.grouped_act_quantize(act, case["dy"], st, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, aq, probs=probs,
-                                    dy=case["dy"] if act == bs.ACT_SRELU_GRAD else None, status=status)
-        run_act()
-        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a0.record(stream)
-        for _ in range(5):
-            run_act()
-        a1.record(stream)
-        torch.cuda.synchronize()
-        act_ms[name] = a0.elapsed_time(a1) / 5
-    if int(status.item()) != 0:
-        raise RuntimeError(f"device status {int(status.item())}")
-    del aq, probs
-
-    # The same step with the MXFP4 recipe (e2m1 operands on the scaled fp4 MFMA), timed on its own
-    # after the MXFP8 step; not part of `value`.
-    mx4 = None
-    if not args.no_mxfp4:
-        mx4 = mxfp4_leg(bs, W, case, st, R, n, h, K, N, E, mg, status, stream)
 
     wgrad_flop = 2.0 * n * h * T
     fprop_flop = 2.0 * T * K * N
