@@ -91,7 +91,7 @@ def _run_wgrad(dy, x, splits, accumulate=False, mg=None):
     return out, dq, xq
 
 
-def _check_wgrad(dy, x, splits, accumulate=False, mg=None, label=""):
+def _check_wgrad(dy, x, splits, accumulate=False, mg=None, label="", rows_sel=None):
     R, n = dy.shape
     h = x.shape[1]
     out, dq, xq = _run_wgrad(dy, x, splits, accumulate, mg)
@@ -99,9 +99,10 @@ def _check_wgrad(dy, x, splits, accumulate=False, mg=None, label=""):
     o_x = oracle.grouped_quantize(W.bf16_bits(x), splits, oracle.RECIPE_MX4, oracle.COLWISE)
     assert_quant_matches(dq, o_dy, splits, R, bs.COLWISE, label + " dy")
     assert_quant_matches(xq, o_x, splits, R, bs.COLWISE, label + " x")
+    sel = np.arange(n, dtype=np.int32) if rows_sel is None else np.asarray(rows_sel, np.int32)
     ref = oracle.grouped_wgrad(o_dy["col_q"], o_dy["col_s"], n, o_x["col_q"], o_x["col_s"], h, splits, R,
-                               oracle.RECIPE_MX4)
-    got = out.cpu().numpy().astype(np.float64)
+                               oracle.RECIPE_MX4, rows_sel=sel)
+    got = out.cpu().numpy()[:, sel, :].astype(np.float64)
     for e, k in enumerate(splits):
         if k == 0:
             if accumulate:
@@ -109,7 +110,7 @@ def _check_wgrad(dy, x, splits, accumulate=False, mg=None, label=""):
             else:
                 assert (out[e] == 0).all(), f"{label} empty expert {e} not zero"
             continue
-        part = got[e] - mg[e].cpu().numpy().astype(np.float64) if accumulate else got[e]
+        part = got[e] - mg[e].cpu().numpy()[sel].astype(np.float64) if accumulate else got[e]
         r = rel_err(part, ref[e])
         assert r <= REL_TOL, f"{label} expert {e} (k={k}): rel {r:.3e}"
     return out
@@ -237,3 +238,93 @@ def test_mx4_repeated_calls_bitwise_identical():
         bs.grouped_gemm_wgrad(dq, n, xq, h, st, R, MX4, out)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int32), first.view(torch.int32))
+
+
+# ------------------------------------------------------------------------------------------
+# the MoE shapes at full size
+# ------------------------------------------------------------------------------------------
+
+def test_mx4_moe32_full_size_sampled():
+    """32 experts, 65,536 Zipf-routed rows (empty experts, counts not multiples of 32), garbage
+    padding, hidden 4096, ffn 1536: quantize bit-exact on the full tensors, wgrad on 64 sampled dy
+    channels of every expert, fprop fp32 on 32 sampled output columns."""
+    case = W.moe32_zipf(DEV)
+    splits, R = case["splits"], case["R"]
+    flush(f"mx4 moe32 R={R}")
+    rng = np.random.default_rng(41)
+    rows = np.sort(rng.choice(case["n"], 64, replace=False)).astype(np.int32)
+    _check_wgrad(case["dy"], case["x"], splits, label="mx4 moe32 wgrad", rows_sel=rows)
+    K, N = case["K"], case["N"]
+    cols = np.sort(rng.choice(N, 32, replace=False)).astype(np.int32)
+    w = case["W"].view(-1, K)
+    st = W.splits_tensor(splits, DEV)
+    xq = gpu_quantize(case["x"], splits, MX4, bs.ROWWISE)
+    wq = gpu_quantize(w, None, MX4, bs.ROWWISE)
+    out = torch.full((R, N), float("nan"), device=DEV)
+    bs.grouped_gemm_fprop(xq, K, wq, N, st, R, out, bs.OUT_F32, recipe=MX4)
+    torch.cuda.synchronize()
+    o_x = oracle.grouped_quantize(W.bf16_bits(case["x"]), splits, oracle.RECIPE_MX4, oracle.ROWWISE)
+    o_w = oracle.grouped_quantize(W.bf16_bits(w), None, oracle.RECIPE_MX4, oracle.ROWWISE)
+    assert_quant_matches(xq, o_x, splits, R, bs.ROWWISE, "mx4 moe32 x")
+    assert_quant_matches(wq, o_w, None, w.shape[0], bs.ROWWISE, "mx4 moe32 w")
+    ref = oracle.grouped_fprop(o_x["row_q"], o_x["row_s"], o_w["row_q"], o_w["row_s"], N, splits, cols_sel=cols,
+                               recipe=oracle.RECIPE_MX4)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isnan(got[sum(splits):]).all()
+    _check_rows(got[:, cols], ref, splits, bs.OUT_F32, "mx4 moe32 fprop")
+
+
+def test_mx4_moe128_sampled_experts():
+    """The benchmark's MXFP4 launches on the 128-expert shape (wgrad accumulating into main_grad,
+    fprop bf16), checked on three experts (largest, smallest non-empty, one between) against the
+    oracle on those experts' rows; empty experts' main_grad bitwise untouched."""
+    case = W.moe128_top8(DEV)
+    splits, R = case["splits"], case["R"]
+    n, h, K, N = case["n"], case["h"], case["K"], case["N"]
+    E = len(splits)
+    st = W.splits_tensor(splits, DEV)
+    flush("mx4 moe128")
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    xq = gpu_quantize(case["x"], splits, MX4, bs.COLWISE | bs.ROWWISE, status=status)
+    dq = gpu_quantize(case["dy"], splits, MX4, bs.COLWISE, status=status)
+    w2 = case["W"].view(E * N, K)
+    wq = gpu_quantize(w2, None, MX4, bs.ROWWISE)
+    mg0 = case["main_grad"]
+    empty = [e for e, k in enumerate(splits) if k == 0]
+    mg_empty = mg0[empty].clone()
+    live = [e for e, k in enumerate(splits) if k > 0]
+    sample = sorted({max(live, key=lambda e: splits[e]), min(live, key=lambda e: splits[e]), live[len(live) // 2]})
+    mg_before = {e: mg0[e].cpu().numpy().astype(np.float64) for e in sample}
+    rng = np.random.default_rng(51)
+    rows = np.sort(rng.choice(n, 32, replace=False)).astype(np.int32)
+    cols = np.sort(rng.choice(N, 16, replace=False)).astype(np.int32)
+    bs.grouped_gemm_wgrad(dq, n, xq, h, st, R, MX4, mg0, accumulate=True, status=status)
+    fout = torch.empty(R, N, dtype=torch.bfloat16, device=DEV)
+    bs.grouped_gemm_fprop(xq, K, wq, N, st, R, fout, bs.OUT_BF16, status=status, recipe=MX4)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(mg0[empty].view(torch.int32), mg_empty.view(torch.int32))
+    offs = np.concatenate([[0], np.cumsum(splits)])
+    kps = [128 * ((k + 127) // 128) for k in splits]
+    pofs = np.concatenate([[0], np.cumsum(kps)])
+    for e in sample:
+        k, off, P, kp = splits[e], int(offs[e]), int(pofs[e]), kps[e]
+        flush(f"mx4 moe128 expert {e} k={k}")
+        ox = oracle.grouped_quantize(W.bf16_bits(case["x"][off:off + k]), [k], oracle.RECIPE_MX4,
+                                     oracle.COLWISE | oracle.ROWWISE)
+        ody = oracle.grouped_quantize(W.bf16_bits(case["dy"][off:off + k]), [k], oracle.RECIPE_MX4, oracle.COLWISE)
+        ow = oracle.grouped_quantize(W.bf16_bits(w2[e * N:(e + 1) * N]), None, oracle.RECIPE_MX4, oracle.ROWWISE)
+        assert np.array_equal(xq["col_q"][h * P // 2:h * (P + kp) // 2].cpu().numpy(), ox["col_q"])
+        assert np.array_equal(dq["col_q"][n * P // 2:n * (P + kp) // 2].cpu().numpy(), ody["col_q"])
+        assert np.array_equal(dq["col_s"][n * P // 32:n * (P + kp) // 32].cpu().numpy(), ody["col_s"])
+        assert np.array_equal(xq["row_q"][off:off + k].cpu().numpy(), ox["row_q"])
+        assert np.array_equal(wq["row_q"][e * N:(e + 1) * N].cpu().numpy(), ow["row_q"])
+        ref = oracle.grouped_wgrad(ody["col_q"], ody["col_s"], n, ox["col_q"], ox["col_s"], h, [k], k,
+                                   oracle.RECIPE_MX4, rows_sel=rows)
+        got = mg0[e].cpu().numpy()[rows].astype(np.float64) - mg_before[e][rows]
+        r = rel_err(got, ref[0])
+        assert r <= REL_TOL, f"mx4 moe128 wgrad expert {e}: rel {r:.3e}"
+        fref = oracle.grouped_fprop(ox["row_q"], ox["row_s"], ow["row_q"], ow["row_s"], N, [k], cols_sel=cols,
+                                    recipe=oracle.RECIPE_MX4)
+        fgot = fout[off:off + k].float().cpu().numpy().astype(np.float64)[:, cols]
+        assert_bf16_close(fgot, fref, f"mx4 moe128 fprop expert {e}")
