@@ -6,6 +6,8 @@
 //         group's padded extent Kp_e, a multiple of 128 whose pad lanes hold zeros.
 //  fprop (m-grouped; TE PR #3224, grouped GEMM over a single grouped weight; the token axis is
 //         a free dimension): out[off_e + t] = x[off_e + t] W_e^T for t < k_e.
+//  dgrad (m-grouped, TE #3484 scope: the token axis is free in everything but wgrad): the fprop
+//         kernel with the colwise-quantized weight as B, out[off_e + t] = dy[off_e + t] W_e.
 //
 // Arithmetic.  The operands stay e4m3 (one byte) in HBM and LDS.  In registers every e4m3 value
 // is widened to bf16 with its block scale folded in (exact: e4m3 has 4 significant bits and a
@@ -23,21 +25,22 @@
 // sum of e2m1 products inside a block is a small multiple of 1/4, so the instruction's inner
 // sums are exact and the result is fp32-accumulated like the bf16 path.
 //
-// Tiling.  Workgroup tile BM x BN, K step 128, each wave owning a WM x WN block of 32 x 32
-// fragments.  MX recipe: 256 x 256 with 8 waves of 128 x 64 (two waves per SIMD, 128 fp32
-// accumulators each, so one wave's MFMAs run while the other waits on LDS or the barrier);
-// per-channel recipe: 128 x 128 with 4 waves of 64 x 64.  Per K step the A and
-// B tiles (rows of 128 bytes) and their scales are moved straight from HBM into LDS by
-// global_load_lds (16 bytes per lane, no staging registers), double-buffered; the 16-byte
-// chunks of each row are XOR-swizzled so that the fragment reads of consecutive rows spread
-// over all banks.  A lane of a 32 x 32 fragment owns row (lane % 32) and reads, for the K half
-// s of the step, chunks 4s + h and 4s + 2 + h (h = lane / 32): the first lies in 32-block 2s,
-// the second in 2s + 1, so each half-fragment has a single block scale.  The next step's loads
-// are issued once the first K half's fragments are read and overlap the step's MFMAs.
+// Tiling.  Workgroup tile BM x BN, K step of 128 bytes per row, each wave owning a WM x WN
+// block of 32 x 32 fragments.  MX recipes: 256 x 256 with 8 waves of 128 x 64 (two waves per
+// SIMD, 128 fp32 accumulators each, so one wave's MFMAs run while the other waits on LDS or the
+// barrier); per-channel recipe: 128 x 128 with 4 waves of 64 x 64.  Per K step the A and B
+// tiles (rows of 128 bytes) and their scales are moved straight from HBM into LDS by LDS DMA
+// (buffer loads with the lds flag, 16 bytes per lane, no staging registers), double-buffered;
+// the 16-byte chunks of each row are XOR-swizzled so that the fragment reads of consecutive
+// rows spread over all banks.  A lane of a 32 x 32 fragment owns row (lane % 32) and reads, for
+// the K half s of the step, chunks 4s + h and 4s + 2 + h (h = lane / 32): for MXFP8 the first
+// lies in 32-block 2s, the second in 2s + 1, so each half-fragment has a single block scale.
+// The next step's loads are issued once the first K half's fragments are read and overlap the
+// step's MFMAs.
 //
 // Determinism: one workgroup per output tile, fixed instruction order, no atomics, no split-K.
-// Rows past a group's live rows are clamped to its last live row on load (never read beyond
-// it) and their results are not stored.
+// Rows past a group's live rows lie outside the buffer range of the tile's loads, so they read
+// as zeros (nothing beyond the live rows is fetched), and their results are not stored.
 #include "common.hpp"
 #include "tile_addr.hpp"
 #include "tile_sched.hpp"
@@ -53,7 +56,7 @@ struct GemmArgs {
   const void* b_s;
   int64_t M;           // wgrad: n (dy channels)   fprop: unused (group rows)
   int64_t N;           // wgrad: h (x channels)    fprop: n (weight rows per expert)
-  int64_t K;           // fprop: reduction length
+  int64_t K;           // fprop / dgrad: reduction length in bytes of a row
   int64_t R;           // capacity rows
   // m-grouped B operand (fprop: the rowwise weight; dgrad: the colwise-quantized weight):
   int64_t b_ld;        // bytes per B row
@@ -624,7 +627,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
     const int64_t left = (MODE == kModeWgrad ? args.M : (int64_t)gi.k) - row0;
     const int vrows = left < 0 ? 0 : (left > WM ? WM : (int)left);  // valid rows of the block
     const int64_t org = (MODE == kModeWgrad ? (int64_t)e * args.M + row0 : gi.off + row0) * args.N + col0;
-    const uint32_t nbytes = vrows > 0 && col0 < args.N ? (uint32_t)(((int64_t)(vrows - 1) * args.N + args.N - col0) * ES) : 0u;
+    const uint32_t nbytes =
+        vrows > 0 && col0 < args.N ? (uint32_t)(((int64_t)(vrows - 1) * args.N + args.N - col0) * ES) : 0u;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((uint8_t*)args.out + org * ES, (short)0, (int)nbytes, 0x00020000);
     // byte offsets below WM * N * ES < 2^31 (host bound on N); a lane past the last column starts
