@@ -68,6 +68,9 @@ def lib():
         L.oracle_grouped_quantize.argtypes = [_vp, _i64, _i64, _vp, _i32, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_float, _vp, _vp, _vp, _vp]
         L.oracle_act_values.argtypes = [ctypes.c_int, _vp, _vp, _vp, _i64, _vp]
+        L.oracle_exp2_spec.restype = ctypes.c_float
+        L.oracle_exp2_spec.argtypes = [ctypes.c_float]
+        L.oracle_glu_values.argtypes = [ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _vp, _vp]
         L.oracle_grouped_act_quantize.restype = ctypes.c_int
         L.oracle_grouped_act_quantize.argtypes = [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _vp, _i32, ctypes.c_int,
                                                   ctypes.c_int, _vp, _vp, _vp, _vp]
@@ -191,6 +194,26 @@ def grouped_quantize(x_bits, splits, recipe, which, zero_amax_scale=1e-30):
 
 ACT_SRELU_FWD = 1  # y = p * relu(h)^2
 ACT_SRELU_BWD = 2  # g = dy * p * 2 relu(h)
+ACT_SWIGLU_FWD = 3  # y = silu(a) * b * p, (a | b) the halves of fc1's output row
+ACT_SWIGLU_BWD = 4  # (da | db) from dy * p
+
+
+def exp2_spec(x):
+    """The stated fp32 2^x of the GLU activations (see oracle.c), element by element."""
+    x = np.asarray(x, np.float32)
+    return np.array([lib().oracle_exp2_spec(float(v)) for v in x.ravel()], np.float32).reshape(x.shape)
+
+
+def glu_values(act, a_bits, b_bits, p, dy_bits=None):
+    """SwiGLU values (act 3: y; act 4: (da, db)) of bf16 a, b (and dy) with float32 p."""
+    a = _c(a_bits, np.uint16)
+    b = _c(b_bits, np.uint16)
+    pp = _c(p, np.float32)
+    d = None if dy_bits is None else _c(dy_bits, np.uint16)
+    o0 = np.empty(a.shape, np.float32)
+    o1 = np.empty(a.shape, np.float32) if act == ACT_SWIGLU_BWD else None
+    lib().oracle_glu_values(act, _p(a), _p(b), _p(pp), _p(d), a.size, _p(o0), _p(o1))
+    return o0 if act == ACT_SWIGLU_FWD else (o0, o1)
 
 
 def act_values(act, h_bits, p, dy_bits=None):
@@ -206,10 +229,14 @@ def act_values(act, h_bits, p, dy_bits=None):
 
 def grouped_act_quantize(act, h_bits, probs, dy_bits, splits, recipe, which):
     """Scaled squared ReLU (act 1) or its gradient (act 2) in fp32 on the live rows of the bf16
-    [R, C] buffer(s), then the grouped quantize of those values (MX recipes).  probs: float32 [R]
-    or None (p = 1).  Returns the same dict as grouped_quantize."""
+    [R, C] buffer(s), or scaled SwiGLU (act 3, h [R, 2F] -> y [R, F]) and its gradient (act 4,
+    h [R, 2F] and dy [R, F] -> (da | db) [R, 2F]), then the grouped quantize of those values (MX
+    recipes).  probs: float32 [R] or None (p = 1).  Returns the same dict as grouped_quantize."""
     h = _c(h_bits, np.uint16)
     R, C = h.shape
+    if act >= ACT_SWIGLU_FWD:
+        C //= 2  # the GLU width F
+    Cout = 2 * C if act == ACT_SWIGLU_BWD else C
     s = _c(splits, np.int32)
     p = None if probs is None else _c(probs, np.float32)
     d = None if dy_bits is None else _c(dy_bits, np.uint16)
@@ -217,13 +244,13 @@ def grouped_act_quantize(act, h_bits, probs, dy_bits, splits, recipe, which):
     out = {}
     row_q = row_s = col_q = col_s = None
     if which & ROWWISE:
-        row_q = np.zeros((R, C // per), np.uint8)
-        row_s = np.zeros((C // 32, R), np.uint8)
+        row_q = np.zeros((R, Cout // per), np.uint8)
+        row_s = np.zeros((Cout // 32, R), np.uint8)
         out["row_q"], out["row_s"] = row_q, row_s
     if which & COLWISE:
         rows = padded_rows(s)
-        col_q = np.zeros(C * rows // per, np.uint8)
-        col_s = np.zeros(C * rows // 32, np.uint8)
+        col_q = np.zeros(Cout * rows // per, np.uint8)
+        col_s = np.zeros(Cout * rows // 32, np.uint8)
         out["col_q"], out["col_s"] = col_q, col_s
     rc = lib().oracle_grouped_act_quantize(act, _p(h), _p(p), _p(d), R, C, _p(s), s.size, recipe, which,
                                            _p(row_q), _p(row_s), _p(col_q), _p(col_s))

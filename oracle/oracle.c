@@ -439,12 +439,76 @@ static float act_value(int act, float hv, float p, float d) {
   }
 }
 
+/* 2^x in fp32 by a stated algorithm, so that any IEEE fp32 machine reproduces it bit for bit:
+ * x is clamped to [-126, 126]; k = floor(x + 0.5) and r = x - k (exact, |r| <= 0.5); 2^r is the
+ * degree-7 Taylor polynomial of exp(r ln 2), coefficients (ln 2)^n / n! rounded to fp32, in
+ * Horner form with every operation rounded to fp32; the result is scaled by 2^k exactly.
+ * Relative error below 2e-7 (the truncated series term is below 1.5e-8). */
+float oracle_exp2_spec(float x) {
+  static const float c[8] = {1.0f, 0.693147182f, 0.240226507f, 0.0555041087f, 0.00961812911f,
+                             0.00133335581f, 0.000154035304f, 1.52527338e-05f};
+  float r, poly;
+  int k, n;
+  if (x > 126.0f) x = 126.0f;
+  if (x < -126.0f) x = -126.0f;
+  k = (int)floorf(x + 0.5f);
+  r = x - (float)k;
+  poly = c[7];
+  for (n = 6; n >= 0; --n) poly = poly * r + c[n];
+  return ldexpf(poly, k);
+}
+
+/* SwiGLU scaled by the token's probability, and its gradient, in fp32 with the stated exp:
+ *   sg = 1 / (1 + exp2_spec(-a * log2(e)));  s = a * sg                  (silu(a))
+ *   act 3 (forward) : y = (s * b) * p
+ *   act 4 (backward): q = dy * p;  da = (q * b) * (sg * (1 + a * (1 - sg)));  db = q * s
+ * with a, b the two halves of fc1's output row (a the first). */
+static void glu_values(float a, float b, float p, float d, float* y, float* da, float* db) {
+  const float log2e = 1.44269502f;
+  float t = oracle_exp2_spec(-a * log2e);
+  float den = 1.0f + t;
+  float sg = 1.0f / den;
+  float sl = a * sg;
+  if (y) {
+    float sb = sl * b;
+    *y = sb * p;
+  }
+  if (da) {
+    float q = d * p;
+    float u = 1.0f - sg;
+    float v = a * u;
+    float w = 1.0f + v;
+    float ds = sg * w;
+    float qb = q * b;
+    *da = qb * ds;
+    *db = q * sl;
+  }
+}
+
+/* The GLU values element by element: a, b, dy bf16 and p fp32 per element; act 3 writes y to
+ * out0, act 4 writes da to out0 and db to out1. */
+void oracle_glu_values(int act, const uint16_t* a, const uint16_t* b, const float* p, const uint16_t* dy, int64_t n,
+                       float* out0, float* out1) {
+  int64_t i;
+  for (i = 0; i < n; ++i) {
+    if (act == 3)
+      glu_values(bf16_to_f32(a[i]), bf16_to_f32(b[i]), p[i], 0.0f, &out0[i], NULL, NULL);
+    else
+      glu_values(bf16_to_f32(a[i]), bf16_to_f32(b[i]), p[i], bf16_to_f32(dy[i]), NULL, &out0[i], &out1[i]);
+  }
+}
+
 /* The activation values themselves, element by element (h, dy bf16; p fp32 per element). */
 void oracle_act_values(int act, const uint16_t* h, const float* p, const uint16_t* dy, int64_t n, float* out) {
   int64_t i;
   for (i = 0; i < n; ++i) out[i] = act_value(act, bf16_to_f32(h[i]), p[i], dy ? bf16_to_f32(dy[i]) : 0.0f);
 }
 
+/*
+ * acts 1, 2: h [R][C] (and dy [R][C]); the quantized output is [R][C].
+ * acts 3, 4 (SwiGLU): C is the GLU width F; h is [R][2F] (a = columns [0, F), b = [F, 2F));
+ *   act 3 quantizes y [R][F]; act 4 takes dy [R][F] and quantizes (da | db) as [R][2F].
+ */
 int oracle_grouped_act_quantize(int act, const uint16_t* h, const float* probs, const uint16_t* dy,
                                 int64_t R, int64_t C, const int32_t* splits, int32_t E, int recipe,
                                 int which, uint8_t* row_q, uint8_t* row_s, uint8_t* col_q, void* col_s) {
@@ -452,21 +516,32 @@ int oracle_grouped_act_quantize(int act, const uint16_t* h, const float* probs, 
   group_t* g;
   int32_t e;
   int rc;
-  if ((act != 1 && act != 2) || (act == 2 && dy == NULL) || recipe == RECIPE_PC) return ORACLE_EINVAL;
+  int64_t Cout = act == 4 ? 2 * C : C;
+  if (act < 1 || act > 4 || ((act == 2 || act == 4) && dy == NULL) || recipe == RECIPE_PC) return ORACLE_EINVAL;
   if (C <= 0 || C % 32 != 0 || R < 0 || splits == NULL || E <= 0) return ORACLE_EINVAL;
   g = (group_t*)malloc(sizeof(group_t) * (size_t)E);
-  y = (float*)calloc((size_t)(R > 0 ? R : 1) * (size_t)C, sizeof(float));
+  y = (float*)calloc((size_t)(R > 0 ? R : 1) * (size_t)Cout, sizeof(float));
   if (!g || !y) { free(g); free(y); return ORACLE_ENOMEM; }
   if (group_layout(splits, E, R, g) != ORACLE_OK) { free(g); free(y); return ORACLE_EINVAL; }
   for (e = 0; e < E; ++e) {
     int64_t t, c;
     for (t = g[e].off; t < g[e].off + g[e].k; ++t) { /* live rows only */
       float p = probs ? probs[t] : 1.0f;
-      for (c = 0; c < C; ++c)
-        y[t * C + c] = act_value(act, bf16_to_f32(h[t * C + c]), p, act == 2 ? bf16_to_f32(dy[t * C + c]) : 0.0f);
+      if (act <= 2) {
+        for (c = 0; c < C; ++c)
+          y[t * C + c] = act_value(act, bf16_to_f32(h[t * C + c]), p, act == 2 ? bf16_to_f32(dy[t * C + c]) : 0.0f);
+      } else {
+        for (c = 0; c < C; ++c) {
+          float a = bf16_to_f32(h[t * 2 * C + c]), b = bf16_to_f32(h[t * 2 * C + C + c]);
+          if (act == 3)
+            glu_values(a, b, p, 0.0f, &y[t * C + c], NULL, NULL);
+          else
+            glu_values(a, b, p, bf16_to_f32(dy[t * C + c]), NULL, &y[t * 2 * C + c], &y[t * 2 * C + C + c]);
+        }
+      }
     }
   }
-  rc = quantize_values(NULL, y, R, C, splits, E, recipe, which, 0.0f, row_q, row_s, col_q, col_s);
+  rc = quantize_values(NULL, y, R, Cout, splits, E, recipe, which, 0.0f, row_q, row_s, col_q, col_s);
   free(g);
   free(y);
   return rc;
