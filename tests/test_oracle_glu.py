@@ -4,8 +4,9 @@ The GLU activations need exp, whose last bits differ between libraries, so the m
 own fp32 exp2 (range reduction to |r| <= 1/2 and the degree-7 Taylor polynomial of 2^r); the pins
 are against the mathematics, in double precision:
 
-* the stated 2^x: exact at integers; relative error <= 3e-7 over [-126, 126] (a wrong
-  coefficient or reduction step shows up far above that, r = +-1/2 included); clamped outside;
+* the stated 2^x: exact at integers; relative error <= 3e-7 over [-126, 126]; clamped outside;
+  on the reduced range bit-equal to the polynomial with coefficients (ln 2)^n / n! computed from
+  their definition;
 * silu(a) = a / (1 + e^-a), its derivative sigma(a) (1 + a (1 - sigma(a))), and the product rule
   of the gradient (da, db) against double-precision formulas and a central finite difference;
 * the quantized outputs equal the torch MXFP8 route applied to the oracle's own activation values
@@ -37,6 +38,19 @@ def test_exp2_spec_against_the_exact_power():
     # clamped outside [-126, 126]
     assert oracle.exp2_spec(np.float32([300.0]))[0] == np.float32(2.0 ** 126)
     assert oracle.exp2_spec(np.float32([-300.0]))[0] == np.float32(2.0 ** -126)
+
+
+def test_exp2_spec_is_the_stated_polynomial():
+    """On the reduced range the value is the stated polynomial, bit for bit: coefficients
+    (ln 2)^n / n! computed here from their definition and rounded to fp32, Horner order, fp32
+    operations."""
+    c = [np.float32(math.log(2.0) ** n / math.factorial(n)) for n in range(8)]
+    rng = np.random.default_rng(3)
+    r = np.concatenate([rng.uniform(-0.5, 0.4999, 5000), [0.0, -0.5, 0.25, -0.25]]).astype(np.float32)
+    poly = np.full(r.shape, c[7], np.float32)
+    for n in range(6, -1, -1):
+        poly = (poly * r + c[n]).astype(np.float32)
+    assert np.array_equal(oracle.exp2_spec(r), poly)
 
 
 def test_silu_and_its_gradient_against_double_precision():
