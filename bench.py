@@ -312,7 +312,33 @@ def main():
         act_ms[name] = a0.elapsed_time(a1) / 5
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())}")
-    del aq, probs, g_act
+    del aq, g_act
+
+    # The scaled SwiGLU variant: fc1's output is (a | b) [T, 2 ffn]; forward y = p silu(a) b into
+    # [T, ffn], gradient (da | db) into [T, 2 ffn] from the gradient at y [T, ffn].
+    log("SwiGLU activation + quantize leg")
+    gen = torch.Generator(device=dev).manual_seed(79)
+    h_glu = W.randn_bf16((R, 2 * n), gen, dev, scale=2.0)
+    g_glu = W.randn_bf16((R, n), gen, dev)
+    for name, act, cols in (("act_swiglu_quantize", bs.ACT_SWIGLU, n),
+                            ("act_swiglu_grad_quantize", bs.ACT_SWIGLU_GRAD, 2 * n)):
+        gq = bs.alloc_quantized(R, cols, E, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, dev)
+
+        def run_glu():
+            bs.grouped_act_quantize(act, h_glu, st, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, gq, probs=probs,
+                                    dy=g_glu if act == bs.ACT_SWIGLU_GRAD else None, status=status)
+        run_glu()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(5):
+            run_glu()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        act_ms[name] = a0.elapsed_time(a1) / 5
+        del gq
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    del probs, h_glu, g_glu
 
     # The same step with the MXFP4 recipe (e2m1 operands on the scaled fp4 MFMA), timed on its own
     # after the MXFP8 step; not part of `value`.
@@ -349,6 +375,9 @@ def main():
     fprop_bytes = T * K * (1 + 1 / 32) + E * N * K * (1 + 1 / 32) + T * N * 2
     # fused activation + quantize of [T, n]: read h (and dy) and probs, write both MXFP8 layouts
     bytes_act = T * n * 2 + 4 * T + (T + kp_rows) * n * (1 + 1 / 32)
+    # SwiGLU: read (a | b) [T, 2n] and probs (and dy [T, n]); write [T, n] (gradient: [T, 2n])
+    bytes_glu = T * 2 * n * 2 + 4 * T + (T + kp_rows) * n * (1 + 1 / 32)
+    bytes_glu_grad = T * 2 * n * 2 + T * n * 2 + 4 * T + (T + kp_rows) * 2 * n * (1 + 1 / 32)
 
     wg_s = leg_ms["wgrad"] / 1e3
     achieved = wgrad_flop / wg_s / 1e12
@@ -401,6 +430,11 @@ def main():
             "act_srelu_grad_quantize": {"ms": round(act_ms["act_srelu_grad_quantize"], 3),
                                         "GB/s": round((bytes_act + 2 * T * n)
                                                       / (act_ms["act_srelu_grad_quantize"] / 1e3) / 1e9, 1)},
+            "act_swiglu_quantize": {"ms": round(act_ms["act_swiglu_quantize"], 3),
+                                    "GB/s": round(bytes_glu / (act_ms["act_swiglu_quantize"] / 1e3) / 1e9, 1)},
+            "act_swiglu_grad_quantize": {"ms": round(act_ms["act_swiglu_grad_quantize"], 3),
+                                         "GB/s": round(bytes_glu_grad
+                                                       / (act_ms["act_swiglu_grad_quantize"] / 1e3) / 1e9, 1)},
             # outside the step: the data-gradient GEMM and its quantize passes
             "quantize_dy_row": {"ms": round(dleg[0], 3),
                                 "GB/s": round(T * n * (2 + 1 + 1 / 32) / (dleg[0] / 1e3) / 1e9, 1)},

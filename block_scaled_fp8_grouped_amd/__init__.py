@@ -25,6 +25,8 @@ ROWWISE = 1
 COLWISE = 2
 ACT_SRELU = 1  # BSFP8_ACT_SRELU: y = p * max(h, 0)^2
 ACT_SRELU_GRAD = 2  # BSFP8_ACT_SRELU_GRAD: g = dy * p * 2 max(h, 0)
+ACT_SWIGLU = 3  # BSFP8_ACT_SWIGLU: y = p * silu(a) * b, h = (a | b)
+ACT_SWIGLU_GRAD = 4  # BSFP8_ACT_SWIGLU_GRAD: (da | db) of the scaled SwiGLU
 OUT_F32 = 0
 OUT_BF16 = 1
 STATUS_NEGATIVE_SPLIT = 1
@@ -176,9 +178,15 @@ def grouped_quantize(x, split_sizes, recipe, which, out, zero_amax_scale=1e-30, 
 def grouped_act_quantize(activation, h, split_sizes, recipe, which, out, probs=None, dy=None, status=None,
                          stream=None):
     """bsfp8_grouped_act_quantize: the scaled squared ReLU (ACT_SRELU) of the bf16 [R, C] tensor
-    h, or its gradient (ACT_SRELU_GRAD, with the bf16 gradient dy), times the float32 per-row
-    probs (None: 1), quantized into ``out`` (see alloc_quantized) with an MX recipe."""
+    h, or its gradient (ACT_SRELU_GRAD, with the bf16 gradient dy [R, C]); or the scaled SwiGLU
+    (ACT_SWIGLU) of h = (a | b) [R, 2F], or its gradient (ACT_SWIGLU_GRAD, dy [R, F]); times the
+    float32 per-row probs (None: 1), quantized into ``out`` with an MX recipe.  ``out`` comes
+    from alloc_quantized for [R, C], [R, F] (ACT_SWIGLU) or [R, 2F] (ACT_SWIGLU_GRAD)."""
     R, C = h.shape
+    if activation in (ACT_SWIGLU, ACT_SWIGLU_GRAD):
+        if C % 2:
+            raise ValueError("grouped_act_quantize: a GLU input has an even number of columns")
+        C //= 2
     E = int(split_sizes.numel())
     rc = lib().bsfp8_grouped_act_quantize(activation, _ptr(h), _ptr(probs), _ptr(dy), R, C, _ptr(split_sizes), E,
                                           recipe, which, _ptr(out.get("row_q")), _ptr(out.get("row_s")),

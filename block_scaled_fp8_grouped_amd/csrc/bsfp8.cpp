@@ -111,7 +111,8 @@ int bsfp8_grouped_act_quantize(int activation, const void* h_bf16, const float* 
                                int64_t capacity_rows, int64_t cols, const int32_t* split_sizes, int32_t num_groups,
                                int recipe, int which, uint8_t* row_q, uint8_t* row_s, uint8_t* col_q, void* col_s,
                                uint32_t* status, void* stream) {
-  if (activation != BSFP8_ACT_SRELU && activation != BSFP8_ACT_SRELU_GRAD) return BSFP8_ERR_ARGUMENT;
+  if (activation < BSFP8_ACT_SRELU || activation > BSFP8_ACT_SWIGLU_GRAD) return BSFP8_ERR_ARGUMENT;
+  const bool grad = activation == BSFP8_ACT_SRELU_GRAD || activation == BSFP8_ACT_SWIGLU_GRAD;
   if (!valid_recipe(recipe)) return BSFP8_ERR_RECIPE;
   if (!mx_recipe(recipe)) return BSFP8_ERR_LAYOUT;
   if (which <= 0 || (which & ~(BSFP8_ROWWISE | BSFP8_COLWISE)) != 0) return BSFP8_ERR_ARGUMENT;
@@ -119,15 +120,14 @@ int bsfp8_grouped_act_quantize(int activation, const void* h_bf16, const float* 
   if (split_sizes == nullptr) return BSFP8_ERR_NULL_POINTER;
   if (!valid_groups(num_groups)) return BSFP8_ERR_NUM_GROUPS;
   if (capacity_rows == 0) return BSFP8_OK;  // nothing to read or write
-  if (h_bf16 == nullptr || (activation == BSFP8_ACT_SRELU_GRAD && dy_bf16 == nullptr)) return BSFP8_ERR_NULL_POINTER;
+  if (h_bf16 == nullptr || (grad && dy_bf16 == nullptr)) return BSFP8_ERR_NULL_POINTER;
   if ((which & BSFP8_ROWWISE) && (row_q == nullptr || row_s == nullptr)) return BSFP8_ERR_NULL_POINTER;
   if ((which & BSFP8_COLWISE) && (col_q == nullptr || col_s == nullptr)) return BSFP8_ERR_NULL_POINTER;
   if (!aligned16(h_bf16) || !aligned16(dy_bf16) || !aligned4(probs) || !aligned4(split_sizes) || !aligned4(status))
     return BSFP8_ERR_ALIGNMENT;
   if ((which & BSFP8_ROWWISE) && (!aligned16(row_q) || !aligned16(row_s))) return BSFP8_ERR_ALIGNMENT;
   if ((which & BSFP8_COLWISE) && (!aligned16(col_q) || !aligned16(col_s))) return BSFP8_ERR_ALIGNMENT;
-  return bsfp8::launch_grouped_act_quantize(activation, h_bf16, probs,
-                                            activation == BSFP8_ACT_SRELU_GRAD ? dy_bf16 : nullptr, capacity_rows,
+  return bsfp8::launch_grouped_act_quantize(activation, h_bf16, probs, grad ? dy_bf16 : nullptr, capacity_rows,
                                             cols, split_sizes, num_groups, recipe, which,
                                             (which & BSFP8_ROWWISE) ? row_q : nullptr,
                                             (which & BSFP8_ROWWISE) ? row_s : nullptr,

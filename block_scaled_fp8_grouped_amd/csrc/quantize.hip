@@ -17,6 +17,8 @@
 // Rows past the group's live rows are never read: they enter LDS as zeros, which leaves every
 // block amax unchanged and makes the packed pad lanes 0x00.  Tiles are placed by the
 // in-kernel scan of the split sizes (the grid is an upper bound; spare workgroups exit).
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace bsfp8 {
@@ -35,24 +37,68 @@ struct QTile {
 };
 
 // Inputs of the activation fused in front of the quantizer (ACT != 0): the routing probability of
-// each token row (NULL: 1) and, for the gradient, the incoming bf16 gradient.
+// each token row (NULL: 1), for the gradients the incoming bf16 gradient, and for the GLU
+// activations their width F (fc1's output row holds a = [0, F) and b = [F, 2F)).
 struct ActArgs {
   const float* probs;
   const uint16_t* dy;
+  int64_t glu_f;
 };
 
-// The scaled squared ReLU between fc1 and fc2 (TE #3484 reproducer, fc1 -> ScaledSReLU -> fc2),
-// in fp32 with each product rounded in this order; r is +0 for h <= 0 (also for h = -0):
-//   ACT 1: y = (r * r) * p          ACT 2 (its gradient): g = ((2 * r) * p) * dy
+// 2^x in fp32 by a stated algorithm every IEEE fp32 machine reproduces bit for bit: x clamped to
+// [-126, 126]; k = floor(x + 1/2), r = x - k (exact); the degree-7 Taylor polynomial of
+// exp(r ln 2) (coefficients (ln 2)^n / n! in fp32, Horner order, no fused multiply-add) times 2^k.
+__device__ __forceinline__ float exp2_stated(float x) {
+  x = x > 126.0f ? 126.0f : (x < -126.0f ? -126.0f : x);
+  const int k = (int)floorf(x + 0.5f);
+  const float r = x - (float)k;
+  float poly = 1.52527338e-05f;
+  poly = poly * r + 0.000154035304f;
+  poly = poly * r + 0.00133335581f;
+  poly = poly * r + 0.00961812911f;
+  poly = poly * r + 0.0555041087f;
+  poly = poly * r + 0.240226507f;
+  poly = poly * r + 0.693147182f;
+  poly = poly * r + 1.0f;
+  return ldexpf(poly, k);
+}
+
+// The activations between fc1 and fc2 (TE #3484: fc1 -> ScaledSReLU / ScaledSwiGLU -> fc2 with
+// per-token probs), in fp32, each operation rounded in the order written:
+//   ACT 1: r = max(h, 0) (+0 for h <= 0);  y = (r * r) * p
+//   ACT 2: its gradient                     g = ((2 * r) * p) * dy
+//   ACT 3: sg = 1 / (1 + 2^(-a log2 e)), s = a * sg;  y = (s * b) * p
+//   ACT 4: its gradient, q = dy * p:  da = (q * b) * (sg * (1 + a * (1 - sg)))  (second = false)
+//                                     db = q * s                                 (second = true)
 template <int ACT>
-__device__ __forceinline__ float act_value(float h, float p, float d) {
-  const float r = h > 0.0f ? h : 0.0f;
-  if constexpr (ACT == 1) {
-    const float r2 = r * r;
-    return r2 * p;
+__device__ __forceinline__ float act_value(float h, float b, float p, float d, bool second) {
+  if constexpr (ACT <= 2) {
+    const float r = h > 0.0f ? h : 0.0f;
+    if constexpr (ACT == 1) {
+      const float r2 = r * r;
+      return r2 * p;
+    } else {
+      const float tp = (2.0f * r) * p;
+      return tp * d;
+    }
   } else {
-    const float tp = (2.0f * r) * p;
-    return tp * d;
+    const float t = exp2_stated(-h * 1.44269502f);
+    const float den = 1.0f + t;
+    const float sg = 1.0f / den;
+    const float sl = h * sg;
+    if constexpr (ACT == 3) {
+      const float sb = sl * b;
+      return sb * p;
+    } else {
+      const float q = d * p;
+      if (second) return q * sl;
+      const float u = 1.0f - sg;
+      const float v = h * u;
+      const float w = 1.0f + v;
+      const float ds = sg * w;
+      const float qb = q * b;
+      return qb * ds;
+    }
   }
 }
 
@@ -70,7 +116,9 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t tile[kQRows][kQCols / 2];  // bf16 pairs
   __shared__ float pc_amax[4][kQCols];
   __shared__ uint8_t rs_tile[kQCols / 32][kQRows];
-  __shared__ __attribute__((aligned(16))) uint32_t tile_dy[ACT == 2 ? kQRows : 1][kQCols / 2];  // gradient
+  // second input: the gradient (ACT 2) or the GLU's b half (ACT 3, 4); third: the GLU gradient
+  __shared__ __attribute__((aligned(16))) uint32_t tile_dy[ACT >= 2 ? kQRows : 1][kQCols / 2];
+  __shared__ __attribute__((aligned(16))) uint32_t tile3[ACT == 4 ? kQRows : 1][kQCols / 2];
   __shared__ float prow[ACT != 0 ? kQRows : 1];  // the tile rows' probabilities (0 past the live rows)
 
   const int tid = threadIdx.x;
@@ -116,7 +164,8 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
 
   // this thread's share of a tile: 16 lanes per row, 8 channels (16 bytes) each
   v4i pre[kQRows / 16];
-  v4i pre_dy[ACT == 2 ? kQRows / 16 : 1];
+  v4i pre_dy[ACT >= 2 ? kQRows / 16 : 1];
+  v4i pre3[ACT == 4 ? kQRows / 16 : 1];
   float pre_p = 0.0f;
   auto load_tile = [&](const QTile& q) {
 #pragma unroll
@@ -124,10 +173,22 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
       const int r = pass * 16 + (tid >> 4);
       const int ch = tid & 15;
       pre[pass] = v4i{0, 0, 0, 0};
-      if (r < q.nlive && ch * 8 < ncols) pre[pass] = *(const v4i*)(in + (q.row0 + r) * C + c0 + ch * 8);
-      if constexpr (ACT == 2) {
-        pre_dy[pass] = v4i{0, 0, 0, 0};
-        if (r < q.nlive && ch * 8 < ncols) pre_dy[pass] = *(const v4i*)(act.dy + (q.row0 + r) * C + c0 + ch * 8);
+      if constexpr (ACT >= 2) pre_dy[pass] = v4i{0, 0, 0, 0};
+      if constexpr (ACT == 4) pre3[pass] = v4i{0, 0, 0, 0};
+      if (r < q.nlive && ch * 8 < ncols) {
+        if constexpr (ACT <= 2) {
+          pre[pass] = *(const v4i*)(in + (q.row0 + r) * C + c0 + ch * 8);
+          if constexpr (ACT == 2) pre_dy[pass] = *(const v4i*)(act.dy + (q.row0 + r) * C + c0 + ch * 8);
+        } else {
+          // output column cc takes a and b at column j of the halves (j = cc - F in the gradient's
+          // db half); 8 columns never straddle F (a multiple of 32)
+          const int64_t F = act.glu_f, cc = c0 + ch * 8;
+          const int64_t j = (ACT == 4 && cc >= F) ? cc - F : cc;
+          const uint16_t* hr = in + (q.row0 + r) * 2 * F;
+          pre[pass] = *(const v4i*)(hr + j);
+          pre_dy[pass] = *(const v4i*)(hr + F + j);
+          if constexpr (ACT == 4) pre3[pass] = *(const v4i*)(act.dy + (q.row0 + r) * F + j);
+        }
       }
     }
     if constexpr (ACT != 0) {
@@ -143,7 +204,8 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
 #pragma unroll
     for (int pass = 0; pass < kQRows / 16; ++pass) {
       *(v4i*)&tile[pass * 16 + (tid >> 4)][(tid & 15) * 4] = pre[pass];
-      if constexpr (ACT == 2) *(v4i*)&tile_dy[pass * 16 + (tid >> 4)][(tid & 15) * 4] = pre_dy[pass];
+      if constexpr (ACT >= 2) *(v4i*)&tile_dy[pass * 16 + (tid >> 4)][(tid & 15) * 4] = pre_dy[pass];
+      if constexpr (ACT == 4) *(v4i*)&tile3[pass * 16 + (tid >> 4)][(tid & 15) * 4] = pre3[pass];
     }
     if constexpr (ACT != 0) {
       if (tid < kQRows) prow[tid] = pre_p;
@@ -165,10 +227,14 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int r = wave * 32 + i;
-        const uint32_t hw = tile[r][lane], dw = ACT == 2 ? tile_dy[r][lane] : 0u;
+        // h (or a), and the second input: dy (ACT 2) or b (ACT 3, 4); the GLU gradient's dy
+        const uint32_t hw = tile[r][lane], w2 = ACT >= 2 ? tile_dy[r][lane] : 0u;
+        const uint32_t w3 = ACT == 4 ? tile3[r][lane] : 0u;
+        const uint32_t bw = ACT >= 3 ? w2 : 0u, dw = ACT == 2 ? w2 : w3;
+        const bool second = ACT == 4 && c0 + c >= act.glu_f;
         const float p = prow[r];
-        y0[i] = act_value<ACT>(bf16_lo(hw), p, bf16_lo(dw));
-        y1[i] = act_value<ACT>(bf16_hi(hw), p, bf16_hi(dw));
+        y0[i] = act_value<ACT>(bf16_lo(hw), bf16_lo(bw), p, bf16_lo(dw), second);
+        y1[i] = act_value<ACT>(bf16_hi(hw), bf16_hi(bw), p, bf16_hi(dw), second);
         m0 = max(m0, __float_as_uint(y0[i]) & 0x7fffffffu);
         m1 = max(m1, __float_as_uint(y1[i]) & 0x7fffffffu);
       }
@@ -300,12 +366,17 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
         uint32_t m = 0;
         float yv[8];  // the values this lane quantizes (bf16 inputs, or the activation's fp32 values)
         if constexpr (ACT != 0) {
-          const v4i vd = ACT == 2 ? *(const v4i*)&tile_dy[r][ch * 4] : v4i{0, 0, 0, 0};
+          const v4i v2 = ACT >= 2 ? *(const v4i*)&tile_dy[r][ch * 4] : v4i{0, 0, 0, 0};
+          const v4i v3 = ACT == 4 ? *(const v4i*)&tile3[r][ch * 4] : v4i{0, 0, 0, 0};
+          const v4i vb = ACT >= 3 ? v2 : v4i{0, 0, 0, 0}, vd = ACT == 2 ? v2 : v3;
+          const bool second = ACT == 4 && c0 + ch * 8 >= act.glu_f;
           const float p = prow[r];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            yv[2 * i] = act_value<ACT>(bf16_lo((uint32_t)v[i]), p, bf16_lo((uint32_t)vd[i]));
-            yv[2 * i + 1] = act_value<ACT>(bf16_hi((uint32_t)v[i]), p, bf16_hi((uint32_t)vd[i]));
+            yv[2 * i] = act_value<ACT>(bf16_lo((uint32_t)v[i]), bf16_lo((uint32_t)vb[i]), p, bf16_lo((uint32_t)vd[i]),
+                                       second);
+            yv[2 * i + 1] = act_value<ACT>(bf16_hi((uint32_t)v[i]), bf16_hi((uint32_t)vb[i]), p,
+                                           bf16_hi((uint32_t)vd[i]), second);
             m = max(m, max(__float_as_uint(yv[2 * i]) & 0x7fffffffu, __float_as_uint(yv[2 * i + 1]) & 0x7fffffffu));
           }
         } else {
@@ -368,26 +439,26 @@ int launch_grouped_quantize(const void* in, int64_t R, int64_t C, const int32_t*
   if (recipe == BSFP8_RECIPE_MX_1X32_E8M0) {
     if (row && col)
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MX_1X32_E8M0, true, true>), grid, block, 0, stream, x,
-                         R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{});
+                         R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{nullptr, nullptr, 0});
     else if (row)
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MX_1X32_E8M0, true, false>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{});
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{nullptr, nullptr, 0});
     else
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MX_1X32_E8M0, false, true>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{});
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{nullptr, nullptr, 0});
   } else if (recipe == BSFP8_RECIPE_MXFP4_1X32_E8M0) {
     if (row && col)
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MXFP4_1X32_E8M0, true, true>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{});
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{nullptr, nullptr, 0});
     else if (row)
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MXFP4_1X32_E8M0, true, false>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{});
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{nullptr, nullptr, 0});
     else
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MXFP4_1X32_E8M0, false, true>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{});
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{nullptr, nullptr, 0});
   } else {
     hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_PER_CHANNEL_128_F32, false, true>), grid, block, 0,
-                       stream, x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{});
+                       stream, x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{nullptr, nullptr, 0});
   }
   return hipGetLastError() == hipSuccess ? BSFP8_OK : BSFP8_ERR_LAUNCH;
 }
@@ -407,9 +478,11 @@ static void launch_act(dim3 grid, dim3 block, hipStream_t stream, bool row, bool
                        0.0f, row_q, row_s, col_q, col_s, nullptr, status, a);
 }
 
-int launch_grouped_act_quantize(int act, const void* h, const float* probs, const void* dy, int64_t R, int64_t C,
+int launch_grouped_act_quantize(int act, const void* h, const float* probs, const void* dy, int64_t R, int64_t cols,
                                 const int32_t* splits, int E, int recipe, int which, uint8_t* row_q, uint8_t* row_s,
                                 uint8_t* col_q, void* col_s, uint32_t* status, hipStream_t stream) {
+  // output columns: cols, or 2 cols for the GLU gradient (da | db)
+  const int64_t C = act == BSFP8_ACT_SWIGLU_GRAD ? 2 * cols : cols;
   const int64_t gx = (quantize_row_tiles(R, E, true) + kQTilesPerWG - 1) / kQTilesPerWG;
   const int64_t gy = (C + kQCols - 1) / kQCols;
   if (gx <= 0 || gy <= 0) return BSFP8_OK;
@@ -417,22 +490,27 @@ int launch_grouped_act_quantize(int act, const void* h, const float* probs, cons
   dim3 grid((unsigned)(gx * gy)), block(kQThreads);
   const uint16_t* x = (const uint16_t*)h;
   const bool row = (which & BSFP8_ROWWISE) != 0, col = (which & BSFP8_COLWISE) != 0;
-  const ActArgs a{probs, (const uint16_t*)dy};
-  if (recipe == BSFP8_RECIPE_MX_1X32_E8M0) {
-    if (act == BSFP8_ACT_SRELU)
-      launch_act<BSFP8_RECIPE_MX_1X32_E8M0, 1>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q,
-                                               col_s, status, a);
-    else
-      launch_act<BSFP8_RECIPE_MX_1X32_E8M0, 2>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q,
-                                               col_s, status, a);
-  } else {
-    if (act == BSFP8_ACT_SRELU)
-      launch_act<BSFP8_RECIPE_MXFP4_1X32_E8M0, 1>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s,
-                                                  col_q, col_s, status, a);
-    else
-      launch_act<BSFP8_RECIPE_MXFP4_1X32_E8M0, 2>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s,
-                                                  col_q, col_s, status, a);
-  }
+  const ActArgs a{probs, (const uint16_t*)dy, cols};
+  auto go = [&](auto recipe_tag) {
+    constexpr int RC = decltype(recipe_tag)::value;
+    switch (act) {
+      case BSFP8_ACT_SRELU:
+        launch_act<RC, 1>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q, col_s, status, a);
+        break;
+      case BSFP8_ACT_SRELU_GRAD:
+        launch_act<RC, 2>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q, col_s, status, a);
+        break;
+      case BSFP8_ACT_SWIGLU:
+        launch_act<RC, 3>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q, col_s, status, a);
+        break;
+      default:
+        launch_act<RC, 4>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q, col_s, status, a);
+    }
+  };
+  if (recipe == BSFP8_RECIPE_MX_1X32_E8M0)
+    go(std::integral_constant<int, BSFP8_RECIPE_MX_1X32_E8M0>());
+  else
+    go(std::integral_constant<int, BSFP8_RECIPE_MXFP4_1X32_E8M0>());
   return hipGetLastError() == hipSuccess ? BSFP8_OK : BSFP8_ERR_LAUNCH;
 }
 

@@ -54,6 +54,8 @@ extern "C" {
 /* Activations of bsfp8_grouped_act_quantize. */
 #define BSFP8_ACT_SRELU 1      /* y = p * max(h, 0)^2 (scaled squared ReLU) */
 #define BSFP8_ACT_SRELU_GRAD 2 /* g = dy * p * 2 max(h, 0) (its gradient with respect to h) */
+#define BSFP8_ACT_SWIGLU 3     /* y = p * silu(a) * b, (a | b) the halves of fc1's output row */
+#define BSFP8_ACT_SWIGLU_GRAD 4 /* (da | db): the gradient of the scaled SwiGLU */
 
 /* Output element types of bsfp8_grouped_gemm_fprop. */
 #define BSFP8_OUT_F32 0
@@ -145,18 +147,30 @@ int bsfp8_grouped_quantize(const void* in_bf16, int64_t capacity_rows, int64_t c
 
 /* ----------------------------------------------------------------------------------------- */
 /* Activation fused with the grouped quantize (TE #3484 reproducer: fc1 -> ScaledSReLU -> fc2   */
-/* with per-token probs; the activation's formula is the usual scaled squared ReLU).          */
+/* with per-token probs; its additional context names the ScaledSwiGLU family beside it; the  */
+/* formulas are the usual scaled squared ReLU and scaled SwiGLU).                             */
 /* ----------------------------------------------------------------------------------------- */
 /*
- * h_bf16      [capacity_rows][cols] bf16: fc1's output (forward) or fc1's output saved for the
- *             backward (BSFP8_ACT_SRELU_GRAD).
- * probs       device fp32 [capacity_rows]: the token's routing probability p, or NULL for p = 1.
- * dy_bf16     [capacity_rows][cols] bf16, the gradient arriving at the activation's output
- *             (BSFP8_ACT_SRELU_GRAD only; NULL otherwise).
- * activation  BSFP8_ACT_SRELU:      y = (r * r) * p
- *             BSFP8_ACT_SRELU_GRAD: g = ((2 * r) * p) * dy
- *             with r = h for h > 0 and +0 otherwise, every product rounded to fp32 in this order
- *             (no fused multiply-add).  The fp32 values of the live rows are quantized as
+ * SReLU (activation 1, 2): cols is the row length of h and of the output.
+ *   h_bf16   [capacity_rows][cols] bf16: fc1's output (forward) or fc1's output saved for the
+ *            backward (BSFP8_ACT_SRELU_GRAD).
+ *   dy_bf16  [capacity_rows][cols] bf16, the gradient arriving at the activation's output
+ *            (BSFP8_ACT_SRELU_GRAD only; NULL otherwise).
+ *   BSFP8_ACT_SRELU:      y = (r * r) * p
+ *   BSFP8_ACT_SRELU_GRAD: g = ((2 * r) * p) * dy
+ *   with r = h for h > 0 and +0 otherwise.
+ * SwiGLU (activation 3, 4): cols is the GLU width F; h_bf16 is [capacity_rows][2F] with
+ *   a = columns [0, F) and b = [F, 2F) of each row; dy_bf16 [capacity_rows][F] (gradient only).
+ *   With t = exp2s(-a * log2(e)), sg = 1 / (1 + t), s = a * sg:
+ *   BSFP8_ACT_SWIGLU:      y = (s * b) * p, quantized as [capacity_rows][F]
+ *   BSFP8_ACT_SWIGLU_GRAD: q = dy * p; da = (q * b) * (sg * (1 + a * (1 - sg))); db = q * s,
+ *                          quantized as [capacity_rows][2F] = (da | db)
+ *   exp2s is a stated fp32 2^x: x clamped to [-126, 126], k = floor(x + 1/2), r = x - k, the
+ *   degree-7 Taylor polynomial of exp(r ln 2) with fp32 coefficients (ln 2)^n / n! in Horner
+ *   form, times 2^k (relative error below 3e-7; reproducible bit for bit on any IEEE machine).
+ * probs      device fp32 [capacity_rows]: the token's routing probability p, or NULL for p = 1.
+ * Every operation is rounded to fp32 in the order written (no fused multiply-add); division is
+ * correctly rounded.  The fp32 values of the live rows are quantized as
  *             bsfp8_grouped_quantize quantizes a bf16 input, for recipe
  *             BSFP8_RECIPE_MX_1X32_E8M0 or BSFP8_RECIPE_MXFP4_1X32_E8M0, into the same layouts
  *             (rowwise for the next GEMM's forward, colwise for its weight gradient).

@@ -172,13 +172,15 @@ def _a(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(act=0), -7), (dict(act=3), -7), (dict(recipe=PC), -6), (dict(recipe=9), -3),
+    (dict(act=0), -7), (dict(act=5), -7), (dict(recipe=PC), -6), (dict(recipe=9), -3),
     (dict(which=0), -7), (dict(which=8), -7), (dict(C=48), -4), (dict(R=-1), -4),
     (dict(splits=None), -1), (dict(E=0), -2), (dict(E=1025), -2),
     (dict(h=None), -1), (dict(act=bs.ACT_SRELU_GRAD), -1), (dict(col_s=None), -1),
     (dict(which=bs.ROWWISE, row_q=None), -1),
     (dict(h=P + 8), -5), (dict(act=bs.ACT_SRELU_GRAD, dy=P + 2), -5), (dict(probs=P + 2), -5),
     (dict(col_q=P + 4), -5), (dict(status=P + 1), -5),
+    (dict(act=bs.ACT_SWIGLU, C=48), -4), (dict(act=bs.ACT_SWIGLU, recipe=PC), -6),
+    (dict(act=bs.ACT_SWIGLU_GRAD), -1), (dict(act=bs.ACT_SWIGLU_GRAD, dy=P + 2), -5),
 ])
 def test_act_quantize_rejects_before_launch(kw, code):
     assert _a(**kw) == code
@@ -187,6 +189,7 @@ def test_act_quantize_rejects_before_launch(kw, code):
 def test_act_quantize_zero_rows_and_optional_probs():
     assert _a(R=0, h=None, probs=None, col_q=None, col_s=None) == 0
     assert _a(R=0, act=bs.ACT_SRELU_GRAD, h=None, dy=None, col_q=None, col_s=None) == 0
+    assert _a(R=0, act=bs.ACT_SWIGLU_GRAD, h=None, dy=None, col_q=None, col_s=None) == 0
 
 
 def test_strerror_covers_codes():

@@ -1,11 +1,13 @@
 """The activation fused with the grouped quantize (the ScaledSReLU step between fc1 and fc2 in the
-TransformerEngine #3484 reproducer, and its gradient) on the GPU vs the CPU oracle: quantized
-bytes and scales bit-exact (both sides compute the activation in fp32 with the same rounding
-order, then take every quantization decision on the same fp32 value).
+TransformerEngine #3484 reproducer, the ScaledSwiGLU of the same family, and their gradients) on
+the GPU vs the CPU oracle: quantized bytes and scales bit-exact (both sides compute the
+activation in fp32 with the same rounding order and the same stated exp2, then take every
+quantization decision on the same fp32 value).
 
 Ragged groups, both layouts, MXFP8 and MXFP4, with and without probs (negative ones too),
 garbage padding (NaN/Inf in h, dy and probs past the live rows), signed zeros, the device status
-word, and the 32-expert MoE shape at full size.
+word, GLU widths that are and are not multiples of the 128-column tile (the gradient's da | db
+boundary inside a tile), and the 32-expert MoE shape at full size.
 """
 import numpy as np
 import pytest
@@ -36,19 +38,33 @@ def _inputs(R, C, splits, seed, negative_probs=False):
     return h, dy, p
 
 
+GRADS = (bs.ACT_SRELU_GRAD, bs.ACT_SWIGLU_GRAD)
+
+
+def _out_cols(act, h):
+    """Columns of the quantized output: h's, F = half of them (SwiGLU) or 2F = all (its gradient)."""
+    return h.shape[1] // 2 if act == bs.ACT_SWIGLU else h.shape[1]
+
+
 def _check(act, h, dy, p, splits, recipe, which, label):
-    R, C = h.shape
+    R = h.shape[0]
     st = W.splits_tensor(splits, DEV)
-    out = poisoned_quant_outputs(R, C, len(splits), recipe, which)
+    out = poisoned_quant_outputs(R, _out_cols(act, h), len(splits), recipe, which)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
-    bs.grouped_act_quantize(act, h, st, recipe, which, out, probs=p, dy=dy if act == bs.ACT_SRELU_GRAD else None,
+    bs.grouped_act_quantize(act, h, st, recipe, which, out, probs=p, dy=dy if act in GRADS else None,
                             status=status)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     ref = oracle.grouped_act_quantize(act, W.bf16_bits(h), None if p is None else p.cpu().numpy(),
-                                      W.bf16_bits(dy) if act == bs.ACT_SRELU_GRAD else None, splits,
-                                      recipe, which)
+                                      W.bf16_bits(dy) if act in GRADS else None, splits, recipe, which)
     assert_quant_matches(out, ref, splits, R, which, label)
+
+
+def _glu_inputs(R, F, splits, seed, negative_probs=False):
+    """h = (a | b) [R, 2F] and dy [R, F] with the garbage padding of _inputs."""
+    h, _, p = _inputs(R, 2 * F, splits, seed, negative_probs)
+    _, dy, _ = _inputs(R, F, splits, seed + 1)
+    return h, dy, p
 
 
 @pytest.mark.parametrize("act", [bs.ACT_SRELU, bs.ACT_SRELU_GRAD])
@@ -114,3 +130,43 @@ def test_act_quantize_moe32_shape():
     p = torch.rand(R, generator=g, device=DEV)
     _check(bs.ACT_SRELU, h, None, p, splits, bs.RECIPE_MX, bs.ROWWISE | bs.COLWISE, "moe32")
     assert T < R
+
+
+@pytest.mark.parametrize("act", [bs.ACT_SWIGLU, bs.ACT_SWIGLU_GRAD])
+@pytest.mark.parametrize("recipe", [bs.RECIPE_MX, bs.RECIPE_MX4])
+@pytest.mark.parametrize("splits", RAGGED)
+@pytest.mark.parametrize("F", [32, 96, 256])
+def test_swiglu_quantize_parity(act, recipe, splits, F):
+    """F = 96: the gradient's 192 output columns put the da | db boundary inside the first tile."""
+    flush(f"swiglu act={act} recipe={recipe} F={F} splits={splits}")
+    T = sum(splits)
+    h, dy, p = _glu_inputs(T + 29, F, splits, seed=F + T + act, negative_probs=(F == 96))
+    _check(act, h, dy, p, splits, recipe, bs.ROWWISE | bs.COLWISE, f"act{act} r{recipe} F={F}")
+
+
+@pytest.mark.parametrize("which", [bs.ROWWISE, bs.COLWISE])
+@pytest.mark.parametrize("act", [bs.ACT_SWIGLU, bs.ACT_SWIGLU_GRAD])
+def test_swiglu_single_layout_no_probs_and_large_inputs(which, act):
+    """Inputs up to |a| = 96 (2^(-a log2 e) at the clamp of the stated exp2 on both sides), signed
+    zeros, no probs."""
+    flush(f"swiglu act={act} which={which} wide range")
+    splits = [130, 0, 257, 31]
+    h, dy, _ = _glu_inputs(sum(splits) + 20, 160, splits, seed=8)
+    h[:, :32] = h[:, :32] * 48.0
+    h[:8, 32:40] = -0.0
+    h[8:16, 32:40] = 0.0
+    _check(act, h, dy, None, splits, bs.RECIPE_MX, which, f"swiglu act{act} which{which}")
+
+
+def test_swiglu_moe32_shape():
+    """fc1's GLU output of the 32-expert layer (65,536 routed rows, ffn 1536 so h is [R, 3072]),
+    Zipf routing with empty experts, garbage padding: the gradient, both MXFP8 layouts, all
+    bytes."""
+    flush("swiglu moe32")
+    case = W.moe32_zipf(DEV, with_weight=False)
+    splits, R = case["splits"], case["R"]
+    g = torch.Generator(device=DEV).manual_seed(41)
+    dy = case["dy"]
+    h = torch.cat([dy, W.randn_bf16(dy.shape, g, DEV, scale=2.0)], dim=1)
+    p = torch.rand(R, generator=g, device=DEV)
+    _check(bs.ACT_SWIGLU_GRAD, h, dy, p, splits, bs.RECIPE_MX, bs.ROWWISE | bs.COLWISE, "swiglu moe32")
