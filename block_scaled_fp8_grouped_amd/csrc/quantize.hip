@@ -17,6 +17,12 @@
 // Rows past the group's live rows are never read: they enter LDS as zeros, which leaves every
 // block amax unchanged and makes the packed pad lanes 0x00.  Tiles are placed by the
 // in-kernel scan of the split sizes (the grid is an upper bound; spare workgroups exit).
+//
+// With an activation fused in front (fc1's output -> activation -> quantize), each thread
+// evaluates the activation once per element from the registers its loads landed in and stages
+// the fp32 values in LDS (64 KB: two workgroups per CU); both layouts quantize those values.
+// The GLU gradient's tile pairs 64 da columns with the 64 db columns of the same inputs, so one
+// sigmoid serves both outputs.
 #include <type_traits>
 
 #include "common.hpp"
@@ -68,10 +74,8 @@ __device__ __forceinline__ float exp2_stated(float x) {
 //   ACT 1: r = max(h, 0) (+0 for h <= 0);  y = (r * r) * p
 //   ACT 2: its gradient                     g = ((2 * r) * p) * dy
 //   ACT 3: sg = 1 / (1 + 2^(-a log2 e)), s = a * sg;  y = (s * b) * p
-//   ACT 4: its gradient, q = dy * p:  da = (q * b) * (sg * (1 + a * (1 - sg)))  (second = false)
-//                                     db = q * s                                 (second = true)
 template <int ACT>
-__device__ __forceinline__ float act_value(float h, float b, float p, float d, bool second) {
+__device__ __forceinline__ float act_value(float h, float b, float p, float d) {
   if constexpr (ACT <= 2) {
     const float r = h > 0.0f ? h : 0.0f;
     if constexpr (ACT == 1) {
@@ -86,20 +90,26 @@ __device__ __forceinline__ float act_value(float h, float b, float p, float d, b
     const float den = 1.0f + t;
     const float sg = 1.0f / den;
     const float sl = h * sg;
-    if constexpr (ACT == 3) {
-      const float sb = sl * b;
-      return sb * p;
-    } else {
-      const float q = d * p;
-      if (second) return q * sl;
-      const float u = 1.0f - sg;
-      const float v = h * u;
-      const float w = 1.0f + v;
-      const float ds = sg * w;
-      const float qb = q * b;
-      return qb * ds;
-    }
+    const float sb = sl * b;
+    return sb * p;
   }
+}
+
+//   ACT 4: the gradient of ACT 3, q = dy * p:  da = (q * b) * (sg * (1 + a * (1 - sg))),  db = q * s
+// (sg and s shared by the two outputs of one element)
+__device__ __forceinline__ void glu_grad(float a, float b, float p, float d, float& da, float& db) {
+  const float t = exp2_stated(-a * 1.44269502f);
+  const float den = 1.0f + t;
+  const float sg = 1.0f / den;
+  const float sl = a * sg;
+  const float q = d * p;
+  db = q * sl;
+  const float u = 1.0f - sg;
+  const float v = a * u;
+  const float w = 1.0f + v;
+  const float ds = sg * w;
+  const float qb = q * b;
+  da = qb * ds;
 }
 
 template <int RECIPE, bool ROW, bool COL, int ACT = 0>
@@ -113,13 +123,11 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
   // they hold, which lets a captured graph skip re-quantizing a cached weight
   if (noop_flag != nullptr && *noop_flag != 0.0f) return;
   __shared__ GroupScanSmem<kQThreads> gsm;
-  __shared__ __attribute__((aligned(16))) uint32_t tile[kQRows][kQCols / 2];  // bf16 pairs
+  // the tile: bf16 pairs, or with an activation its fp32 values (evaluated once per element)
+  __shared__ __attribute__((aligned(16))) uint32_t tile[ACT == 0 ? kQRows : 1][kQCols / 2];
+  __shared__ __attribute__((aligned(16))) float ytile[ACT != 0 ? kQRows : 1][ACT != 0 ? kQCols : 1];
   __shared__ float pc_amax[4][kQCols];
   __shared__ uint8_t rs_tile[kQCols / 32][kQRows];
-  // second input: the gradient (ACT 2) or the GLU's b half (ACT 3, 4); third: the GLU gradient
-  __shared__ __attribute__((aligned(16))) uint32_t tile_dy[ACT >= 2 ? kQRows : 1][kQCols / 2];
-  __shared__ __attribute__((aligned(16))) uint32_t tile3[ACT == 4 ? kQRows : 1][kQCols / 2];
-  __shared__ float prow[ACT != 0 ? kQRows : 1];  // the tile rows' probabilities (0 past the live rows)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -129,6 +137,20 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
   const int64_t rt0 = (int64_t)blockIdx.x / ctiles * kQTilesPerWG, ctile = (int64_t)blockIdx.x % ctiles;
   const int64_t c0 = ctile * kQCols;
   const int ncols = (int)((C - c0) < kQCols ? (C - c0) : kQCols);  // a multiple of 32
+  // The GLU gradient pairs its outputs: tile columns [0, 64) are da at input columns
+  // [c0h, c0h + gw) and [64, 128) db at the same input columns, so one evaluation of the sigmoid
+  // serves both (C = 2F; gw, a multiple of 32, is the tile's live width of each half).
+  constexpr int kHalf = kQCols / 2;
+  const int64_t c0h = ctile * kHalf;
+  const int gw = ACT == 4 ? (int)((act.glu_f - c0h) < kHalf ? (act.glu_f - c0h) : kHalf) : 0;
+  auto out_col = [&](int lc) -> int64_t {  // output column of tile column lc
+    if constexpr (ACT == 4) return (lc < kHalf ? c0h : act.glu_f + c0h - kHalf) + lc;
+    return c0 + lc;
+  };
+  auto live_col = [&](int lc) -> bool {  // lc a multiple of 2 (colwise) or 8 (rowwise)
+    if constexpr (ACT == 4) return (lc & (kHalf - 1)) < gw;
+    return lc < ncols;
+  };
 
   // group of the run's first tile from the scan of the split sizes; later tiles walk forward
   GroupInfo g{};
@@ -162,38 +184,68 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
     return true;
   };
 
-  // this thread's share of a tile: 16 lanes per row, 8 channels (16 bytes) each
-  v4i pre[kQRows / 16];
-  v4i pre_dy[ACT >= 2 ? kQRows / 16 : 1];
-  v4i pre3[ACT == 4 ? kQRows / 16 : 1];
-  float pre_p = 0.0f;
+  // this thread's share of a tile: 16 lanes per row, 8 channels (16 bytes) each (the GLU
+  // gradient: 8 lanes per row, 8 input columns of a, b and dy each)
+  constexpr int kLanesPerRow = ACT == 4 ? 8 : 16;
+  constexpr int kPasses = kQRows * kLanesPerRow / kQThreads;
+  v4i pre[kPasses];
+  v4i pre2[ACT >= 2 ? kPasses : 1];  // dy (ACT 2) or b (ACT 3, 4)
+  v4i pre3[ACT == 4 ? kPasses : 1];  // dy of the GLU gradient
+  float pre_p[ACT != 0 ? kPasses : 1];
   auto load_tile = [&](const QTile& q) {
 #pragma unroll
-    for (int pass = 0; pass < kQRows / 16; ++pass) {
-      const int r = pass * 16 + (tid >> 4);
-      const int ch = tid & 15;
+    for (int pass = 0; pass < kPasses; ++pass) {
+      const int r = pass * (kQThreads / kLanesPerRow) + tid / kLanesPerRow;
+      const int ch = tid % kLanesPerRow;
       pre[pass] = v4i{0, 0, 0, 0};
-      if constexpr (ACT >= 2) pre_dy[pass] = v4i{0, 0, 0, 0};
+      if constexpr (ACT >= 2) pre2[pass] = v4i{0, 0, 0, 0};
       if constexpr (ACT == 4) pre3[pass] = v4i{0, 0, 0, 0};
-      if (r < q.nlive && ch * 8 < ncols) {
+      if constexpr (ACT != 0) pre_p[pass] = 0.0f;
+      if (r < q.nlive && live_col(ch * 8)) {
         if constexpr (ACT <= 2) {
           pre[pass] = *(const v4i*)(in + (q.row0 + r) * C + c0 + ch * 8);
-          if constexpr (ACT == 2) pre_dy[pass] = *(const v4i*)(act.dy + (q.row0 + r) * C + c0 + ch * 8);
+          if constexpr (ACT == 2) pre2[pass] = *(const v4i*)(act.dy + (q.row0 + r) * C + c0 + ch * 8);
         } else {
-          // output column cc takes a and b at column j of the halves (j = cc - F in the gradient's
-          // db half); 8 columns never straddle F (a multiple of 32)
-          const int64_t F = act.glu_f, cc = c0 + ch * 8;
-          const int64_t j = (ACT == 4 && cc >= F) ? cc - F : cc;
+          // a and b at input column j of the two halves of the [2F] row
+          const int64_t F = act.glu_f, j = (ACT == 4 ? c0h : c0) + ch * 8;
           const uint16_t* hr = in + (q.row0 + r) * 2 * F;
           pre[pass] = *(const v4i*)(hr + j);
-          pre_dy[pass] = *(const v4i*)(hr + F + j);
+          pre2[pass] = *(const v4i*)(hr + F + j);
           if constexpr (ACT == 4) pre3[pass] = *(const v4i*)(act.dy + (q.row0 + r) * F + j);
         }
+        if constexpr (ACT != 0) pre_p[pass] = act.probs != nullptr ? act.probs[q.row0 + r] : 1.0f;
       }
     }
-    if constexpr (ACT != 0) {
-      pre_p = 0.0f;
-      if (tid < q.nlive) pre_p = act.probs != nullptr ? act.probs[q.row0 + tid] : 1.0f;
+  };
+  // with an activation: its fp32 values into the LDS tile, once per element (rows and columns
+  // past the live ones hold zero inputs and p = 0, which give +0)
+  auto commit_act = [&]() {
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+      const int r = pass * (kQThreads / kLanesPerRow) + tid / kLanesPerRow;
+      const int ch = tid % kLanesPerRow;
+      const float p = pre_p[pass];
+      float y[8], z[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t hw = (uint32_t)pre[pass][i];
+        const uint32_t w2 = ACT >= 2 ? (uint32_t)pre2[pass][i] : 0u;
+        if constexpr (ACT == 4) {
+          const uint32_t w3 = (uint32_t)pre3[pass][i];
+          glu_grad(bf16_lo(hw), bf16_lo(w2), p, bf16_lo(w3), y[2 * i], z[2 * i]);
+          glu_grad(bf16_hi(hw), bf16_hi(w2), p, bf16_hi(w3), y[2 * i + 1], z[2 * i + 1]);
+        } else {
+          // ACT 2 takes w2 as its dy, ACT 3 as b
+          y[2 * i] = act_value<ACT>(bf16_lo(hw), bf16_lo(w2), p, bf16_lo(w2));
+          y[2 * i + 1] = act_value<ACT>(bf16_hi(hw), bf16_hi(w2), p, bf16_hi(w2));
+        }
+      }
+      *(float4*)&ytile[r][ch * 8] = make_float4(y[0], y[1], y[2], y[3]);
+      *(float4*)&ytile[r][ch * 8 + 4] = make_float4(y[4], y[5], y[6], y[7]);
+      if constexpr (ACT == 4) {
+        *(float4*)&ytile[r][kHalf + ch * 8] = make_float4(z[0], z[1], z[2], z[3]);
+        *(float4*)&ytile[r][kHalf + ch * 8 + 4] = make_float4(z[4], z[5], z[6], z[7]);
+      }
     }
   };
 
@@ -201,14 +253,11 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
   if (!place(rt0, cur)) return;
   load_tile(cur);
   for (int t = 0; t < kQTilesPerWG; ++t) {
-#pragma unroll
-    for (int pass = 0; pass < kQRows / 16; ++pass) {
-      *(v4i*)&tile[pass * 16 + (tid >> 4)][(tid & 15) * 4] = pre[pass];
-      if constexpr (ACT >= 2) *(v4i*)&tile_dy[pass * 16 + (tid >> 4)][(tid & 15) * 4] = pre_dy[pass];
-      if constexpr (ACT == 4) *(v4i*)&tile3[pass * 16 + (tid >> 4)][(tid & 15) * 4] = pre3[pass];
-    }
     if constexpr (ACT != 0) {
-      if (tid < kQRows) prow[tid] = pre_p;
+      commit_act();
+    } else {
+#pragma unroll
+      for (int pass = 0; pass < kPasses; ++pass) *(v4i*)&tile[pass * 16 + (tid >> 4)][(tid & 15) * 4] = pre[pass];
     }
     __syncthreads();
     // the next tile's loads are in flight while this one is quantized
@@ -226,15 +275,9 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
       uint32_t m0 = 0, m1 = 0;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const int r = wave * 32 + i;
-        // h (or a), and the second input: dy (ACT 2) or b (ACT 3, 4); the GLU gradient's dy
-        const uint32_t hw = tile[r][lane], w2 = ACT >= 2 ? tile_dy[r][lane] : 0u;
-        const uint32_t w3 = ACT == 4 ? tile3[r][lane] : 0u;
-        const uint32_t bw = ACT >= 3 ? w2 : 0u, dw = ACT == 2 ? w2 : w3;
-        const bool second = ACT == 4 && c0 + c >= act.glu_f;
-        const float p = prow[r];
-        y0[i] = act_value<ACT>(bf16_lo(hw), bf16_lo(bw), p, bf16_lo(dw), second);
-        y1[i] = act_value<ACT>(bf16_hi(hw), bf16_hi(bw), p, bf16_hi(dw), second);
+        const float2 yy = *(const float2*)&ytile[wave * 32 + i][c];
+        y0[i] = yy.x;
+        y1[i] = yy.y;
         m0 = max(m0, __float_as_uint(y0[i]) & 0x7fffffffu);
         m1 = max(m1, __float_as_uint(y1[i]) & 0x7fffffffu);
       }
@@ -242,7 +285,8 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
       const int e1 = F4 ? e8m0_exponent_fp4(__uint_as_float(m1)) : e8m0_exponent(__uint_as_float(m1));
       const float s0 = exp2_neg(e0), s1 = exp2_neg(e1);
       const uint32_t sbits = (uint32_t)(e0 + 127) | ((uint32_t)(e1 + 127) << 8);
-      if (c0 + c < C) {
+      if (live_col(c)) {
+        const int64_t oc = out_col(c);
         if constexpr (F4) {
           v4i q0, q1;
 #pragma unroll
@@ -252,7 +296,7 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
             q0[i] = (int)e2m1x8(a[0] * s0, a[1] * s0, a[2] * s0, a[3] * s0, a[4] * s0, a[5] * s0, a[6] * s0, a[7] * s0);
             q1[i] = (int)e2m1x8(b[0] * s1, b[1] * s1, b[2] * s1, b[3] * s1, b[4] * s1, b[5] * s1, b[6] * s1, b[7] * s1);
           }
-          uint8_t* dst = col_q + (C * P + (c0 + c) * kp) / 2 + kQRows / 2 * jblk + 16 * wave;
+          uint8_t* dst = col_q + (C * P + oc * kp) / 2 + kQRows / 2 * jblk + 16 * wave;
           *(v4i*)dst = q0;
           *(v4i*)(dst + kp / 2) = q1;
         } else {
@@ -262,13 +306,13 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
             q0[i >> 2][i & 3] = (int)e4m3x4(y0[4 * i] * s0, y0[4 * i + 1] * s0, y0[4 * i + 2] * s0, y0[4 * i + 3] * s0);
             q1[i >> 2][i & 3] = (int)e4m3x4(y1[4 * i] * s1, y1[4 * i + 1] * s1, y1[4 * i + 2] * s1, y1[4 * i + 3] * s1);
           }
-          uint8_t* dst = col_q + C * P + (c0 + c) * kp + kQRows * jblk + 32 * wave;
+          uint8_t* dst = col_q + C * P + oc * kp + kQRows * jblk + 32 * wave;
           *(v4i*)dst = q0[0];
           *(v4i*)(dst + 16) = q0[1];
           *(v4i*)(dst + kp) = q1[0];
           *(v4i*)(dst + kp + 16) = q1[1];
         }
-        *(uint16_t*)((uint8_t*)col_s + C * P / 32 + (4 * jblk + wave) * C + c0 + c) = (uint16_t)sbits;
+        *(uint16_t*)((uint8_t*)col_s + C * P / 32 + (4 * jblk + wave) * C + oc) = (uint16_t)sbits;
       }
     } else if constexpr (COL) {
       // ---- colwise: wave -> 32 tokens, lane -> channel pair ----
@@ -362,24 +406,16 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
       for (int pass = 0; pass < kQRows / 16; ++pass) {
         const int r = pass * 16 + (tid >> 4);
         const int ch = tid & 15;
-        const v4i v = *(const v4i*)&tile[r][ch * 4];
         uint32_t m = 0;
         float yv[8];  // the values this lane quantizes (bf16 inputs, or the activation's fp32 values)
         if constexpr (ACT != 0) {
-          const v4i v2 = ACT >= 2 ? *(const v4i*)&tile_dy[r][ch * 4] : v4i{0, 0, 0, 0};
-          const v4i v3 = ACT == 4 ? *(const v4i*)&tile3[r][ch * 4] : v4i{0, 0, 0, 0};
-          const v4i vb = ACT >= 3 ? v2 : v4i{0, 0, 0, 0}, vd = ACT == 2 ? v2 : v3;
-          const bool second = ACT == 4 && c0 + ch * 8 >= act.glu_f;
-          const float p = prow[r];
+          const float4 ya = *(const float4*)&ytile[r][ch * 8], yb = *(const float4*)&ytile[r][ch * 8 + 4];
+          yv[0] = ya.x, yv[1] = ya.y, yv[2] = ya.z, yv[3] = ya.w;
+          yv[4] = yb.x, yv[5] = yb.y, yv[6] = yb.z, yv[7] = yb.w;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            yv[2 * i] = act_value<ACT>(bf16_lo((uint32_t)v[i]), bf16_lo((uint32_t)vb[i]), p, bf16_lo((uint32_t)vd[i]),
-                                       second);
-            yv[2 * i + 1] = act_value<ACT>(bf16_hi((uint32_t)v[i]), bf16_hi((uint32_t)vb[i]), p,
-                                           bf16_hi((uint32_t)vd[i]), second);
-            m = max(m, max(__float_as_uint(yv[2 * i]) & 0x7fffffffu, __float_as_uint(yv[2 * i + 1]) & 0x7fffffffu));
-          }
+          for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(yv[i]) & 0x7fffffffu);
         } else {
+          const v4i v = *(const v4i*)&tile[r][ch * 4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             yv[2 * i] = bf16_lo((uint32_t)v[i]);
@@ -393,15 +429,15 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
         const float amax = __uint_as_float(m);
         const int e = RECIPE == BSFP8_RECIPE_MXFP4_1X32_E8M0 ? e8m0_exponent_fp4(amax) : e8m0_exponent(amax);
         const float s = exp2_neg(e);
-        if (r < nlive && ch * 8 < ncols) {
+        if (r < nlive && live_col(ch * 8)) {
           if constexpr (RECIPE == BSFP8_RECIPE_MXFP4_1X32_E8M0) {  // 8 codes -> 4 bytes
-            *(uint32_t*)(row_q + ((row0 + r) * C + c0 + ch * 8) / 2) = e2m1x8(
+            *(uint32_t*)(row_q + ((row0 + r) * C + out_col(ch * 8)) / 2) = e2m1x8(
                 yv[0] * s, yv[1] * s, yv[2] * s, yv[3] * s, yv[4] * s, yv[5] * s, yv[6] * s, yv[7] * s);
           } else {
             v2i q;
             q[0] = (int)e4m3x4(yv[0] * s, yv[1] * s, yv[2] * s, yv[3] * s);
             q[1] = (int)e4m3x4(yv[4] * s, yv[5] * s, yv[6] * s, yv[7] * s);
-            *(v2i*)(row_q + (row0 + r) * C + c0 + ch * 8) = q;
+            *(v2i*)(row_q + (row0 + r) * C + out_col(ch * 8)) = q;
           }
         }
         if ((ch & 3) == 0) rs_tile[ch >> 2][r] = (uint8_t)(e + 127);
@@ -411,7 +447,7 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
       for (int i = 0; i < (kQCols / 32) * kQRows / kQThreads; ++i) {
         const int idx = tid + i * kQThreads;
         const int b = idx / kQRows, r = idx % kQRows;
-        if (r < nlive && b * 32 < ncols) row_s[(c0 / 32 + b) * R + row0 + r] = rs_tile[b][r];
+        if (r < nlive && live_col(b * 32)) row_s[(out_col(b * 32) / 32) * R + row0 + r] = rs_tile[b][r];
       }
     }
     __syncthreads();  // the LDS tile and row scales are free for the next tile
