@@ -24,6 +24,10 @@ Reported (one JSON line on stdout):
   legs        mean duration and rate of every kernel of the step.
   graph       the step captured once in a HIP graph and replayed, with the weight quantize run
               and with it skipped on the device by its noop flag (a cached-weight microbatch).
+  mfma_probe  what the matrix cores sustain on this GPU with nothing else in the loop (the
+              probe library libbsfp8_peak.so): bf16 32x32x16 on random and on all-zero
+              operands, scaled fp8 and fp4 32x32x64 on random operands, in TFLOP/s; the
+              roofline object sets the wgrad kernel against the bf16 figure too.
   cpu_baseline the CPU oracle (quantize + fp64 wgrad) on one expert and a slice of the dy
               channels, in the same unit, with the number of threads it used.
 """
@@ -109,6 +113,58 @@ def cpu_baseline(case, experts, channels):
                   f"dy and x rows, then fp64 wgrad of {channels} of {n} dy channels x all {h} x channels "
                   f"({flops / 1e9:.0f} GFLOP useful) in {dt:.1f} s",
     }
+
+
+def mfma_probe(dev, stream, iters=150000):
+    """TFLOP/s of the MFMA-only probe kernels: 2 workgroups of 4 waves per CU, each wave 4
+    independent accumulator chains; 1 warm-up launch, then the mean of 3 launches timed with
+    HIP events on the launch stream."""
+    import ctypes
+
+    import torch
+
+    import workloads as W
+
+    path = os.path.join(ROOT, "block_scaled_fp8_grouped_amd", "libbsfp8_peak.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    lib.bsfp8_mfma_peak_probe.restype = ctypes.c_int
+    lib.bsfp8_mfma_peak_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_void_p]
+    lib.bsfp8_mfma_peak_flops.restype = ctypes.c_double
+    lib.bsfp8_mfma_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]
+    words = 8192  # BSFP8_PEAK_POOL_WORDS
+    blocks = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator(device=dev).manual_seed(90)
+    pools = {
+        "bf16_random": (1, W.randn_bf16((2 * words,), g, dev).view(torch.int32)),
+        "bf16_zero": (1, torch.zeros(words, dtype=torch.int32, device=dev)),
+        "fp8_random": (2, (torch.randn(4 * words, generator=g, device=dev) * 8).to(torch.float8_e4m3fn)
+                       .view(torch.int32)),
+        "fp4_random": (3, torch.randint(-2 ** 31, 2 ** 31 - 1, (words,), generator=g, device=dev,
+                                        dtype=torch.int64).to(torch.int32)),
+    }
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    res = {}
+    for name, (kind, pool) in pools.items():
+        assert pool.numel() == words and pool.is_contiguous()
+
+        def launch():
+            rc = lib.bsfp8_mfma_peak_probe(kind, pool.data_ptr(), out.data_ptr(), blocks, iters,
+                                           ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"mfma probe {name}: error {rc}")
+        launch()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 3
+        res[name + "_TFLOP/s"] = round(lib.bsfp8_mfma_peak_flops(kind, blocks, iters) / (ms / 1e3) / 1e12, 1)
+    return res
 
 
 def graph_leg(graph_step, flag, stream):
@@ -459,6 +515,14 @@ def main():
                         "ms_per_step_cached_weight": round(graph_ms["replay_cached_weight"], 3),
                         "note": "the step captured once and replayed; cached_weight: weight quantize "
                                 "skipped on the device by its noop flag"}
+    log("MFMA-only probe")
+    probe = mfma_probe(dev, stream)
+    out["mfma_probe"] = dict(probe, note="MFMA-only kernels, no memory traffic in the loop: what the "
+                                         "matrix cores sustain on this GPU")
+    out["roofline"]["frac_of_probe_bf16"] = round(achieved / probe["bf16_random_TFLOP/s"], 4)
+    if mx4 is not None:
+        out["mxfp4"]["wgrad_frac_of_fp4_probe"] = round(T4 / (mx4["wgrad"] / 1e3) / 1e12
+                                                        / probe["fp4_random_TFLOP/s"], 4)
     if args.calibrate_copy_gb > 0:
         nbytes = int(args.calibrate_copy_gb * 1e9) // 16 * 16
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)

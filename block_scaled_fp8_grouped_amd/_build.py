@@ -13,6 +13,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libbsfp8.so")
 SOURCES = ["bsfp8.cpp", "quantize.hip", "gemm.hip"]
+# the MFMA-only throughput probe, a library of its own (measurement, not the path)
+PEAK_LIB_PATH = os.path.join(HERE, "libbsfp8_peak.so")
+PEAK_SOURCES = ["mfma_peak.hip"]
 HEADERS = ["common.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -33,21 +36,28 @@ def _compile(src, obj):
     return obj
 
 
-def build(verbose=True):
-    """Compile every source for gfx950 and link libbsfp8.so next to this file."""
-    objdir = os.path.join(ROOT, "_build")
-    os.makedirs(objdir, exist_ok=True)
-    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        list(ex.map(_compile, SOURCES, objs))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path):
+    tmp = path + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose=True):
+    """Compile every source for gfx950 and link libbsfp8.so (and the probe libbsfp8_peak.so)
+    next to this file."""
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = SOURCES + PEAK_SOURCES
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in srcs]
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        list(ex.map(_compile, srcs, objs))
+    _link(objs[:len(SOURCES)], LIB_PATH)
+    _link(objs[len(SOURCES):], PEAK_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}", file=sys.stderr)
+        print(f"built {LIB_PATH} and {PEAK_LIB_PATH}", file=sys.stderr)
     return LIB_PATH
 
 

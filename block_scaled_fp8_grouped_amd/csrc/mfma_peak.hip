@@ -1,0 +1,90 @@
+// MFMA-only throughput probe (libbsfp8_peak.so): the rate the matrix cores sustain on this
+// machine with nothing else in the loop, to set the grouped GEMMs against.
+//
+// Each wave holds its A and B operands in registers (read once from the caller's pool) and
+// issues 4 independent accumulator chains of one instruction per iteration; with 2 workgroups
+// of 4 waves per CU the MFMA pipe of every SIMD always has an independent instruction ready.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bsfp8_peak.h"
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kChains = 4;
+
+template <int KIND>
+__global__ __launch_bounds__(BSFP8_PEAK_THREADS) void mfma_peak_kernel(const uint32_t* __restrict__ pool,
+                                                                        float* __restrict__ out, int64_t iters) {
+  const int64_t t = (int64_t)blockIdx.x * BSFP8_PEAK_THREADS + threadIdx.x;
+  v8i a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (int)pool[(t * 16 + i) & (BSFP8_PEAK_POOL_WORDS - 1)];
+    b[i] = (int)pool[(t * 16 + 8 + i) & (BSFP8_PEAK_POOL_WORDS - 1)];
+  }
+  v16f acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = v16f{};
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) {
+      if constexpr (KIND == BSFP8_PEAK_BF16) {
+        const v4i a4 = v4i{a[0], a[1], a[2], a[3]}, b4 = v4i{b[0], b[1], b[2], b[3]};
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a4), __builtin_bit_cast(v8bf, b4),
+                                                         acc[c], 0, 0, 0);
+      } else if constexpr (KIND == BSFP8_PEAK_FP8) {
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[c], 0, 0, 0, 127, 0, 127);
+      } else {
+        const v8i a4 = v8i{a[0], a[1], a[2], a[3], 0, 0, 0, 0}, b4 = v8i{b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, acc[c], 4, 4, 0, 127, 0, 127);
+      }
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc[c][i];
+  out[t] = s;
+}
+
+double mfma_flops(int kind) {
+  switch (kind) {
+    case BSFP8_PEAK_BF16: return 2.0 * 32 * 32 * 16;
+    case BSFP8_PEAK_FP8:
+    case BSFP8_PEAK_FP4: return 2.0 * 32 * 32 * 64;
+    default: return 0.0;
+  }
+}
+
+}  // namespace
+
+extern "C" int bsfp8_mfma_peak_probe(int kind, const uint32_t* pool, float* out, int64_t blocks, int64_t iters,
+                                     void* stream) {
+  if (pool == nullptr || out == nullptr) return -1;
+  if (mfma_flops(kind) == 0.0) return -2;
+  if (blocks < 1 || blocks > 65536 || iters < 1 || iters > (int64_t(1) << 31)) return -3;
+  const dim3 grid((unsigned)blocks), block(BSFP8_PEAK_THREADS);
+  hipStream_t s = (hipStream_t)stream;
+  switch (kind) {
+    case BSFP8_PEAK_BF16:
+      hipLaunchKernelGGL(mfma_peak_kernel<BSFP8_PEAK_BF16>, grid, block, 0, s, pool, out, iters);
+      break;
+    case BSFP8_PEAK_FP8:
+      hipLaunchKernelGGL(mfma_peak_kernel<BSFP8_PEAK_FP8>, grid, block, 0, s, pool, out, iters);
+      break;
+    default:
+      hipLaunchKernelGGL(mfma_peak_kernel<BSFP8_PEAK_FP4>, grid, block, 0, s, pool, out, iters);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+extern "C" double bsfp8_mfma_peak_flops(int kind, int64_t blocks, int64_t iters) {
+  return mfma_flops(kind) * (double)blocks * (BSFP8_PEAK_THREADS / 64) * (double)iters * kChains;
+}

@@ -1,0 +1,50 @@
+/*
+ * bsfp8_peak.h — MFMA-only throughput probe for MI355X (gfx950), built as libbsfp8_peak.so.
+ *
+ * Not part of the quantize / GEMM path.  The grouped-GEMM throughput is quoted as a fraction of
+ * the matrix-core peak; the published dense peaks assume the full engine clock, which a chip
+ * running dense MFMA work on random operands need not hold.  This probe measures what the
+ * matrix cores sustain on this machine when they do nothing else: every wave of the grid
+ * issues independent chains of one MFMA instruction on operands read once from a caller pool,
+ * with no memory traffic inside the loop, so the GEMM kernels can be set against it.
+ *
+ * All pointers are device pointers owned by the caller; nothing is allocated.  Calls are
+ * asynchronous on `stream` (a hipStream_t, NULL = the default stream).
+ */
+#ifndef BSFP8_PEAK_H
+#define BSFP8_PEAK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Instruction of a probe launch. */
+#define BSFP8_PEAK_BF16 1 /* v_mfma_f32_32x32x16_bf16: the instruction of the MXFP8 GEMMs */
+#define BSFP8_PEAK_FP8 2  /* v_mfma_scale_f32_32x32x64_f8f6f4, e4m3 x e4m3, unit scales */
+#define BSFP8_PEAK_FP4 3  /* the same, e2m1 x e2m1: the instruction of the MXFP4 GEMMs */
+
+#define BSFP8_PEAK_POOL_WORDS 8192  /* uint32 words of the operand pool */
+#define BSFP8_PEAK_THREADS 256      /* threads per workgroup (4 waves) */
+
+/*
+ * Run `blocks` workgroups of 4 waves; each wave issues iters x 4 MFMAs of `kind` (4 independent
+ * accumulator chains).  Lane t of the grid takes its A and B operand words from the pool at
+ * words [16 t, 16 t + 16) modulo BSFP8_PEAK_POOL_WORDS (bf16: 4 words each; fp8: 8 words;
+ * fp4: the first 4 of 8), so the operands are whatever the caller put there (random values
+ * give the switching activity of real data).  out (fp32 [blocks * 256]) receives one sum of
+ * each lane's accumulators, which keeps the work live; its value has no meaning.
+ * Returns 0, or a negative code: -1 NULL pointer, -2 kind, -3 blocks or iters out of range
+ * (1 <= blocks <= 65536, 1 <= iters <= 2^31), -4 the launch failed.
+ */
+int bsfp8_mfma_peak_probe(int kind, const uint32_t* pool, float* out, int64_t blocks, int64_t iters, void* stream);
+
+/* Dense FLOPs one probe launch performs (2 M N K per MFMA), or 0 for an invalid kind. */
+double bsfp8_mfma_peak_flops(int kind, int64_t blocks, int64_t iters);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSFP8_PEAK_H */

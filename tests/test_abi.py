@@ -1,7 +1,8 @@
 """C-ABI checks that need no GPU: every function declared in include/bsfp8.h is exported by
-libbsfp8.so, the size queries follow their documented formulas, and every host-checkable error
-is returned before the library touches a pointer or makes a HIP call (the fake pointers used
-below are never dereferenced)."""
+libbsfp8.so (and those of include/bsfp8_peak.h by the probe library libbsfp8_peak.so), the size
+queries follow their documented formulas, and every host-checkable error is returned before the
+library touches a pointer or makes a HIP call (the fake pointers used below are never
+dereferenced)."""
 import ctypes
 import os
 import re
@@ -17,8 +18,8 @@ P = 1 << 20  # a fake, 16-byte-aligned device address; never dereferenced by the
 MX, PC, MX4 = bs.RECIPE_MX, bs.RECIPE_PC, bs.RECIPE_MX4
 
 
-def _declared():
-    text = open(HDR).read()
+def _declared(hdr=HDR):
+    text = open(hdr).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(bsfp8_\w+)\s*\(", text)))
 
@@ -34,6 +35,33 @@ def test_every_declared_symbol_is_exported():
     L = bs.lib()
     for n in names:
         assert hasattr(L, n), n
+
+
+def _peak_lib():
+    L = ctypes.CDLL(os.path.join(ROOT, "block_scaled_fp8_grouped_amd", "libbsfp8_peak.so"))
+    L.bsfp8_mfma_peak_probe.restype = ctypes.c_int
+    L.bsfp8_mfma_peak_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_void_p]
+    L.bsfp8_mfma_peak_flops.restype = ctypes.c_double
+    L.bsfp8_mfma_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]
+    return L
+
+
+def test_probe_library_exports_and_rejects_before_launch():
+    L = _peak_lib()
+    names = _declared(os.path.join(ROOT, "include", "bsfp8_peak.h"))
+    assert names == ["bsfp8_mfma_peak_flops", "bsfp8_mfma_peak_probe"]
+    for n in names:
+        assert hasattr(L, n), n
+    probe = L.bsfp8_mfma_peak_probe
+    assert probe(1, None, P, 512, 10, None) == -1 and probe(1, P, None, 512, 10, None) == -1
+    assert probe(0, P, P, 512, 10, None) == -2 and probe(4, P, P, 512, 10, None) == -2
+    assert probe(1, P, P, 0, 10, None) == -3 and probe(1, P, P, 65537, 10, None) == -3
+    assert probe(1, P, P, 512, 0, None) == -3 and probe(1, P, P, 512, (1 << 31) + 1, None) == -3
+    # 2 M N K per MFMA x 4 chains x 4 waves per workgroup
+    assert L.bsfp8_mfma_peak_flops(1, 512, 10) == 2 * 32 * 32 * 16 * 4 * 4 * 512 * 10
+    assert L.bsfp8_mfma_peak_flops(3, 3, 7) == 2 * 32 * 32 * 64 * 4 * 4 * 3 * 7
+    assert L.bsfp8_mfma_peak_flops(5, 3, 7) == 0.0
 
 
 def test_binding_constants_match_header():

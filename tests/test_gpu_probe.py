@@ -1,0 +1,46 @@
+"""The MFMA-only probe (libbsfp8_peak.so) does the work it is credited with: on all-ones operands
+every MFMA adds K to each of a lane's 16 accumulators, so each lane's output is
+chains x 16 x K x iters, which fixes K (16 for bf16 32x32x16, 64 for the scaled fp8 and fp4
+32x32x64) and the number of MFMAs the FLOP count assumes."""
+import ctypes
+import os
+
+import pytest
+import torch
+
+from gpu_util import DEV, flush
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+WORDS = 8192
+
+# one 32-bit pool word of ones: bf16 1.0 = 0x3F80, e4m3 1.0 = 0x38, e2m1 1.0 = code 2 per nibble
+ONES = {1: 0x3F803F80, 2: 0x38383838, 3: 0x22222222}
+K = {1: 16, 2: 64, 3: 64}
+
+
+def _lib():
+    L = ctypes.CDLL(os.path.join(ROOT, "block_scaled_fp8_grouped_amd", "libbsfp8_peak.so"))
+    L.bsfp8_mfma_peak_probe.restype = ctypes.c_int
+    L.bsfp8_mfma_peak_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_void_p]
+    L.bsfp8_mfma_peak_flops.restype = ctypes.c_double
+    L.bsfp8_mfma_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]
+    return L
+
+
+@pytest.mark.parametrize("kind", [1, 2, 3])
+def test_probe_counts_its_mfmas(kind):
+    flush(f"mfma probe kind={kind}")
+    L = _lib()
+    blocks, iters = 6, 37
+    word = ONES[kind]
+    pool = torch.full((WORDS,), word - (1 << 32) if word >= 1 << 31 else word, dtype=torch.int32, device=DEV)
+    out = torch.full((blocks * 256,), float("nan"), dtype=torch.float32, device=DEV)
+    rc = L.bsfp8_mfma_peak_probe(kind, pool.data_ptr(), out.data_ptr(), blocks, iters,
+                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert torch.equal(out, torch.full_like(out, 4 * 16 * K[kind] * iters))
+    # the credited FLOPs: 2 * 32 * 32 * K per MFMA, 4 chains per iteration, 4 waves per workgroup
+    assert L.bsfp8_mfma_peak_flops(kind, blocks, iters) == 2 * 32 * 32 * K[kind] * 4 * iters * 4 * blocks
