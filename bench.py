@@ -131,7 +131,10 @@ def mfma_probe(dev, stream, iters=150000):
     lib = ctypes.CDLL(path)
     lib.bsfp8_mfma_peak_probe.restype = ctypes.c_int
     lib.bsfp8_mfma_peak_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                          ctypes.c_int64, ctypes.c_void_p]
+                                          ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bsfp8_wall_clock_khz.restype = ctypes.c_int
+    lib.bsfp8_wall_clock_khz.argtypes = [ctypes.c_int]
+    wall_khz = lib.bsfp8_wall_clock_khz(torch.cuda.current_device())
     lib.bsfp8_mfma_peak_flops.restype = ctypes.c_double
     lib.bsfp8_mfma_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]
     words = 8192  # BSFP8_PEAK_POOL_WORDS
@@ -146,12 +149,14 @@ def mfma_probe(dev, stream, iters=150000):
                                         dtype=torch.int64).to(torch.int32)),
     }
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stamps = torch.zeros(blocks, 4, dtype=torch.int64, device=dev)
     res = {}
     for name, (kind, pool) in pools.items():
         assert pool.numel() == words and pool.is_contiguous()
 
-        def launch():
+        def launch(stamp=None):
             rc = lib.bsfp8_mfma_peak_probe(kind, pool.data_ptr(), out.data_ptr(), blocks, iters,
+                                           None if stamp is None else stamp.data_ptr(),
                                            ctypes.c_void_p(stream.cuda_stream))
             if rc != 0:
                 raise RuntimeError(f"mfma probe {name}: error {rc}")
@@ -164,6 +169,12 @@ def mfma_probe(dev, stream, iters=150000):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / 3
         res[name + "_TFLOP/s"] = round(lib.bsfp8_mfma_peak_flops(kind, blocks, iters) / (ms / 1e3) / 1e12, 1)
+        # one more launch with clock stamps: the shader clock held over each workgroup's loop
+        launch(stamps)
+        torch.cuda.synchronize()
+        st = stamps.cpu().double()
+        ghz = ((st[:, 2] - st[:, 0]) / (st[:, 3] - st[:, 1]) * wall_khz / 1e6).median().item()
+        res[name + "_clock_GHz"] = round(ghz, 3)
     return res
 
 
@@ -311,6 +322,9 @@ def main():
     # GPU-side span of the timed steps (first kernel start to last kernel end), per step
     event_ms_per_step = events[0][0].elapsed_time(events[-1][5]) / args.steps
     leg_ms = {name: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps for i, name in enumerate(legs)}
+    wgrad_each = sorted(ev[3].elapsed_time(ev[4]) for ev in events)
+    wgrad_median = wgrad_each[len(wgrad_each) // 2] if len(wgrad_each) % 2 else \
+        (wgrad_each[len(wgrad_each) // 2 - 1] + wgrad_each[len(wgrad_each) // 2]) / 2
 
     # The data-gradient GEMM (dx_e = dy_e @ W_e), the next GEMM of the expert backward: timed on
     # its own after the step (it is not part of the step or of `value`), with its two quantize
@@ -475,7 +489,8 @@ def main():
                             "GB/s": round(bytes_dy / (leg_ms["quantize_dy"] / 1e3) / 1e9, 1)},
             "quantize_w": {"ms": round(leg_ms["quantize_w"], 3),
                            "GB/s": round(bytes_w / (leg_ms["quantize_w"] / 1e3) / 1e9, 1)},
-            "wgrad": {"ms": round(leg_ms["wgrad"], 3), "TFLOP/s": round(achieved, 1),
+            "wgrad": {"ms": round(leg_ms["wgrad"], 3), "ms_median": round(wgrad_median, 3),
+                      "ms_min": round(wgrad_each[0], 3), "TFLOP/s": round(achieved, 1),
                       "algorithmic_GB": round(wgrad_bytes / 1e9, 2)},
             "fprop": {"ms": round(leg_ms["fprop"], 3),
                       "TFLOP/s": round(fprop_flop / (leg_ms["fprop"] / 1e3) / 1e12, 1),

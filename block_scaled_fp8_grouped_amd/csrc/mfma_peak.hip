@@ -4,6 +4,8 @@
 // Each wave holds its A and B operands in registers (read once from the caller's pool) and
 // issues 4 independent accumulator chains of one instruction per iteration; with 2 workgroups
 // of 4 waves per CU the MFMA pipe of every SIMD always has an independent instruction ready.
+// Optionally the first wave of each workgroup stamps the shader-clock counter and the
+// constant-rate real-time counter around its loop, which gives the clock the chip held.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,7 +22,8 @@ constexpr int kChains = 4;
 
 template <int KIND>
 __global__ __launch_bounds__(BSFP8_PEAK_THREADS) void mfma_peak_kernel(const uint32_t* __restrict__ pool,
-                                                                        float* __restrict__ out, int64_t iters) {
+                                                                        float* __restrict__ out, int64_t iters,
+                                                                        uint64_t* __restrict__ stamps) {
   const int64_t t = (int64_t)blockIdx.x * BSFP8_PEAK_THREADS + threadIdx.x;
   v8i a, b;
 #pragma unroll
@@ -31,6 +34,11 @@ __global__ __launch_bounds__(BSFP8_PEAK_THREADS) void mfma_peak_kernel(const uin
   v16f acc[kChains];
 #pragma unroll
   for (int c = 0; c < kChains; ++c) acc[c] = v16f{};
+  uint64_t clk0 = 0, rt0 = 0;
+  if (stamps != nullptr && threadIdx.x == 0) {
+    clk0 = __builtin_amdgcn_s_memtime();
+    rt0 = __builtin_amdgcn_s_memrealtime();
+  }
   for (int64_t it = 0; it < iters; ++it) {
 #pragma unroll
     for (int c = 0; c < kChains; ++c) {
@@ -51,6 +59,15 @@ __global__ __launch_bounds__(BSFP8_PEAK_THREADS) void mfma_peak_kernel(const uin
   for (int c = 0; c < kChains; ++c)
 #pragma unroll
     for (int i = 0; i < 16; ++i) s += acc[c][i];
+  if (stamps != nullptr && threadIdx.x == 0) {
+    // the end stamps follow the sum of every accumulator, i.e. the wave's last MFMA result
+    asm volatile("" ::"v"(s));
+    const uint64_t clk1 = __builtin_amdgcn_s_memtime(), rt1 = __builtin_amdgcn_s_memrealtime();
+    stamps[4 * blockIdx.x + 0] = clk0;
+    stamps[4 * blockIdx.x + 1] = rt0;
+    stamps[4 * blockIdx.x + 2] = clk1;
+    stamps[4 * blockIdx.x + 3] = rt1;
+  }
   out[t] = s;
 }
 
@@ -66,7 +83,7 @@ double mfma_flops(int kind) {
 }  // namespace
 
 extern "C" int bsfp8_mfma_peak_probe(int kind, const uint32_t* pool, float* out, int64_t blocks, int64_t iters,
-                                     void* stream) {
+                                     uint64_t* stamps, void* stream) {
   if (pool == nullptr || out == nullptr) return -1;
   if (mfma_flops(kind) == 0.0) return -2;
   if (blocks < 1 || blocks > 65536 || iters < 1 || iters > (int64_t(1) << 31)) return -3;
@@ -74,17 +91,23 @@ extern "C" int bsfp8_mfma_peak_probe(int kind, const uint32_t* pool, float* out,
   hipStream_t s = (hipStream_t)stream;
   switch (kind) {
     case BSFP8_PEAK_BF16:
-      hipLaunchKernelGGL(mfma_peak_kernel<BSFP8_PEAK_BF16>, grid, block, 0, s, pool, out, iters);
+      hipLaunchKernelGGL(mfma_peak_kernel<BSFP8_PEAK_BF16>, grid, block, 0, s, pool, out, iters, stamps);
       break;
     case BSFP8_PEAK_FP8:
-      hipLaunchKernelGGL(mfma_peak_kernel<BSFP8_PEAK_FP8>, grid, block, 0, s, pool, out, iters);
+      hipLaunchKernelGGL(mfma_peak_kernel<BSFP8_PEAK_FP8>, grid, block, 0, s, pool, out, iters, stamps);
       break;
     default:
-      hipLaunchKernelGGL(mfma_peak_kernel<BSFP8_PEAK_FP4>, grid, block, 0, s, pool, out, iters);
+      hipLaunchKernelGGL(mfma_peak_kernel<BSFP8_PEAK_FP4>, grid, block, 0, s, pool, out, iters, stamps);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 extern "C" double bsfp8_mfma_peak_flops(int kind, int64_t blocks, int64_t iters) {
   return mfma_flops(kind) * (double)blocks * (BSFP8_PEAK_THREADS / 64) * (double)iters * kChains;
+}
+
+extern "C" int bsfp8_wall_clock_khz(int device) {
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) != hipSuccess) return -1;
+  return khz;
 }

@@ -34,11 +34,20 @@ extern "C" {
  * words [16 t, 16 t + 16) modulo BSFP8_PEAK_POOL_WORDS (bf16: 4 words each; fp8: 8 words;
  * fp4: the first 4 of 8), so the operands are whatever the caller put there (random values
  * give the switching activity of real data).  out (fp32 [blocks * 256]) receives one sum of
- * each lane's accumulators, which keeps the work live; its value has no meaning.
- * Returns 0, or a negative code: -1 NULL pointer, -2 kind, -3 blocks or iters out of range
+ * each lane's accumulators, which keeps the work live (all-ones operands make it exactly
+ * 4 * 16 * K * iters, K = 16 for bf16 and 64 for fp8 / fp4).
+ * stamps (nullable, uint64 [blocks][4]): the first wave of workgroup b writes the shader-clock
+ * counter and the real-time counter before its loop and after its last MFMA result,
+ * (clk0, rt0, clk1, rt1); (clk1 - clk0) / (rt1 - rt0) times the real-time rate
+ * (bsfp8_wall_clock_khz) is the shader clock the chip held meanwhile.
+ * Returns 0, or a negative code: -1 NULL pool or out, -2 kind, -3 blocks or iters out of range
  * (1 <= blocks <= 65536, 1 <= iters <= 2^31), -4 the launch failed.
  */
-int bsfp8_mfma_peak_probe(int kind, const uint32_t* pool, float* out, int64_t blocks, int64_t iters, void* stream);
+int bsfp8_mfma_peak_probe(int kind, const uint32_t* pool, float* out, int64_t blocks, int64_t iters,
+                          uint64_t* stamps, void* stream);
+
+/* Rate of the real-time counter of `device` in kHz (HIP's wall-clock rate), or -1. */
+int bsfp8_wall_clock_khz(int device);
 
 /* Dense FLOPs one probe launch performs (2 M N K per MFMA), or 0 for an invalid kind. */
 double bsfp8_mfma_peak_flops(int kind, int64_t blocks, int64_t iters);

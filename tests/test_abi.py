@@ -41,7 +41,7 @@ def _peak_lib():
     L = ctypes.CDLL(os.path.join(ROOT, "block_scaled_fp8_grouped_amd", "libbsfp8_peak.so"))
     L.bsfp8_mfma_peak_probe.restype = ctypes.c_int
     L.bsfp8_mfma_peak_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                        ctypes.c_int64, ctypes.c_void_p]
+                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     L.bsfp8_mfma_peak_flops.restype = ctypes.c_double
     L.bsfp8_mfma_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]
     return L
@@ -50,14 +50,15 @@ def _peak_lib():
 def test_probe_library_exports_and_rejects_before_launch():
     L = _peak_lib()
     names = _declared(os.path.join(ROOT, "include", "bsfp8_peak.h"))
-    assert names == ["bsfp8_mfma_peak_flops", "bsfp8_mfma_peak_probe"]
+    assert names == ["bsfp8_mfma_peak_flops", "bsfp8_mfma_peak_probe", "bsfp8_wall_clock_khz"]
     for n in names:
         assert hasattr(L, n), n
-    probe = L.bsfp8_mfma_peak_probe
-    assert probe(1, None, P, 512, 10, None) == -1 and probe(1, P, None, 512, 10, None) == -1
-    assert probe(0, P, P, 512, 10, None) == -2 and probe(4, P, P, 512, 10, None) == -2
-    assert probe(1, P, P, 0, 10, None) == -3 and probe(1, P, P, 65537, 10, None) == -3
-    assert probe(1, P, P, 512, 0, None) == -3 and probe(1, P, P, 512, (1 << 31) + 1, None) == -3
+    def probe(kind, pool, out, blocks, iters):
+        return L.bsfp8_mfma_peak_probe(kind, pool, out, blocks, iters, None, None)
+    assert probe(1, None, P, 512, 10) == -1 and probe(1, P, None, 512, 10) == -1
+    assert probe(0, P, P, 512, 10) == -2 and probe(4, P, P, 512, 10) == -2
+    assert probe(1, P, P, 0, 10) == -3 and probe(1, P, P, 65537, 10) == -3
+    assert probe(1, P, P, 512, 0) == -3 and probe(1, P, P, 512, (1 << 31) + 1) == -3
     # 2 M N K per MFMA x 4 chains x 4 waves per workgroup
     assert L.bsfp8_mfma_peak_flops(1, 512, 10) == 2 * 32 * 32 * 16 * 4 * 4 * 512 * 10
     assert L.bsfp8_mfma_peak_flops(3, 3, 7) == 2 * 32 * 32 * 64 * 4 * 4 * 3 * 7

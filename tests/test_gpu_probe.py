@@ -1,7 +1,8 @@
 """The MFMA-only probe (libbsfp8_peak.so) does the work it is credited with: on all-ones operands
 every MFMA adds K to each of a lane's 16 accumulators, so each lane's output is
 chains x 16 x K x iters, which fixes K (16 for bf16 32x32x16, 64 for the scaled fp8 and fp4
-32x32x64) and the number of MFMAs the FLOP count assumes."""
+32x32x64) and the number of MFMAs the FLOP count assumes; the clock stamps give a shader clock
+within the chip's range."""
 import ctypes
 import os
 
@@ -23,7 +24,9 @@ def _lib():
     L = ctypes.CDLL(os.path.join(ROOT, "block_scaled_fp8_grouped_amd", "libbsfp8_peak.so"))
     L.bsfp8_mfma_peak_probe.restype = ctypes.c_int
     L.bsfp8_mfma_peak_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                        ctypes.c_int64, ctypes.c_void_p]
+                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    L.bsfp8_wall_clock_khz.restype = ctypes.c_int
+    L.bsfp8_wall_clock_khz.argtypes = [ctypes.c_int]
     L.bsfp8_mfma_peak_flops.restype = ctypes.c_double
     L.bsfp8_mfma_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]
     return L
@@ -37,10 +40,23 @@ def test_probe_counts_its_mfmas(kind):
     word = ONES[kind]
     pool = torch.full((WORDS,), word - (1 << 32) if word >= 1 << 31 else word, dtype=torch.int32, device=DEV)
     out = torch.full((blocks * 256,), float("nan"), dtype=torch.float32, device=DEV)
-    rc = L.bsfp8_mfma_peak_probe(kind, pool.data_ptr(), out.data_ptr(), blocks, iters,
-                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    stamps = torch.zeros(blocks, 4, dtype=torch.int64, device=DEV)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rc = L.bsfp8_mfma_peak_probe(kind, pool.data_ptr(), out.data_ptr(), blocks, iters, None, s)
     torch.cuda.synchronize()
     assert rc == 0
     assert torch.equal(out, torch.full_like(out, 4 * 16 * K[kind] * iters))
+    out.fill_(float("nan"))
+    rc = L.bsfp8_mfma_peak_probe(kind, pool.data_ptr(), out.data_ptr(), blocks, 20000, stamps.data_ptr(), s)
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert torch.equal(out, torch.full_like(out, 4 * 16 * K[kind] * 20000))
+    st = stamps.cpu().double()
+    assert (st[:, 2] > st[:, 0]).all() and (st[:, 3] > st[:, 1]).all()
+    khz = L.bsfp8_wall_clock_khz(torch.cuda.current_device())
+    assert khz > 0
+    ghz = (st[:, 2] - st[:, 0]) / (st[:, 3] - st[:, 1]) * khz / 1e6
+    flush(f"probe kind={kind}: wall clock {khz} kHz, shader clock {ghz.median().item():.3f} GHz")
+    assert 0.3 < ghz.median().item() < 3.0
     # the credited FLOPs: 2 * 32 * 32 * K per MFMA, 4 chains per iteration, 4 waves per workgroup
     assert L.bsfp8_mfma_peak_flops(kind, blocks, iters) == 2 * 32 * 32 * K[kind] * 4 * iters * 4 * blocks
