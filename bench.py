@@ -530,6 +530,22 @@ def main():
                         "ms_per_step_cached_weight": round(graph_ms["replay_cached_weight"], 3),
                         "note": "the step captured once and replayed; cached_weight: weight quantize "
                                 "skipped on the device by its noop flag"}
+    # what a plain device copy reaches on this GPU (read + write bytes), beside the HBM-bound legs
+    log("device copy reference")
+    cp_src = torch.empty(1 << 30, dtype=torch.float32, device=dev).fill_(1.0)
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        cp_dst.copy_(cp_src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / 5
+    out["hbm_copy_reference"] = {"bytes": 2 * 4 * (1 << 30), "ms": round(copy_ms, 3),
+                                 "GB/s": round(2 * 4 * (1 << 30) / (copy_ms / 1e3) / 1e9, 1),
+                                 "note": "torch copy of 4 GiB (read + write); the HBM-bound legs compare to it"}
+    del cp_src, cp_dst
     log("MFMA-only probe")
     probe = mfma_probe(dev, stream)
     out["mfma_probe"] = dict(probe, note="MFMA-only kernels, no memory traffic in the loop: what the "

@@ -78,6 +78,26 @@ __device__ __forceinline__ void buffer_dma16(__amdgpu_buffer_rsrc_t rs, uint8_t*
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
+// The MXFP4 loop issues its DMAs as inline assembly (M0 = the wave-uniform LDS byte address,
+// one wait state between setting M0 and its use).  Issued through the builtins, the compiler
+// cannot tell the DMA into the next LDS stage from the reads of the current one and makes the
+// step's later fragment reads wait for it, which leaves the DMA no time to hide behind; the
+// kernel waits for its DMAs itself (s_waitcnt vmcnt(0) before a stage is read), and any wait
+// the compiler places for its own loads only waits longer, as loads complete in order.
+__device__ __forceinline__ void asm_dma16(v4i rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void asm_dma4(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "{m0}"(lds) : "memory");
+}
+// The four words of a raw buffer resource (base, stride 0, num_records bytes, the flags word
+// passed to __builtin_amdgcn_make_buffer_rsrc elsewhere), wave-uniform.
+__device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t num_records) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return v4i{__builtin_amdgcn_readfirstlane((int)(uint32_t)a), __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff)),
+             __builtin_amdgcn_readfirstlane((int)num_records), 0x00020000};
+}
+
 template <bool B>
 struct BoolC {
   static constexpr bool value = B;
@@ -226,9 +246,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
       (void*)(a_data + a_row0 * lda), (short)0, (int)tile_range(a_valid - a_row0, lda), 0x00020000);
   const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(b_data + b_row0 * ldb), (short)0, (int)tile_range(b_valid - b_row0, ldb), 0x00020000);
+  // LDS byte address of a place in smem (MXFP4's assembly DMAs take it in M0)
+  const uint32_t smem_lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem);
+  auto lds_of = [&](const uint8_t* p) { return smem_lds + (uint32_t)(p - smem); };
   auto dma4 = [&](const void* g, uint8_t* l) {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+    if constexpr (F4) asm_dma4(g, lds_of(l));
+    else __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
   };
+  const v4i a_rw = rsrc_words(a_data + a_row0 * lda, (uint32_t)tile_range(a_valid - a_row0, lda));
+  const v4i b_rw = rsrc_words(b_data + b_row0 * ldb, (uint32_t)tile_range(b_valid - b_row0, ldb));
   constexpr int FA_ROWS = SBLK * BM / NT;  // fprop: A-scale bytes (rows) each thread stages per K step
   uint8_t fa_b[FA_ROWS];                 // fprop: those bytes, held in registers until settle
   uint32_t a_off[S::A_INS], b_off[S::B_INS];
@@ -269,12 +296,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
 #pragma unroll
     for (int u = 0; u < S::A_INS; ++u) {
       const int g = wave * S::A_INS + u;
-      buffer_dma16(a_rs, base + S::A_OFF + g * 1024, a_off[u] + k0);
+      if constexpr (F4) asm_dma16(a_rw, lds_of(base + S::A_OFF + g * 1024), a_off[u] + k0);
+      else buffer_dma16(a_rs, base + S::A_OFF + g * 1024, a_off[u] + k0);
     }
 #pragma unroll
     for (int u = 0; u < S::B_INS; ++u) {
       const int g = wave * S::B_INS + u;
-      buffer_dma16(b_rs, base + S::B_OFF + g * 1024, b_off[u] + k0);
+      if constexpr (F4) asm_dma16(b_rw, lds_of(base + S::B_OFF + g * 1024), b_off[u] + k0);
+      else buffer_dma16(b_rs, base + S::B_OFF + g * 1024, b_off[u] + k0);
     }
     if constexpr (PC) {
       // one fp32 per row: BM + BN dwords, 64 per instruction
