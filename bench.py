@@ -245,6 +245,92 @@ def mxfp4_leg(bs, W, case, st, R, n, h, K, N, E, mg, status, stream):
     return ms
 
 
+def moe32_step_bench(args):
+    """The same step on the 32-expert layer (65,536 routed rows, Zipf counts with 4 empty
+    experts, hidden 4096, ffn 1536, padded capacity with garbage rows): quantize x (row+col),
+    dy (col), W (row); wgrad stored fp32 [32, 1536, 4096]; fprop fp32 [R, 1536].  Near the
+    MFMA/HBM ridge, so the kernels are reported in microseconds beside their rates.  Prints one
+    JSON line; used for profiling this shape, not the headline figure."""
+    import torch
+
+    import block_scaled_fp8_grouped_amd as bs
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = W.moe32_zipf(dev)
+    splits, R, T = case["splits"], case["R"], case["T"]
+    n, h, K, N = case["n"], case["h"], case["K"], case["N"]
+    E = len(splits)
+    st = W.splits_tensor(splits, dev)
+    xq = bs.alloc_quantized(R, h, E, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, dev)
+    dq = bs.alloc_quantized(R, n, E, bs.RECIPE_MX, bs.COLWISE, dev)
+    wq = bs.alloc_quantized(E * N, K, 1, bs.RECIPE_MX, bs.ROWWISE, dev)
+    dw = torch.empty(E, n, h, dtype=torch.float32, device=dev)
+    fout = torch.empty(R, N, dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    w2 = case["W"].view(E * N, K)
+    legs = ["quantize_x", "quantize_dy", "quantize_w", "wgrad", "fprop"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        bs.grouped_quantize(case["x"], st, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, xq, status=status)
+        mark(1)
+        bs.grouped_quantize(case["dy"], st, bs.RECIPE_MX, bs.COLWISE, dq, status=status)
+        mark(2)
+        bs.grouped_quantize(w2, None, bs.RECIPE_MX, bs.ROWWISE, wq)
+        mark(3)
+        bs.grouped_gemm_wgrad(dq, n, xq, h, st, R, bs.RECIPE_MX, dw, accumulate=False, status=status)
+        mark(4)
+        bs.grouped_gemm_fprop(xq, K, wq, N, st, R, fout, bs.OUT_F32, status=status)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    leg_ms = {name: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps for i, name in enumerate(legs)}
+    flop = 2.0 * n * h * T
+    kp_rows = sum(128 * ((k + 127) // 128) for k in splits)
+    wgrad_bytes = (n + h) * kp_rows * (1 + 1 / 32) + 4.0 * n * h * E
+    fprop_bytes = T * K * (1 + 1 / 32) + E * N * K * (1 + 1 / 32) + 4.0 * T * N
+    out = {
+        "metric": METRIC, "value": round(flop / (ms_per_step / 1e3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "moe32_zipf: 32 experts, 65,536 expert rows (Zipf counts, 4 empty), hidden 4096, "
+                               "ffn 1536, capacity padded with garbage rows, MXFP8 1x32 E8M0, wgrad stored fp32, "
+                               "fprop fp32", "experts": E, "expert_rows": T, "capacity_rows": R, "hidden": h,
+                   "ffn": n},
+        "legs": {k: {"us": round(v * 1e3, 1)} for k, v in leg_ms.items()},
+    }
+    out["legs"]["wgrad"].update({"TFLOP/s": round(flop / (leg_ms["wgrad"] / 1e3) / 1e12, 1),
+                                 "algorithmic_GB/s": round(wgrad_bytes / (leg_ms["wgrad"] / 1e3) / 1e9, 1)})
+    out["legs"]["fprop"].update({"TFLOP/s": round(flop / (leg_ms["fprop"] / 1e3) / 1e12, 1),
+                                 "algorithmic_GB/s": round(fprop_bytes / (leg_ms["fprop"] / 1e3) / 1e9, 1)})
+    if args.calibrate_copy_gb > 0:
+        nbytes = int(args.calibrate_copy_gb * 1e9) // 16 * 16
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calibration_copy_bytes"] = nbytes
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,11 +344,17 @@ def main():
     ap.add_argument("--calibrate-copy-gb", type=float, default=0.0,
                     help="after the timed region, run one device copy of this many GB (for counter "
                          "calibration against a kernel of known traffic)")
+    ap.add_argument("--workload", default="moe128_top8", choices=["moe128_top8", "moe32_zipf"],
+                    help="moe128_top8: the headline step and every leg; moe32_zipf: the step on the "
+                         "32-expert shape only (for profiling that shape)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "moe32_zipf":
+        moe32_step_bench(args)
+        return
 
     import torch
 
