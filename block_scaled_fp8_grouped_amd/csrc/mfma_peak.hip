@@ -1,5 +1,6 @@
-// MFMA-only throughput probe (libbsfp8_peak.so): the rate the matrix cores sustain on this
-// machine with nothing else in the loop, to set the grouped GEMMs against.
+// Probe library (libbsfp8_peak.so).  The MFMA-only throughput probe: the rate the matrix cores
+// sustain on this machine with nothing else in the loop, to set the grouped GEMMs against.  And
+// the check of the fast reciprocal that the fused SwiGLU uses against the IEEE division.
 //
 // Each wave holds its A and B operands in registers (read once from the caller's pool) and
 // issues 4 independent accumulator chains of one instruction per iteration; with 2 workgroups
@@ -10,6 +11,7 @@
 #include <stdint.h>
 
 #include "bsfp8_peak.h"
+#include "common.hpp"  // recip_rn, the reciprocal under test
 
 namespace {
 
@@ -71,6 +73,29 @@ __global__ __launch_bounds__(BSFP8_PEAK_THREADS) void mfma_peak_kernel(const uin
   out[t] = s;
 }
 
+// 64 consecutive bit patterns per thread from lo; mismatching patterns are counted and the
+// lowest one kept.
+__global__ __launch_bounds__(256) void recip_check_kernel(uint32_t lo, uint32_t count, unsigned long long* mism,
+                                                          uint32_t* first) {
+  const uint64_t base = ((uint64_t)blockIdx.x * 256 + threadIdx.x) * 64;
+  unsigned long long local = 0;
+  uint32_t low = 0xFFFFFFFFu;
+  for (int i = 0; i < 64; ++i) {
+    const uint64_t j = base + i;
+    if (j >= count) break;
+    const uint32_t bits = lo + (uint32_t)j;
+    const float d = __uint_as_float(bits);
+    if (__float_as_uint(bsfp8::recip_rn(d)) != __float_as_uint(1.0f / d)) {
+      ++local;
+      low = low < bits ? low : bits;
+    }
+  }
+  if (local) {
+    atomicAdd(mism, local);
+    atomicMin(first, low);
+  }
+}
+
 double mfma_flops(int kind) {
   switch (kind) {
     case BSFP8_PEAK_BF16: return 2.0 * 32 * 32 * 16;
@@ -110,4 +135,15 @@ extern "C" int bsfp8_wall_clock_khz(int device) {
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) != hipSuccess) return -1;
   return khz;
+}
+
+extern "C" int bsfp8_recip_check(uint32_t lo_bits, uint32_t hi_bits, unsigned long long* mismatches,
+                                 uint32_t* first_bits, void* stream) {
+  if (mismatches == nullptr || first_bits == nullptr) return -1;
+  if (hi_bits <= lo_bits) return -3;
+  const uint32_t count = hi_bits - lo_bits;
+  const uint64_t blocks = ((uint64_t)count + 64 * 256 - 1) / (64 * 256);
+  hipLaunchKernelGGL(recip_check_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, lo_bits, count,
+                     mismatches, first_bits);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
 }

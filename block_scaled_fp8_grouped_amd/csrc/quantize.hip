@@ -56,8 +56,9 @@ struct ActArgs {
 // exp(r ln 2) (coefficients (ln 2)^n / n! in fp32, Horner order, no fused multiply-add) times 2^k.
 __device__ __forceinline__ float exp2_stated(float x) {
   x = x > 126.0f ? 126.0f : (x < -126.0f ? -126.0f : x);
-  const int k = (int)floorf(x + 0.5f);
-  const float r = x - (float)k;
+  const float kf = floorf(x + 0.5f);  // an integer in [-126, 126]: exact as fp32 and as int
+  const int k = (int)kf;
+  const float r = x - kf;
   float poly = 1.52527338e-05f;
   poly = poly * r + 0.000154035304f;
   poly = poly * r + 0.00133335581f;
@@ -74,6 +75,7 @@ __device__ __forceinline__ float exp2_stated(float x) {
 //   ACT 1: r = max(h, 0) (+0 for h <= 0);  y = (r * r) * p
 //   ACT 2: its gradient                     g = ((2 * r) * p) * dy
 //   ACT 3: sg = 1 / (1 + 2^(-a log2 e)), s = a * sg;  y = (s * b) * p
+// (the division correctly rounded: recip_rn equals it on the [1, 2^126] that 1 + 2^x spans here)
 template <int ACT>
 __device__ __forceinline__ float act_value(float h, float b, float p, float d) {
   if constexpr (ACT <= 2) {
@@ -87,8 +89,8 @@ __device__ __forceinline__ float act_value(float h, float b, float p, float d) {
     }
   } else {
     const float t = exp2_stated(-h * 1.44269502f);
-    const float den = 1.0f + t;
-    const float sg = 1.0f / den;
+    const float den = 1.0f + t;  // in [1, 2^126]: t <= 2^126 after the clamp
+    const float sg = recip_rn(den);
     const float sl = h * sg;
     const float sb = sl * b;
     return sb * p;
@@ -99,8 +101,8 @@ __device__ __forceinline__ float act_value(float h, float b, float p, float d) {
 // (sg and s shared by the two outputs of one element)
 __device__ __forceinline__ void glu_grad(float a, float b, float p, float d, float& da, float& db) {
   const float t = exp2_stated(-a * 1.44269502f);
-  const float den = 1.0f + t;
-  const float sg = 1.0f / den;
+  const float den = 1.0f + t;  // in [1, 2^126]
+  const float sg = recip_rn(den);
   const float sl = a * sg;
   const float q = d * p;
   db = q * sl;

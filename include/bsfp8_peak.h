@@ -1,5 +1,6 @@
 /*
- * bsfp8_peak.h — MFMA-only throughput probe for MI355X (gfx950), built as libbsfp8_peak.so.
+ * bsfp8_peak.h — probes for MI355X (gfx950), built as libbsfp8_peak.so: the MFMA-only
+ * throughput probe, and the exhaustive check of the reciprocal the fused SwiGLU uses.
  *
  * Not part of the quantize / GEMM path.  The grouped-GEMM throughput is quoted as a fraction of
  * the matrix-core peak; the published dense peaks assume the full engine clock, which a chip
@@ -48,6 +49,17 @@ int bsfp8_mfma_peak_probe(int kind, const uint32_t* pool, float* out, int64_t bl
 
 /* Rate of the real-time counter of `device` in kHz (HIP's wall-clock rate), or -1. */
 int bsfp8_wall_clock_khz(int device);
+
+/*
+ * Check of the fast reciprocal the fused SwiGLU quantize uses (hardware reciprocal and one
+ * fused-multiply-add Newton step) against the IEEE-rounded division 1.0f / d, for every fp32
+ * bit pattern d in [lo_bits, hi_bits).  *mismatches (device uint64, zeroed by the caller) is
+ * increased by the number of patterns that differ; *first_bits (device uint32, set to
+ * 0xFFFFFFFF by the caller) is lowered to the smallest differing pattern.
+ * Returns 0, -1 NULL pointer, -3 empty range, -4 the launch failed.
+ */
+int bsfp8_recip_check(uint32_t lo_bits, uint32_t hi_bits, unsigned long long* mismatches, uint32_t* first_bits,
+                      void* stream);
 
 /* Dense FLOPs one probe launch performs (2 M N K per MFMA), or 0 for an invalid kind. */
 double bsfp8_mfma_peak_flops(int kind, int64_t blocks, int64_t iters);

@@ -50,7 +50,7 @@ def _peak_lib():
 def test_probe_library_exports_and_rejects_before_launch():
     L = _peak_lib()
     names = _declared(os.path.join(ROOT, "include", "bsfp8_peak.h"))
-    assert names == ["bsfp8_mfma_peak_flops", "bsfp8_mfma_peak_probe", "bsfp8_wall_clock_khz"]
+    assert names == ["bsfp8_mfma_peak_flops", "bsfp8_mfma_peak_probe", "bsfp8_recip_check", "bsfp8_wall_clock_khz"]
     for n in names:
         assert hasattr(L, n), n
     def probe(kind, pool, out, blocks, iters):
@@ -63,6 +63,10 @@ def test_probe_library_exports_and_rejects_before_launch():
     assert L.bsfp8_mfma_peak_flops(1, 512, 10) == 2 * 32 * 32 * 16 * 4 * 4 * 512 * 10
     assert L.bsfp8_mfma_peak_flops(3, 3, 7) == 2 * 32 * 32 * 64 * 4 * 4 * 3 * 7
     assert L.bsfp8_mfma_peak_flops(5, 3, 7) == 0.0
+    L.bsfp8_recip_check.restype = ctypes.c_int
+    L.bsfp8_recip_check.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.bsfp8_recip_check(1, 5, None, P, None) == -1 and L.bsfp8_recip_check(1, 5, P, None, None) == -1
+    assert L.bsfp8_recip_check(5, 5, P, P, None) == -3 and L.bsfp8_recip_check(6, 5, P, P, None) == -3
 
 
 def test_binding_constants_match_header():

@@ -2,7 +2,8 @@
 every MFMA adds K to each of a lane's 16 accumulators, so each lane's output is
 chains x 16 x K x iters, which fixes K (16 for bf16 32x32x16, 64 for the scaled fp8 and fp4
 32x32x64) and the number of MFMAs the FLOP count assumes; the clock stamps give a shader clock
-within the chip's range."""
+within the chip's range.  And the fast reciprocal of the fused SwiGLU equals the IEEE division
+for every fp32 in [1, 2^126], the range 1 + 2^x takes there (exhaustive, ~1.06e9 patterns)."""
 import ctypes
 import os
 
@@ -60,3 +61,24 @@ def test_probe_counts_its_mfmas(kind):
     assert 0.3 < ghz.median().item() < 3.0
     # the credited FLOPs: 2 * 32 * 32 * K per MFMA, 4 chains per iteration, 4 waves per workgroup
     assert L.bsfp8_mfma_peak_flops(kind, blocks, iters) == 2 * 32 * 32 * K[kind] * 4 * iters * 4 * blocks
+
+
+def test_recip_equals_ieee_division_on_its_domain():
+    flush("recip check")
+    L = _lib()
+    L.bsfp8_recip_check.restype = ctypes.c_int
+    L.bsfp8_recip_check.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for lo, hi, expect_exact in ((0x3F800000, 0x7E800001, True),   # [1, 2^126]
+                                 (0x7E800001, 0x7E800101, False)):  # just above: subnormal 1/d
+        mism = torch.zeros(1, dtype=torch.int64, device=DEV)
+        first = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        assert L.bsfp8_recip_check(lo, hi, mism.data_ptr(), first.data_ptr(), s) == 0
+        torch.cuda.synchronize()
+        n = int(mism.item())
+        flush(f"recip [{lo:#x}, {hi:#x}): {n} mismatches")
+        if expect_exact:
+            assert n == 0, f"first mismatch {int(first.item()) & 0xFFFFFFFF:#x}"
+        else:
+            assert n > 0  # the check does see a difference where there is one
