@@ -170,3 +170,17 @@ def test_swiglu_moe32_shape():
     h = torch.cat([dy, W.randn_bf16(dy.shape, g, DEV, scale=2.0)], dim=1)
     p = torch.rand(R, generator=g, device=DEV)
     _check(bs.ACT_SWIGLU_GRAD, h, dy, p, splits, bs.RECIPE_MX, bs.ROWWISE | bs.COLWISE, "swiglu moe32")
+
+
+@pytest.mark.parametrize("act", [bs.ACT_SRELU, bs.ACT_SWIGLU_GRAD])
+def test_act_quantize_max_groups(act):
+    """1024 groups of 0 to 129 rows (the scan's maximum), both layouts, garbage padding."""
+    rng = np.random.default_rng(33)
+    splits = [int(v) for v in rng.choice([0, 1, 2, 31, 33, 64, 128, 129], size=bs.MAX_GROUPS)]
+    flush(f"act={act} max groups T={sum(splits)}")
+    T = sum(splits)
+    if act == bs.ACT_SWIGLU_GRAD:
+        h, dy, p = _glu_inputs(T + 17, 32, splits, seed=34)
+    else:
+        h, dy, p = _inputs(T + 17, 64, splits, seed=34)
+    _check(act, h, dy, p, splits, bs.RECIPE_MX, bs.ROWWISE | bs.COLWISE, f"act{act} E=1024")

@@ -297,3 +297,23 @@ def test_status_bits_and_no_writes(splits, R, bit):
     bs.grouped_gemm_fprop(q[bs.RECIPE_MX], h, w, n, st, R, fo, bs.OUT_F32, status=status)
     torch.cuda.synchronize()
     assert int(status.item()) == bit and (fo == 5.0).all()
+
+
+def test_max_groups_wgrad_and_fprop():
+    """num_groups at the 1024 maximum: the scan spans two entries per thread of a 512-thread
+    workgroup; empty groups, one-row groups and 128-row groups mixed, garbage padding."""
+    E = bs.MAX_GROUPS
+    rng = np.random.default_rng(1024)
+    splits = [int(v) for v in rng.choice([0, 1, 2, 31, 33, 64, 128, 129], size=E)]
+    T = sum(splits)
+    n = h = 64
+    R = T + 40
+    flush(f"max groups E={E} T={T}")
+    dy, x = _operands(R, n, h, splits, seed=7)
+    for recipe in (bs.RECIPE_MX, bs.RECIPE_PC):
+        check_wgrad(dy, x, splits, recipe, label=f"E={E} r{recipe}")
+    mg = torch.randn(E, n, h, dtype=torch.float32, device=DEV)
+    check_wgrad(dy, x, splits, bs.RECIPE_MX, accumulate=True, mg=mg, label=f"E={E} acc")
+    g = torch.Generator(device=DEV).manual_seed(8)
+    w = W.randn_bf16((E * 64, h), g, DEV)
+    check_fprop(x, w, splits, 64, bs.OUT_F32, label=f"E={E} fprop")
