@@ -334,8 +334,8 @@ def moe32_step_bench(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-experts", type=int, default=3,
                     help="experts in the CPU-baseline sample (0 skips it)")
     ap.add_argument("--cpu-channels", type=int, default=2048, help="dy channels per sampled expert")
