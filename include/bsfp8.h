@@ -170,10 +170,12 @@ int bsfp8_grouped_quantize(const void* in_bf16, int64_t capacity_rows, int64_t c
  *   form, times 2^k (relative error below 3e-7; reproducible bit for bit on any IEEE machine).
  * probs      device fp32 [capacity_rows]: the token's routing probability p, or NULL for p = 1.
  * Every operation is rounded to fp32 in the order written (no fused multiply-add); division is
- * correctly rounded.  The fp32 values of the live rows are quantized as
- *             bsfp8_grouped_quantize quantizes a bf16 input, for recipe
- *             BSFP8_RECIPE_MX_1X32_E8M0 or BSFP8_RECIPE_MXFP4_1X32_E8M0, into the same layouts
- *             (rowwise for the next GEMM's forward, colwise for its weight gradient).
+ * correctly rounded.  The fp32 values of the live rows are quantized the way
+ * bsfp8_grouped_quantize quantizes a bf16 input, for recipe BSFP8_RECIPE_MX_1X32_E8M0 or
+ * BSFP8_RECIPE_MXFP4_1X32_E8M0, into the same layouts (rowwise for the next GEMM's forward,
+ * colwise for its weight gradient), sized by the size queries for the output's shape:
+ * [capacity_rows][cols] (SReLU), [capacity_rows][F] (SwiGLU) or [capacity_rows][2F] (its
+ * gradient).
  * split_sizes is required; rows at or past sum(split_sizes) (of h, dy and probs) are never read.
  * Outputs, status and errors as bsfp8_grouped_quantize; capacity_rows == 0 returns BSFP8_OK
  * without touching any pointer.
