@@ -1,0 +1,40 @@
+"""bench.py end to end on the GPU, cut to one step and a tiny CPU sample: it prints exactly one JSON
+line on stdout with the fields and types its contract names (the headline metric, the roofline
+object of the wgrad kernel, the CPU-oracle baseline), and the figures are consistent."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from gpu_util import flush
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_prints_one_contract_line():
+    flush("bench.py one step")
+    cmd = [sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "1", "--warmup", "1", "--no-graph",
+           "--no-mxfp4", "--cpu-experts", "1", "--cpu-channels", "64"]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=900, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout
+    d = json.loads(lines[0])
+    for k, t in (("metric", str), ("value", float), ("unit", str), ("n_gpus", int), ("steps", int),
+                 ("warmup", int), ("ms_per_step", float), ("higher_is_better", bool), ("scaling", str),
+                 ("dtype", str), ("data", str), ("config", dict), ("roofline", dict), ("cpu_baseline", dict)):
+        assert isinstance(d[k], t), (k, d.get(k))
+    assert d["n_gpus"] == 1 and d["steps"] == 1 and d["warmup"] == 1 and d["unit"] == "TFLOP/s"
+    assert d["vs_baseline"] is None and "workload" in d["config"]
+    rf = d["roofline"]
+    assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 2500.0
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    assert rf["traffic"] is None or rf["traffic"] > 0
+    # value counts the whole step, so it cannot exceed the wgrad kernel's own rate
+    assert 0 < d["value"] <= rf["achieved"]
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["cores"] >= 1 and cb["value"] > 0
+    assert isinstance(cb["sample"], str) and cb["sample"]
