@@ -92,7 +92,7 @@ def cpu_baseline(case, experts, channels):
     picked = live[mid:mid + experts]
     rows = np.arange(channels, dtype=np.int32)
     offs = np.concatenate([[0], np.cumsum(splits)])
-    flops, dt = 0.0, 0.0
+    flops, dt, qt, qbytes = 0.0, 0.0, 0.0, 0.0
     for k, e in picked:
         off = int(offs[e])
         dy = W.bf16_bits(case["dy"][off:off + k])
@@ -100,18 +100,23 @@ def cpu_baseline(case, experts, channels):
         t0 = time.perf_counter()
         oq_dy = oracle.grouped_quantize(dy, [k], oracle.RECIPE_MX, oracle.COLWISE)
         oq_x = oracle.grouped_quantize(x, [k], oracle.RECIPE_MX, oracle.COLWISE)
+        t1 = time.perf_counter()
         oracle.grouped_wgrad(oq_dy["col_q"], oq_dy["col_s"], n, oq_x["col_q"], oq_x["col_s"], h, [k], k,
                              oracle.RECIPE_MX, rows_sel=rows)
         dt += time.perf_counter() - t0
+        qt += t1 - t0
         flops += 2.0 * channels * h * k
+        kp = 128 * ((k + 127) // 128)
+        qbytes += (n + h) * (2.0 * k + kp * (1 + 1 / 32))  # bf16 read, colwise e4m3 + E8M0 written
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
+        "quantize_GB/s": round(qbytes / qt / 1e9, 2),
         "sample": f"experts {[e for _, e in picked]} ({[k for k, _ in picked]} rows): colwise quantize of their "
-                  f"dy and x rows, then fp64 wgrad of {channels} of {n} dy channels x all {h} x channels "
-                  f"({flops / 1e9:.0f} GFLOP useful) in {dt:.1f} s",
+                  f"dy and x rows ({qt:.1f} s), then fp64 wgrad of {channels} of {n} dy channels x all {h} x "
+                  f"channels ({flops / 1e9:.0f} GFLOP useful); {dt:.1f} s in all",
     }
 
 
