@@ -1,6 +1,8 @@
 // Probe library (libbsfp8_peak.so).  The MFMA-only throughput probe: the rate the matrix cores
-// sustain on this machine with nothing else in the loop, to set the grouped GEMMs against.  And
-// the check of the fast reciprocal that the fused SwiGLU uses against the IEEE division.
+// sustain on this machine with nothing else in the loop, to set the grouped GEMMs against.  The
+// precision probe: one 32 x 32 block-scaled e4m3 dot product through each candidate matrix
+// instruction, which shows why the MXFP8 GEMMs run the bf16 MFMA on widened codes.  And the
+// check of the fast reciprocal that the fused SwiGLU uses against the IEEE division.
 //
 // Each wave holds its A and B operands in registers (read once from the caller's pool) and
 // issues 4 independent accumulator chains of one instruction per iteration; with 2 workgroups
@@ -19,6 +21,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kChains = 4;
 
@@ -96,6 +101,99 @@ __global__ __launch_bounds__(256) void recip_check_kernel(uint32_t lo, uint32_t 
   }
 }
 
+// Eight e4m3 codes -> eight bf16 values times `scale` (exact: 4 significant bits).
+__device__ __forceinline__ v8bf widen8(v2i d, float scale) {
+  const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d[0], scale, false);
+  const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d[0], scale, true);
+  const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d[1], scale, false);
+  const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d[1], scale, true);
+  return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Two 16-byte pieces, `gap` bytes apart, as one 8-register operand.
+__device__ __forceinline__ v8i halves(const uint8_t* p, int gap) {
+  const v4i lo = *(const v4i*)p, hi = *(const v4i*)(p + gap);
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// One wave computes C[i][j] = sum_t A[i][t] B[j][t] for 32 x 32 outputs over k e4m3 values per row
+// with one matrix instruction, each operand given as 32 rows of k codes and E8M0 scales per 32
+// along k (block b of row r at b * 32 + r).  KIND picks the instruction (BSFP8_DOT_*):
+//  - BF16: every code widened to bf16 with its block scale folded in (exact), then the bf16 MFMA
+//    32x32x16; lane l supplies row l % 32 and the 8 values [k0 + 8 (l / 32), +8) of a K=16 step;
+//  - FP8_32X32X64: the scaled MFMA with e4m3 operands.  Lane l = 32 h + r supplies row r of a K=64
+//    step as two 16-code halves, [k0 + 16 h, +16) in its first four registers and
+//    [k0 + 32 + 16 h, +16) in the last four, and the scale byte of block h of the step
+//    ([k0 + 32 h, +32)): the codes of one scale block are split over the lane pair (r, r + 32).
+//    (Measured: with each lane holding one whole block instead, blocks get each other's scales.)
+//  - FP8_16X16X128: the same at 16 x 16 x 128: lane l = 16 q + r supplies row r as
+//    [k0 + 16 q, +16) and [k0 + 64 + 16 q, +16), and the scale of block q; four output tiles;
+//  - FP8_LEGACY: the unscaled fp8 MFMA 32x32x16 (lane l: row l % 32, codes [k0 + 8 (l / 32), +8));
+//    the scales are not applied.
+// A 32 x 32 fp32 result of the 32 x 32 forms: lane l holds column l % 32, its element r row
+// 8 (r / 4) + 4 (l / 32) + r % 4; of the 16 x 16 form: column l % 16, element r row 4 (l / 16) + r.
+template <int KIND>
+__global__ __launch_bounds__(64) void mfma_dot_kernel(const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_s,
+                                                      const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_s,
+                                                      int k, float* __restrict__ out) {
+  const int lane = threadIdx.x;
+  if constexpr (KIND == BSFP8_DOT_FP8_16X16X128) {
+    const int r = lane & 15, q = lane >> 4;
+    v4f acc[2][2] = {};
+    for (int k0 = 0; k0 < k; k0 += 128) {
+      const int kk = k0 + 32 * q;
+      v8i a[2], b[2];
+      int sa[2], sb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        a[t] = halves(a_q + (int64_t)(16 * t + r) * k + k0 + 16 * q, 64);
+        b[t] = halves(b_q + (int64_t)(16 * t + r) * k + k0 + 16 * q, 64);
+        sa[t] = a_s[(kk / 32) * 32 + 16 * t + r];
+        sb[t] = b_s[(kk / 32) * 32 + 16 * t + r];
+      }
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj)
+          acc[ti][tj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[ti], b[tj], acc[ti][tj], 0, 0, 0, sa[ti], 0,
+                                                                         sb[tj]);
+    }
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[(16 * ti + 4 * q + e) * 32 + 16 * tj + r] = acc[ti][tj][e];
+  } else {
+    const int r = lane & 31, h = lane >> 5;
+    v16f acc = {};
+    if constexpr (KIND == BSFP8_DOT_FP8_32X32X64) {
+      for (int k0 = 0; k0 < k; k0 += 64) {
+        const int kk = k0 + 32 * h;
+        const v8i a = halves(a_q + (int64_t)r * k + k0 + 16 * h, 32);
+        const v8i b = halves(b_q + (int64_t)r * k + k0 + 16 * h, 32);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, a_s[(kk / 32) * 32 + r], 0,
+                                                              b_s[(kk / 32) * 32 + r]);
+      }
+    } else {
+      for (int k0 = 0; k0 < k; k0 += 16) {
+        const int kk = k0 + 8 * h;
+        const v2i a = *(const v2i*)(a_q + (int64_t)r * k + kk), b = *(const v2i*)(b_q + (int64_t)r * k + kk);
+        if constexpr (KIND == BSFP8_DOT_FP8_LEGACY) {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b), acc,
+                                                           0, 0, 0);
+        } else {
+          const float fa = __uint_as_float(max((uint32_t)a_s[(kk / 32) * 32 + r] << 23, 0x00400000u));
+          const float fb = __uint_as_float(max((uint32_t)b_s[(kk / 32) * 32 + r] << 23, 0x00400000u));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen8(a, fa), widen8(b, fb), acc, 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) out[(8 * (e / 4) + 4 * h + e % 4) * 32 + r] = acc[e];
+  }
+}
+
 double mfma_flops(int kind) {
   switch (kind) {
     case BSFP8_PEAK_BF16: return 2.0 * 32 * 32 * 16;
@@ -135,6 +233,31 @@ extern "C" int bsfp8_wall_clock_khz(int device) {
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) != hipSuccess) return -1;
   return khz;
+}
+
+extern "C" int bsfp8_mfma_dot_probe(int kind, const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q,
+                                    const uint8_t* b_s, int64_t k, float* out, void* stream) {
+  if (a_q == nullptr || a_s == nullptr || b_q == nullptr || b_s == nullptr || out == nullptr) return -1;
+  if (kind < BSFP8_DOT_BF16 || kind > BSFP8_DOT_FP8_LEGACY) return -2;
+  if (k < 128 || k > 65536 || k % 128 != 0) return -3;
+  if (((uintptr_t)a_q | (uintptr_t)b_q) % 32 != 0) return -5;
+  hipStream_t s = (hipStream_t)stream;
+  const int kk = (int)k;
+  switch (kind) {
+    case BSFP8_DOT_BF16:
+      hipLaunchKernelGGL(mfma_dot_kernel<BSFP8_DOT_BF16>, dim3(1), dim3(64), 0, s, a_q, a_s, b_q, b_s, kk, out);
+      break;
+    case BSFP8_DOT_FP8_32X32X64:
+      hipLaunchKernelGGL(mfma_dot_kernel<BSFP8_DOT_FP8_32X32X64>, dim3(1), dim3(64), 0, s, a_q, a_s, b_q, b_s, kk, out);
+      break;
+    case BSFP8_DOT_FP8_16X16X128:
+      hipLaunchKernelGGL(mfma_dot_kernel<BSFP8_DOT_FP8_16X16X128>, dim3(1), dim3(64), 0, s, a_q, a_s, b_q, b_s, kk,
+                         out);
+      break;
+    default:
+      hipLaunchKernelGGL(mfma_dot_kernel<BSFP8_DOT_FP8_LEGACY>, dim3(1), dim3(64), 0, s, a_q, a_s, b_q, b_s, kk, out);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 extern "C" int bsfp8_recip_check(uint32_t lo_bits, uint32_t hi_bits, unsigned long long* mismatches,

@@ -1,6 +1,7 @@
 /*
  * bsfp8_peak.h — probes for MI355X (gfx950), built as libbsfp8_peak.so: the MFMA-only
- * throughput probe, and the exhaustive check of the reciprocal the fused SwiGLU uses.
+ * throughput probe, the matrix-instruction precision probe, and the exhaustive check of the
+ * reciprocal the fused SwiGLU uses.
  *
  * Not part of the quantize / GEMM path.  The grouped-GEMM throughput is quoted as a fraction of
  * the matrix-core peak; the published dense peaks assume the full engine clock, which a chip
@@ -46,6 +47,31 @@ extern "C" {
  */
 int bsfp8_mfma_peak_probe(int kind, const uint32_t* pool, float* out, int64_t blocks, int64_t iters,
                           uint64_t* stamps, void* stream);
+
+/* Instruction of a precision-probe launch (bsfp8_mfma_dot_probe). */
+#define BSFP8_DOT_BF16 1           /* codes widened to bf16 with the block scale, v_mfma_f32_32x32x16_bf16 */
+#define BSFP8_DOT_FP8_32X32X64 2   /* v_mfma_scale_f32_32x32x64_f8f6f4, e4m3, E8M0 scales in the instruction */
+#define BSFP8_DOT_FP8_16X16X128 3  /* v_mfma_scale_f32_16x16x128_f8f6f4, e4m3, E8M0 scales in the instruction */
+#define BSFP8_DOT_FP8_LEGACY 4     /* v_mfma_f32_32x32x16_fp8_fp8 (unscaled; the scales are ignored) */
+
+/*
+ * Precision probe: the block-scaled e4m3 product C[i][j] = sum_t deq(A)[i][t] deq(B)[j][t] for
+ * i, j < 32, computed by one wave with the instruction `kind` and fp32 accumulation across
+ * instructions.  It exists to measure how exactly each matrix instruction sums products
+ * (MXFP8 block scaling: TransformerEngine issue #3484, "NaN expert weight gradients at
+ * num_groups == 1 with a padded token buffer for SReLU", reproducer; the FP8 k-grouped GEMM
+ * of DeepGEMM issue #365, "Non-deterministic numerical problem of
+ * k_grouped_fp8_gemm_nt_contiguous", reproducer call).
+ *   a_q, b_q  e4m3 codes [32][k] row-major (32-byte aligned device pointers);
+ *   a_s, b_s  E8M0 scale bytes [k / 32][32]: block b of row r at b * 32 + r (the rowwise scale
+ *             layout of bsfp8_grouped_quantize for 32 rows); kind FP8_LEGACY ignores them;
+ *   k         values per row, a multiple of 128 in [128, 65536];
+ *   out       fp32 [32][32] row-major, C[i][j] at i * 32 + j.
+ * One workgroup of one wave, asynchronous on `stream`.  Returns 0, or -1 NULL pointer, -2 kind,
+ * -3 k out of range, -4 the launch failed, -5 a code pointer not 32-byte aligned.
+ */
+int bsfp8_mfma_dot_probe(int kind, const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
+                         int64_t k, float* out, void* stream);
 
 /* Rate of the real-time counter of `device` in kHz (HIP's wall-clock rate), or -1. */
 int bsfp8_wall_clock_khz(int device);

@@ -50,7 +50,8 @@ def _peak_lib():
 def test_probe_library_exports_and_rejects_before_launch():
     L = _peak_lib()
     names = _declared(os.path.join(ROOT, "include", "bsfp8_peak.h"))
-    assert names == ["bsfp8_mfma_peak_flops", "bsfp8_mfma_peak_probe", "bsfp8_recip_check", "bsfp8_wall_clock_khz"]
+    assert names == ["bsfp8_mfma_dot_probe", "bsfp8_mfma_peak_flops", "bsfp8_mfma_peak_probe", "bsfp8_recip_check",
+                     "bsfp8_wall_clock_khz"]
     for n in names:
         assert hasattr(L, n), n
     def probe(kind, pool, out, blocks, iters):
@@ -67,6 +68,19 @@ def test_probe_library_exports_and_rejects_before_launch():
     L.bsfp8_recip_check.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     assert L.bsfp8_recip_check(1, 5, None, P, None) == -1 and L.bsfp8_recip_check(1, 5, P, None, None) == -1
     assert L.bsfp8_recip_check(5, 5, P, P, None) == -3 and L.bsfp8_recip_check(6, 5, P, P, None) == -3
+    L.bsfp8_mfma_dot_probe.restype = ctypes.c_int
+    L.bsfp8_mfma_dot_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+
+    def dot(kind=1, aq=P, as_=P, bq=P, bs_=P, k=128, out=P):
+        return L.bsfp8_mfma_dot_probe(kind, aq, as_, bq, bs_, k, out, None)
+    for i in range(5):
+        args = [P] * 5
+        args[i] = None
+        assert dot(1, args[0], args[1], args[2], args[3], 128, args[4]) == -1
+    assert dot(kind=0) == -2 and dot(kind=5) == -2
+    assert dot(k=64) == -3 and dot(k=192) == -3 and dot(k=65536 + 128) == -3
+    assert dot(aq=P + 16) == -5 and dot(bq=P + 8) == -5
 
 
 def test_binding_constants_match_header():
