@@ -1,4 +1,5 @@
-"""Determinism stress from the DeepGEMM #365 reproducer: the 2048 x 2048, four-expert wgrad
+"""Determinism stress from the DeepGEMM #365 reproducer (its stress test; the root-cause comment
+traces the blow-ups to a race condition inside the GEMM kernel): the 2048 x 2048, four-expert wgrad
 (one all-zero dy channel in each 128-token expert) called 10,000 times on operands cast once,
 for each zero-channel scale in the page's sweep (1, 1e-4, 1e-8, 1e-30).  Every call must be
 bitwise equal to the first, and no call may show the page's blow-up criterion (an expert's
@@ -50,3 +51,77 @@ def test_wgrad_10000_calls_bitwise(sf_val):
     assert np.all(norms <= np.maximum(100 * np.array(ref_norms), 1.0))
     # the zeroed channel gives an exact zero row in the 128-token experts
     assert (first[1, 0] == 0).all() and (first[2, 0] == 0).all()
+
+
+# The same stress on the pipelined block-scaled kernels: the 256 x 256, 8-wave MXFP8 GEMM (next K
+# step's DMA issued in the middle of the current one, E8M0 scales decoded in LDS) and the MXFP4 GEMM
+# (its LDS DMAs issued as inline assembly with hand-placed waits), on the same four-expert 2048 x 2048
+# shape with one all-zero dy channel in each 128-token expert.  wgrad in store mode, wgrad
+# accumulating into a main_grad reset to the same fp32 contents before every call, and the m-grouped
+# forward (fp32 and bf16 out) on a four-expert weight.  Every call must be bitwise equal to the first;
+# the loop counts mismatching calls on the device and reports every 2,500 calls.
+def _stress(run, out, label):
+    run()
+    torch.cuda.synchronize()
+    first = out.clone()
+    assert torch.isfinite(first.float()).all(), label
+    mismatched = torch.zeros((), dtype=torch.int64, device=DEV)
+    bits = torch.int16 if out.dtype == torch.bfloat16 else torch.int32
+    for it in range(ITERS):
+        run()
+        mismatched += torch.ne(out.view(bits), first.view(bits)).any().to(torch.int64)
+        if (it + 1) % 2500 == 0:
+            torch.cuda.synchronize()
+            flush(f"{label}: {it + 1} calls, mismatched={int(mismatched)}")
+            assert int(mismatched) == 0, label
+    torch.cuda.synchronize()
+    assert int(mismatched) == 0, label
+    return first
+
+
+@pytest.mark.parametrize("recipe,accumulate", [(bs.RECIPE_MX, False), (bs.RECIPE_MX, True),
+                                               (bs.RECIPE_MX4, False), (bs.RECIPE_MX4, True)])
+def test_block_scaled_wgrad_10000_calls_bitwise(recipe, accumulate):
+    case = W.deepgemm_case(DEV, 2048, 2048)
+    splits, n, h, R = case["splits"], case["n"], case["h"], case["R"]
+    E = len(splits)
+    st = W.splits_tensor(splits, DEV)
+    dq = gpu_quantize(case["dy"], splits, recipe, bs.COLWISE)
+    xq = gpu_quantize(case["x"], splits, recipe, bs.COLWISE)
+    out = torch.empty(E, n, h, dtype=torch.float32, device=DEV)
+    mg0 = torch.randn(E, n, h, generator=torch.Generator(device=DEV).manual_seed(7), device=DEV)
+
+    def run():
+        if accumulate:
+            out.copy_(mg0)
+        else:
+            out.fill_(float("nan"))
+        bs.grouped_gemm_wgrad(dq, n, xq, h, st, R, recipe, out, accumulate=accumulate)
+
+    label = f"wgrad recipe={recipe} accumulate={accumulate}"
+    flush(label)
+    first = _stress(run, out, label)
+    # the zeroed channel gives an exact zero row (store) or leaves main_grad's row as it was
+    for e in (1, 2):
+        assert torch.equal(first[e, 0], mg0[e, 0] if accumulate else torch.zeros_like(first[e, 0]))
+
+
+@pytest.mark.parametrize("recipe,out_dtype", [(bs.RECIPE_MX, bs.OUT_F32), (bs.RECIPE_MX, bs.OUT_BF16),
+                                              (bs.RECIPE_MX4, bs.OUT_BF16)])
+def test_block_scaled_fprop_10000_calls_bitwise(recipe, out_dtype):
+    case = W.deepgemm_case(DEV, 2048, 2048)
+    splits, K, R = case["splits"], case["h"], case["R"]
+    E, N = len(splits), 2048
+    st = W.splits_tensor(splits, DEV)
+    xq = gpu_quantize(case["x"], splits, recipe, bs.ROWWISE)
+    w = W.randn_bf16((E * N, K), torch.Generator(device=DEV).manual_seed(8), DEV)
+    wq = gpu_quantize(w, None, recipe, bs.ROWWISE)
+    out = torch.empty(R, N, dtype=torch.float32 if out_dtype == bs.OUT_F32 else torch.bfloat16, device=DEV)
+
+    def run():
+        out.fill_(float("nan"))
+        bs.grouped_gemm_fprop(xq, K, wq, N, st, R, out, out_dtype, recipe=recipe)
+
+    label = f"fprop recipe={recipe} out_dtype={out_dtype}"
+    flush(label)
+    _stress(run, out, label)
