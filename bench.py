@@ -18,9 +18,11 @@ Reported (one JSON line on stdout):
               (quantize and fprop time included, so this is a lower bound of the wgrad kernel's
               own rate, which the roofline object reports).
   roofline    the wgrad kernel: achieved = useful FLOP / its mean duration (HIP events on the
-              launch stream inside the timed region), against the bf16 MFMA peak the kernel
-              runs on; `traffic` is the HBM bytes per launch measured with rocprofv3 counters
-              when the committed measurement matches the current kernel source, else null.
+              launch stream inside the timed region), against the dense FP8 MFMA peak the
+              metric names (5.0 PFLOP/s; the fraction of the bf16 peak the kernel's instruction
+              runs at is reported beside it); `traffic` is the L2-to-fabric bytes per launch
+              measured with rocprofv3 counters when the committed measurement matches the
+              current kernel source, else null.
   legs        mean duration and rate of every kernel of the step.
   graph       the step captured once in a HIP graph and replayed, with the weight quantize run
               and with it skipped on the device by its noop flag (a cached-weight microbatch).
@@ -44,7 +46,7 @@ if ROOT not in sys.path:
 
 METRIC = "grouped FP8 wgrad TFLOP/s (useful FLOPs) and % of FP8 MFMA peak, 1 GPU"
 PEAK_BF16_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (the instruction the GEMMs run on)
-PEAK_FP8_MFMA_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_FP8_MFMA_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (the metric's peak)
 PEAK_FP4_MFMA_TFLOPS = 10100.0   # MI355X dense fp4 MFMA (the MXFP4 GEMMs run on it)
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wgrad_moe128_traffic.json")
@@ -571,12 +573,16 @@ def main():
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 1),
-            "peak": PEAK_BF16_MFMA_TFLOPS,
+            "peak": PEAK_FP8_MFMA_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_MFMA_TFLOPS, 4),
+            "frac": round(achieved / PEAK_FP8_MFMA_TFLOPS, 4),
             "traffic": traffic,
+            "traffic_note": "L2-to-fabric bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated): an upper bound "
+                            "of HBM bytes, since reads the MALL serves are counted too",
             "kernel": "grouped_gemm_kernel<wgrad, MX, 256x256, accumulate>",
-            "frac_of_fp8_peak": round(achieved / PEAK_FP8_MFMA_TFLOPS, 4),
+            "instruction": "v_mfma_f32_32x32x16_bf16 on exactly widened e4m3 (the scaled fp8 MFMA "
+                           "truncates inside 8-product groups; see the fp8 precision probe)",
+            "frac_of_bf16_peak": round(achieved / PEAK_BF16_MFMA_TFLOPS, 4),
         },
         "event_ms_per_step": round(event_ms_per_step, 3),
         "legs": {

@@ -30,7 +30,8 @@ def test_bench_prints_one_contract_line():
     assert d["n_gpus"] == 1 and d["steps"] == 1 and d["warmup"] == 1 and d["unit"] == "TFLOP/s"
     assert d["vs_baseline"] is None and "workload" in d["config"]
     rf = d["roofline"]
-    assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 2500.0
+    assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 5000.0  # the FP8 MFMA peak
+    assert abs(rf["frac_of_bf16_peak"] - rf["achieved"] / 2500.0) < 1e-3
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     assert rf["traffic"] is None or rf["traffic"] > 0
     # value counts the whole step, so it cannot exceed the wgrad kernel's own rate
