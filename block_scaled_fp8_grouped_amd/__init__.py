@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libbsfp8.so")
 RECIPE_MX = 1  # BSFP8_RECIPE_MX_1X32_E8M0
 RECIPE_PC = 2  # BSFP8_RECIPE_PER_CHANNEL_128_F32
 RECIPE_MX4 = 3  # BSFP8_RECIPE_MXFP4_1X32_E8M0
+GEMM_FP8_MFMA = 0x100  # BSFP8_GEMM_FP8_MFMA: OR into RECIPE_MX for the GEMMs on the scaled fp8 MFMA
 ROWWISE = 1
 COLWISE = 2
 ACT_SRELU = 1  # BSFP8_ACT_SRELU: y = p * max(h, 0)^2
@@ -199,7 +200,8 @@ def grouped_act_quantize(activation, h, split_sizes, recipe, which, out, probs=N
 def grouped_gemm_wgrad(dy_q, n, x_q, h, split_sizes, capacity_rows, recipe, out, accumulate=False, status=None,
                        stream=None):
     """bsfp8_grouped_gemm_wgrad: dy_q / x_q are the colwise dicts of grouped_quantize; out is
-    fp32 [E, n, h] (overwritten, or accumulated into with ``accumulate``)."""
+    fp32 [E, n, h] (overwritten, or accumulated into with ``accumulate``).  recipe: the data
+    recipe, or RECIPE_MX | GEMM_FP8_MFMA for the MXFP8 operands on the scaled fp8 MFMA."""
     E = int(split_sizes.numel())
     rc = lib().bsfp8_grouped_gemm_wgrad(_ptr(dy_q["col_q"]), _ptr(dy_q["col_s"]), n, _ptr(x_q["col_q"]),
                                         _ptr(x_q["col_s"]), h, _ptr(split_sizes), E, capacity_rows, recipe,
@@ -211,7 +213,8 @@ def grouped_gemm_wgrad(dy_q, n, x_q, h, split_sizes, capacity_rows, recipe, out,
 def grouped_gemm_fprop(x_q, k, w_q, n, split_sizes, capacity_rows, out, out_dtype=OUT_F32, status=None,
                        stream=None, recipe=RECIPE_MX):
     """bsfp8_grouped_gemm_fprop: x_q is the rowwise dict of x [R, k], w_q the rowwise dict of the
-    weight [E*n, k], both of ``recipe`` (MX or MX4); out is [R, n] fp32 or bf16 (rows past
+    weight [E*n, k], both of ``recipe`` (MX or MX4; RECIPE_MX | GEMM_FP8_MFMA multiplies MX
+    operands on the scaled fp8 MFMA); out is [R, n] fp32 or bf16 (rows past
     sum(split_sizes) untouched)."""
     E = int(split_sizes.numel())
     rc = lib().bsfp8_grouped_gemm_fprop(_ptr(x_q["row_q"]), _ptr(x_q["row_s"]), capacity_rows, k,

@@ -35,6 +35,9 @@ bool valid_recipe(int r) {
 }
 // recipes with E8M0 block scales (both layouts; the only ones the m-grouped GEMMs take)
 bool mx_recipe(int r) { return r == BSFP8_RECIPE_MX_1X32_E8M0 || r == BSFP8_RECIPE_MXFP4_1X32_E8M0; }
+// the recipe argument of the GEMM calls: a data recipe, or MXFP8 on the scaled fp8 MFMA
+bool wgrad_recipe(int r) { return valid_recipe(r) || r == (BSFP8_RECIPE_MX_1X32_E8M0 | BSFP8_GEMM_FP8_MFMA); }
+bool mgrouped_recipe(int r) { return mx_recipe(r) || r == (BSFP8_RECIPE_MX_1X32_E8M0 | BSFP8_GEMM_FP8_MFMA); }
 // data elements per byte
 int64_t per_byte(int r) { return r == BSFP8_RECIPE_MXFP4_1X32_E8M0 ? 2 : 1; }
 bool valid_groups(int32_t e) { return e > 0 && e <= BSFP8_MAX_GROUPS; }
@@ -139,7 +142,7 @@ int bsfp8_grouped_gemm_wgrad(const uint8_t* dy_col_q, const void* dy_col_s, int6
                              const void* x_col_s, int64_t h, const int32_t* split_sizes, int32_t num_groups,
                              int64_t capacity_rows, int recipe, float* out, int accumulate, uint32_t* status,
                              void* stream) {
-  if (!valid_recipe(recipe)) return BSFP8_ERR_RECIPE;
+  if (!wgrad_recipe(recipe)) return BSFP8_ERR_RECIPE;
   if (!valid_groups(num_groups)) return BSFP8_ERR_NUM_GROUPS;
   if (!valid_dim(n) || !valid_dim(h) || capacity_rows < 0) return BSFP8_ERR_SHAPE;
   if (capacity_rows + 127 > kMaxKExtent || h > kMaxOutCols) return BSFP8_ERR_SHAPE;
@@ -159,7 +162,7 @@ int bsfp8_grouped_gemm_fprop(const uint8_t* x_row_q, const uint8_t* x_row_s, int
                              const uint8_t* w_q, const uint8_t* w_s, int64_t n, const int32_t* split_sizes,
                              int32_t num_groups, int recipe, void* out, int out_dtype, uint32_t* status,
                              void* stream) {
-  if (!mx_recipe(recipe)) return BSFP8_ERR_RECIPE;
+  if (!mgrouped_recipe(recipe)) return BSFP8_ERR_RECIPE;
   if (!valid_groups(num_groups)) return BSFP8_ERR_NUM_GROUPS;
   if (!valid_dim(k) || !valid_dim(n) || capacity_rows < 0 || k > kMaxKExtent || n > kMaxOutCols)
     return BSFP8_ERR_SHAPE;
@@ -179,7 +182,7 @@ int bsfp8_grouped_gemm_dgrad(const uint8_t* dy_row_q, const uint8_t* dy_row_s, i
                              const uint8_t* w_col_q, const void* w_col_s, int64_t k, const int32_t* split_sizes,
                              int32_t num_groups, int recipe, void* out, int out_dtype, uint32_t* status,
                              void* stream) {
-  if (!mx_recipe(recipe)) return BSFP8_ERR_RECIPE;
+  if (!mgrouped_recipe(recipe)) return BSFP8_ERR_RECIPE;
   if (!valid_groups(num_groups)) return BSFP8_ERR_NUM_GROUPS;
   // the weight rows are n rounded up to 128: that padded length bounds the 32-bit tile offsets
   if (!valid_dim(n) || !valid_dim(k) || capacity_rows < 0 || n + 127 > kMaxKExtent || k > kMaxOutCols)

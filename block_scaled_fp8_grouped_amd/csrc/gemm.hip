@@ -48,6 +48,10 @@
 namespace bsfp8 {
 
 enum { kModeWgrad = 0, kModeFprop = 1 };
+// Arithmetic of an MX GEMM: kFmtBf16 widens e4m3 codes to bf16 with the block scale folded in and
+// runs the bf16 MFMA (also the per-channel recipe's path); kFmtF4 and kFmtF8 hand e2m1 / e4m3
+// codes and their E8M0 bytes to the scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4).
+enum { kFmtBf16 = 0, kFmtF4 = 1, kFmtF8 = 2 };
 
 struct GemmArgs {
   const uint8_t* a_q;  // wgrad: dy colwise   fprop: x rowwise
@@ -128,35 +132,37 @@ __device__ __forceinline__ v8bf widen8(int d0, int d1, float scale) {
   return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-template <int MODE, bool PC, bool F4, int BM, int BN, int WM, int WN>
+template <int MODE, bool PC, int FMT, int BM, int BN, int WM, int WN>
 struct GemmShape {
   static constexpr int BK = 128;                    // bytes of a row per K step
-  static constexpr int SBLK = F4 ? 8 : 4;           // E8M0 scale blocks per K step (MX recipes)
+  static constexpr int SBLK = FMT == kFmtF4 ? 8 : 4;  // E8M0 scale blocks per K step (MX recipes)
   static constexpr int BLK_BYTES = BK / SBLK;       // bytes of one scale block
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int NW = WAVES_M * WAVES_N, NT = NW * 64;
   static constexpr int FM = WM / 32, FN = WN / 32;
   // LDS stage: A rows, B rows, then scales (MX: [SBLK blocks][rows] E8M0 bytes as they arrive,
-  // and for MXFP8 the same decoded to fp32 [4 blocks][rows]; PC: one fp32 per row)
+  // and for the widened MXFP8 path the same decoded to fp32 [4 blocks][rows]; PC: one fp32 per row)
   static constexpr int A_OFF = 0, B_OFF = BM * BK, SA_OFF = (BM + BN) * BK;
   static constexpr int SB_OFF = SA_OFF + (PC ? BM * 4 : SBLK * BM);
   static constexpr int SAF_OFF = SB_OFF + (PC ? BN * 4 : SBLK * BN), SBF_OFF = SAF_OFF + 16 * BM;
-  static constexpr int STAGE = (PC || F4) ? SAF_OFF : SBF_OFF + 16 * BN;
+  static constexpr int STAGE = (PC || FMT != kFmtBf16) ? SAF_OFF : SBF_OFF + 16 * BN;
   static constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;  // 1 KB DMA instructions per wave
   static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
   static_assert(A_INS * 8 * NW == BM && B_INS * 8 * NW == BN, "DMA loader shape");
   static_assert(2 * STAGE + (int)sizeof(GroupScanSmem<NT>) <= 160 * 1024, "LDS budget");
 };
 
-// KTAIL (MXFP8 fprop only): K is not a multiple of 128, so the last K step runs past it.  MXFP4
-// (F4) decides per group at run time whether its last K step is such a tail step.
-template <int MODE, bool PC, bool F4, int BM, int BN, int WM, int WN, bool ACCUM, int OUT, bool KTAIL>
+// KTAIL (widened MXFP8 fprop only): K is not a multiple of 128, so the last K step runs past it.
+// The scaled-MFMA paths (SC: MXFP4, and MXFP8 on the fp8 MFMA) decide per group at run time
+// whether their last K step is such a tail step.
+template <int MODE, bool PC, int FMT, int BM, int BN, int WM, int WN, bool ACCUM, int OUT, bool KTAIL>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kernel(GemmArgs args) {
-  using S = GemmShape<MODE, PC, F4, BM, BN, WM, WN>;
+  using S = GemmShape<MODE, PC, FMT, BM, BN, WM, WN>;
   constexpr int NT = S::NT, NW = S::NW, BK = S::BK, FM = S::FM, FN = S::FN;
   constexpr int SBLK = S::SBLK, BLK_BYTES = S::BLK_BYTES;
+  constexpr bool F4 = FMT == kFmtF4, F8 = FMT == kFmtF8, SC = F4 || F8;
   constexpr int EPB = F4 ? 2 : 1;  // elements per data byte
-  static_assert(!(PC && F4) && !(KTAIL && F4), "recipe flags");
+  static_assert(!(PC && SC) && !(KTAIL && SC), "recipe flags");
   __shared__ GroupScanSmem<NT> gsm;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::STAGE];
 
@@ -251,7 +257,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem);
   auto lds_of = [&](const uint8_t* p) { return smem_lds + (uint32_t)(p - smem); };
   auto dma4 = [&](const void* g, uint8_t* l) {
-    if constexpr (F4) asm_dma4(g, lds_of(l));
+    if constexpr (SC) asm_dma4(g, lds_of(l));
     else __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
   };
   const v4i a_rw = rsrc_words(a_data + a_row0 * lda, (uint32_t)tile_range(a_valid - a_row0, lda));
@@ -274,7 +280,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
       static_assert((FA_ROWS == 2 || FA_ROWS == 4) && NW % SBLK == 0, "fprop A-scale staging shape");
       const int blk = wave / (NW / SBLK), r0 = FA_ROWS * ((wave % (NW / SBLK)) * 64 + lane);
       const int64_t kb = (int64_t)kk * SBLK + blk;
-      if constexpr (F4) {
+      if constexpr (SC) {
         // no branch: a block past kext loads the last valid one; settle() puts unit scales there
         const int64_t kbc = kb < nblk ? kb : nblk - 1;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -296,13 +302,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
 #pragma unroll
     for (int u = 0; u < S::A_INS; ++u) {
       const int g = wave * S::A_INS + u;
-      if constexpr (F4) asm_dma16(a_rw, lds_of(base + S::A_OFF + g * 1024), a_off[u] + k0);
+      if constexpr (SC) asm_dma16(a_rw, lds_of(base + S::A_OFF + g * 1024), a_off[u] + k0);
       else buffer_dma16(a_rs, base + S::A_OFF + g * 1024, a_off[u] + k0);
     }
 #pragma unroll
     for (int u = 0; u < S::B_INS; ++u) {
       const int g = wave * S::B_INS + u;
-      if constexpr (F4) asm_dma16(b_rw, lds_of(base + S::B_OFF + g * 1024), b_off[u] + k0);
+      if constexpr (SC) asm_dma16(b_rw, lds_of(base + S::B_OFF + g * 1024), b_off[u] + k0);
       else buffer_dma16(b_rs, base + S::B_OFF + g * 1024, b_off[u] + k0);
     }
     if constexpr (PC) {
@@ -334,7 +340,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
         uint8_t* dst = base + (is_a ? S::SA_OFF + blk * BM : S::SB_OFF + blk * BN) + part * 256;
         if (MODE == kModeFprop && is_a) {
           // rows of a group start anywhere: single-byte loads per thread instead (above)
-        } else if (F4) {
+        } else if (SC) {
           // no branch: a block past kext loads the last valid one; settle() puts unit scales there
           const int64_t kbc = kb < nblk ? kb : nblk - 1;
           const int r4 = scale_dma_row(part, lane, is_a ? a_last : b_last);
@@ -354,8 +360,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   // bytes its own scale DMA (or tail store) wrote -- visible to it after its own wait -- and the
   // fprop A scales come from the register-staged bytes.
   auto settle = [&](uint8_t* base, int kk) {
-    if constexpr (F4) {
-      // MXFP4: the MFMA takes the E8M0 bytes as they are.  The fprop A scales, staged in
+    if constexpr (SC) {
+      // The scaled MFMA takes the E8M0 bytes as they are.  The fprop A scales, staged in
       // registers, are written to their [blk][row] place, and blocks past kext (a tail step)
       // get unit scales over their zero data, in the 256-byte pieces this wave's DMA filled.
       constexpr int SA_INS = SBLK * BM / 256, SB_INS = SBLK * BN / 256, PER = (SA_INS + SB_INS) / NW;
@@ -521,7 +527,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   // << 4) (4s + 2u is even and row * BK has no bits below 128); its E8M0 byte at
   // SA_OFF + (h * BM + row) + (4s + 2u) * BM.  Six bases per operand stay live, not 24 addresses.
   uint32_t a4b[FM], a4s[FM], b4b[FN], b4s[FN];
-  if constexpr (F4) {
+  if constexpr (SC) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = wm * WM + i * 32 + l32;
@@ -596,6 +602,58 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
 #pragma unroll
       for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(acc[i][j]));
   };
+  // MXFP8 K step on the scaled fp8 MFMA.  MFMA m of the step (K bytes [64 m, 64 m + 64)) takes
+  // from lane (row, h) the two 16-byte chunks 4 m + h and 4 m + 2 + h of its row, in its first and
+  // last four registers, and the E8M0 byte of block 2 m + h: the instruction pairs the chunks
+  // of one scale block over the lanes (row, 0) and (row, 1) (measured on the GPU; the precision
+  // probe of the probe library pins this layout).  These are the chunks the widened path reads
+  // for its K half m.  Same structure as the MXFP4 step: branch-free, the next step's loads
+  // always issued (here first: measured 2% faster than after the first reads), the second
+  // MFMA's reads beside the first's MFMAs.
+  auto step8f = [&](int kk, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+    auto chunk = [&](uint32_t off) { return *(const v4i*)(cur + off); };
+#pragma unroll
+    for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(a4b[i]), "+v"(a4s[i]));
+#pragma unroll
+    for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(b4b[j]), "+v"(b4s[j]));
+    v8i af[2][FM], bf[2][FN];
+    int as[2][FM], bs[2][FN];
+    auto rd = [&](int m, int buf) {
+      const uint32_t lo = (uint32_t)(4 * m) << 4, hi = (uint32_t)(4 * m + 2) << 4;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const v4i a = chunk(a4b[i] ^ lo), b = chunk(a4b[i] ^ hi);
+        af[buf][i] = v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        as[buf][i] = cur[a4s[i] + 2 * m * BM];
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const v4i a = chunk(b4b[j] ^ lo), b = chunk(b4b[j] ^ hi);
+        bf[buf][j] = v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        bs[buf][j] = cur[b4s[j] + 2 * m * BN];
+      }
+    };
+    auto mm = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[buf][i], bf[buf][j], acc[i][j], 0, 0, 0,
+                                                                       as[buf][i], 0, bs[buf][j]);
+    };
+    issue(kk + 1, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    rd(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    rd(1, 1);
+    mm(0);
+    __builtin_amdgcn_sched_barrier(0);
+    mm(1);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(acc[i][j]));
+  };
   issue(0, smem);
   wait_dma();
   settle(smem, 0);
@@ -603,11 +661,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   // the last step runs past kext (MXFP8 fprop with K not a multiple of 128; MXFP4 when the
   // group's K bytes are not a multiple of 128): it is the tail step
   static_assert(!KTAIL || MODE == kModeFprop, "only fprop has a static K tail");
-  if constexpr (F4) {
+  if constexpr (SC) {
     for (int kk = 0; kk < nk; ++kk) {
       uint8_t* cur = smem + (kk & 1) * S::STAGE;
       uint8_t* nxt = smem + ((kk & 1) ^ 1) * S::STAGE;
-      step4(kk, cur, nxt);
+      if constexpr (F4) step4(kk, cur, nxt);
+      else step8f(kk, cur, nxt);
       wait_dma();  // after the last step: the surplus loads have landed before LDS is reused
       if (kk + 1 < nk) settle(nxt, kk + 1);
       __syncthreads();
@@ -704,10 +763,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
 // Launchers
 // ------------------------------------------------------------------------------------------
 
-template <int MODE, bool PC, bool F4, int BM, int BN, int WM, int WN, bool ACCUM, int OUT, bool KTAIL = false>
+template <int MODE, bool PC, int FMT, int BM, int BN, int WM, int WN, bool ACCUM, int OUT, bool KTAIL = false>
 static int launch(const GemmArgs& a, dim3 grid, hipStream_t stream) {
-  using S = GemmShape<MODE, PC, F4, BM, BN, WM, WN>;
-  hipLaunchKernelGGL((grouped_gemm_kernel<MODE, PC, F4, BM, BN, WM, WN, ACCUM, OUT, KTAIL>), grid, dim3(S::NT), 0,
+  using S = GemmShape<MODE, PC, FMT, BM, BN, WM, WN>;
+  hipLaunchKernelGGL((grouped_gemm_kernel<MODE, PC, FMT, BM, BN, WM, WN, ACCUM, OUT, KTAIL>), grid, dim3(S::NT), 0,
                      stream, a);
   return hipGetLastError() == hipSuccess ? BSFP8_OK : BSFP8_ERR_LAUNCH;
 }
@@ -727,6 +786,8 @@ int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, 
   a.E = E;
   a.out = out;
   a.status = status;
+  const bool f8 = (recipe & BSFP8_GEMM_FP8_MFMA) != 0;  // MXFP8 on the scaled fp8 MFMA
+  recipe &= ~BSFP8_GEMM_FP8_MFMA;
   if (recipe == BSFP8_RECIPE_MX_1X32_E8M0 || recipe == BSFP8_RECIPE_MXFP4_1X32_E8M0) {
     constexpr int BM = 256, BN = 256;
     a.tiles_m = (int)((n + BM - 1) / BM);
@@ -735,10 +796,13 @@ int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, 
     if (xcd_launch_size(a.tiles) > 0x7fffffff) return BSFP8_ERR_SHAPE;
     dim3 grid((unsigned)xcd_launch_size(a.tiles));
     if (recipe == BSFP8_RECIPE_MXFP4_1X32_E8M0)
-      return accumulate ? launch<kModeWgrad, false, true, BM, BN, 128, 64, true, 0>(a, grid, stream)
-                        : launch<kModeWgrad, false, true, BM, BN, 128, 64, false, 0>(a, grid, stream);
-    return accumulate ? launch<kModeWgrad, false, false, BM, BN, 128, 64, true, 0>(a, grid, stream)
-                      : launch<kModeWgrad, false, false, BM, BN, 128, 64, false, 0>(a, grid, stream);
+      return accumulate ? launch<kModeWgrad, false, kFmtF4, BM, BN, 128, 64, true, 0>(a, grid, stream)
+                        : launch<kModeWgrad, false, kFmtF4, BM, BN, 128, 64, false, 0>(a, grid, stream);
+    if (f8)
+      return accumulate ? launch<kModeWgrad, false, kFmtF8, BM, BN, 128, 64, true, 0>(a, grid, stream)
+                        : launch<kModeWgrad, false, kFmtF8, BM, BN, 128, 64, false, 0>(a, grid, stream);
+    return accumulate ? launch<kModeWgrad, false, kFmtBf16, BM, BN, 128, 64, true, 0>(a, grid, stream)
+                      : launch<kModeWgrad, false, kFmtBf16, BM, BN, 128, 64, false, 0>(a, grid, stream);
   }
   constexpr int BM = 128, BN = 128;
   a.tiles_m = (int)((n + BM - 1) / BM);
@@ -746,14 +810,15 @@ int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, 
   a.tiles = (int64_t)E * a.tiles_m * a.tiles_n;
   if (xcd_launch_size(a.tiles) > 0x7fffffff) return BSFP8_ERR_SHAPE;
   dim3 grid((unsigned)xcd_launch_size(a.tiles));
-  return accumulate ? launch<kModeWgrad, true, false, BM, BN, 64, 64, true, 0>(a, grid, stream)
-                    : launch<kModeWgrad, true, false, BM, BN, 64, 64, false, 0>(a, grid, stream);
+  return accumulate ? launch<kModeWgrad, true, kFmtBf16, BM, BN, 64, 64, true, 0>(a, grid, stream)
+                    : launch<kModeWgrad, true, kFmtBf16, BM, BN, 64, 64, false, 0>(a, grid, stream);
 }
 
 // m-grouped GEMM: out[off_e + t][j] = sum_c A[off_e + t][c] B_e[j][c] over the rowwise A
 // [R][K] and a per-group B described by its row length and strides (see GemmArgs).  K, b_ld and
 // b_estride are in bytes (K elements / 2 for MXFP4); the scale strides count E8M0 bytes.
-static int launch_mgrouped(bool f4, const uint8_t* a_q, const uint8_t* a_s, int64_t R, int64_t K, const uint8_t* b_q,
+// fmt: kFmtBf16 (MXFP8, widened), kFmtF4 (MXFP4) or kFmtF8 (MXFP8 on the scaled fp8 MFMA).
+static int launch_mgrouped(int fmt, const uint8_t* a_q, const uint8_t* a_s, int64_t R, int64_t K, const uint8_t* b_q,
                            const uint8_t* b_s, int64_t N, int64_t b_ld, int64_t b_estride, int64_t bs_estride,
                            int64_t bs_bstride, const int32_t* splits, int E, void* out, int out_dtype,
                            uint32_t* status, hipStream_t stream) {
@@ -782,17 +847,21 @@ static int launch_mgrouped(bool f4, const uint8_t* a_q, const uint8_t* a_s, int6
   a.tiles = (mt + gm - 1) / gm * gm * a.tiles_n;
   if (xcd_launch_size(a.tiles) > 0x7fffffff) return BSFP8_ERR_SHAPE;
   dim3 grid((unsigned)xcd_launch_size(a.tiles));
-  if (f4)
+  if (fmt == kFmtF4)
     return out_dtype == BSFP8_OUT_F32
-               ? launch<kModeFprop, false, true, BM, BN, 128, 64, false, BSFP8_OUT_F32>(a, grid, stream)
-               : launch<kModeFprop, false, true, BM, BN, 128, 64, false, BSFP8_OUT_BF16>(a, grid, stream);
+               ? launch<kModeFprop, false, kFmtF4, BM, BN, 128, 64, false, BSFP8_OUT_F32>(a, grid, stream)
+               : launch<kModeFprop, false, kFmtF4, BM, BN, 128, 64, false, BSFP8_OUT_BF16>(a, grid, stream);
+  if (fmt == kFmtF8)
+    return out_dtype == BSFP8_OUT_F32
+               ? launch<kModeFprop, false, kFmtF8, BM, BN, 128, 64, false, BSFP8_OUT_F32>(a, grid, stream)
+               : launch<kModeFprop, false, kFmtF8, BM, BN, 128, 64, false, BSFP8_OUT_BF16>(a, grid, stream);
   if (K % 128 != 0)
     return out_dtype == BSFP8_OUT_F32
-               ? launch<kModeFprop, false, false, BM, BN, 128, 64, false, BSFP8_OUT_F32, true>(a, grid, stream)
-               : launch<kModeFprop, false, false, BM, BN, 128, 64, false, BSFP8_OUT_BF16, true>(a, grid, stream);
+               ? launch<kModeFprop, false, kFmtBf16, BM, BN, 128, 64, false, BSFP8_OUT_F32, true>(a, grid, stream)
+               : launch<kModeFprop, false, kFmtBf16, BM, BN, 128, 64, false, BSFP8_OUT_BF16, true>(a, grid, stream);
   return out_dtype == BSFP8_OUT_F32
-             ? launch<kModeFprop, false, false, BM, BN, 128, 64, false, BSFP8_OUT_F32>(a, grid, stream)
-             : launch<kModeFprop, false, false, BM, BN, 128, 64, false, BSFP8_OUT_BF16>(a, grid, stream);
+             ? launch<kModeFprop, false, kFmtBf16, BM, BN, 128, 64, false, BSFP8_OUT_F32>(a, grid, stream)
+             : launch<kModeFprop, false, kFmtBf16, BM, BN, 128, 64, false, BSFP8_OUT_BF16>(a, grid, stream);
 }
 
 int launch_grouped_gemm_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R, int64_t K, const uint8_t* w_q,
@@ -800,8 +869,9 @@ int launch_grouped_gemm_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R,
                               int out_dtype, uint32_t* status, hipStream_t stream) {
   // W rowwise [E*N][K], scales [K/32][E*N]
   const bool f4 = recipe == BSFP8_RECIPE_MXFP4_1X32_E8M0;
+  const int fmt = f4 ? kFmtF4 : (recipe & BSFP8_GEMM_FP8_MFMA) ? kFmtF8 : kFmtBf16;
   const int64_t kb = f4 ? K / 2 : K;  // bytes of a row
-  return launch_mgrouped(f4, x_q, x_s, R, kb, w_q, w_s, N, kb, N * kb, N, (int64_t)E * N, splits, E, out, out_dtype,
+  return launch_mgrouped(fmt, x_q, x_s, R, kb, w_q, w_s, N, kb, N * kb, N, (int64_t)E * N, splits, E, out, out_dtype,
                          status, stream);
 }
 
@@ -812,8 +882,9 @@ int launch_grouped_gemm_dgrad(const uint8_t* dy_q, const uint8_t* dy_s, int64_t 
   // (n along the contraction, pad lanes 0), data at element k * np * e; E8M0 (e, b, c) at
   // k * np * e / 32 + b * k + c
   const bool f4 = recipe == BSFP8_RECIPE_MXFP4_1X32_E8M0;
+  const int fmt = f4 ? kFmtF4 : (recipe & BSFP8_GEMM_FP8_MFMA) ? kFmtF8 : kFmtBf16;
   const int64_t np = (n + 127) / 128 * 128, epb = f4 ? 2 : 1;
-  return launch_mgrouped(f4, dy_q, dy_s, R, n / epb, w_q, (const uint8_t*)w_s, k, np / epb, k * np / epb, k * np / 32,
+  return launch_mgrouped(fmt, dy_q, dy_s, R, n / epb, w_q, (const uint8_t*)w_s, k, np / epb, k * np / epb, k * np / 32,
                          k, splits, E, out, out_dtype, status, stream);
 }
 

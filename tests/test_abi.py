@@ -87,6 +87,8 @@ def test_binding_constants_match_header():
     c = _hdr_consts()
     assert c["BSFP8_RECIPE_MX_1X32_E8M0"] == bs.RECIPE_MX and c["BSFP8_RECIPE_PER_CHANNEL_128_F32"] == bs.RECIPE_PC
     assert c["BSFP8_RECIPE_MXFP4_1X32_E8M0"] == bs.RECIPE_MX4
+    text = open(HDR).read()
+    assert "#define BSFP8_GEMM_FP8_MFMA 0x100" in text and bs.GEMM_FP8_MFMA == 0x100
     assert c["BSFP8_ROWWISE"] == bs.ROWWISE and c["BSFP8_COLWISE"] == bs.COLWISE
     assert c["BSFP8_OUT_F32"] == bs.OUT_F32 and c["BSFP8_OUT_BF16"] == bs.OUT_BF16
     assert c["BSFP8_MAX_GROUPS"] == bs.MAX_GROUPS
@@ -138,7 +140,7 @@ def _f(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(recipe=0), -3), (dict(recipe=4), -3),
+    (dict(recipe=0), -3), (dict(recipe=4), -3), (dict(recipe=MX | 0x100), -3),
     (dict(which=0), -7), (dict(which=4), -7),
     (dict(which=bs.ROWWISE, recipe=PC), -6), (dict(which=bs.ROWWISE | bs.COLWISE, recipe=PC), -6),
     (dict(C=33), -4), (dict(C=0), -4), (dict(R=-1), -4),
@@ -161,7 +163,8 @@ def test_quantize_zero_rows_returns_without_touching_pointers():
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(recipe=5), -3), (dict(E=0), -2), (dict(E=2000), -2),
+    (dict(recipe=5), -3), (dict(recipe=PC | 0x100), -3), (dict(recipe=MX4 | 0x100), -3), (dict(recipe=0x100), -3),
+    (dict(E=0), -2), (dict(E=2000), -2),
     (dict(n=100), -4), (dict(h=0), -4), (dict(R=-5), -4),
     (dict(acc=2), -7), (dict(R=(1 << 24)), -4), (dict(h=(1 << 21) + 32), -4),
     (dict(splits=None), -1), (dict(out=None), -1), (dict(dyq=None), -1), (dict(xs=None), -1),
@@ -174,6 +177,7 @@ def test_wgrad_rejects_before_launch(kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(E=0), -2), (dict(k=48), -4), (dict(n=-32), -4), (dict(dtype=2), -7), (dict(k=1 << 24), -4),
     (dict(n=(1 << 21) + 32), -4), (dict(recipe=PC), -3), (dict(recipe=0), -3), (dict(recipe=4), -3),
+    (dict(recipe=MX4 | 0x100), -3), (dict(recipe=0x100), -3),
     (dict(xq=None), -1), (dict(ws=None), -1), (dict(splits=None), -1), (dict(out=None), -1),
     (dict(out=P + 2), -5), (dict(wq=P + 8), -5),
 ])
@@ -193,6 +197,7 @@ def _d(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(E=0), -2), (dict(E=2000), -2), (dict(n=48), -4), (dict(k=-32), -4), (dict(k=(1 << 21) + 32), -4),
     (dict(n=(1 << 24) - 224), -4), (dict(dtype=2), -7), (dict(R=-1), -4), (dict(recipe=PC), -3),
+    (dict(recipe=PC | 0x100), -3), (dict(recipe=MX4 | 0x100), -3),
     (dict(yq=None), -1), (dict(ws=None), -1), (dict(splits=None), -1), (dict(out=None), -1),
     (dict(out=P + 2), -5), (dict(wq=P + 8), -5), (dict(ys=P + 1), -5),
 ])

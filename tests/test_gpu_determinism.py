@@ -58,7 +58,7 @@ def test_wgrad_10000_calls_bitwise(sf_val):
 # (its LDS DMAs issued as inline assembly with hand-placed waits), on the same four-expert 2048 x 2048
 # shape with one all-zero dy channel in each 128-token expert.  wgrad in store mode, wgrad
 # accumulating into a main_grad reset to the same fp32 contents before every call, and the m-grouped
-# forward (fp32 and bf16 out) on a four-expert weight.  Every call must be bitwise equal to the first;
+# forward (fp32 and bf16 out) on a four-expert weight; also the MXFP8 operands on the scaled fp8 MFMA.  Every call must be bitwise equal to the first;
 # the loop counts mismatching calls on the device and reports every 2,500 calls.
 def _stress(run, out, label):
     run()
@@ -79,15 +79,20 @@ def _stress(run, out, label):
     return first
 
 
+F8 = bs.RECIPE_MX | bs.GEMM_FP8_MFMA  # MXFP8 operands on the scaled fp8 MFMA
+
+
 @pytest.mark.parametrize("recipe,accumulate", [(bs.RECIPE_MX, False), (bs.RECIPE_MX, True),
-                                               (bs.RECIPE_MX4, False), (bs.RECIPE_MX4, True)])
+                                               (bs.RECIPE_MX4, False), (bs.RECIPE_MX4, True),
+                                               (F8, False), (F8, True)])
 def test_block_scaled_wgrad_10000_calls_bitwise(recipe, accumulate):
     case = W.deepgemm_case(DEV, 2048, 2048)
     splits, n, h, R = case["splits"], case["n"], case["h"], case["R"]
     E = len(splits)
     st = W.splits_tensor(splits, DEV)
-    dq = gpu_quantize(case["dy"], splits, recipe, bs.COLWISE)
-    xq = gpu_quantize(case["x"], splits, recipe, bs.COLWISE)
+    qrecipe = recipe & ~bs.GEMM_FP8_MFMA  # the data recipe
+    dq = gpu_quantize(case["dy"], splits, qrecipe, bs.COLWISE)
+    xq = gpu_quantize(case["x"], splits, qrecipe, bs.COLWISE)
     out = torch.empty(E, n, h, dtype=torch.float32, device=DEV)
     mg0 = torch.randn(E, n, h, generator=torch.Generator(device=DEV).manual_seed(7), device=DEV)
 
@@ -107,15 +112,16 @@ def test_block_scaled_wgrad_10000_calls_bitwise(recipe, accumulate):
 
 
 @pytest.mark.parametrize("recipe,out_dtype", [(bs.RECIPE_MX, bs.OUT_F32), (bs.RECIPE_MX, bs.OUT_BF16),
-                                              (bs.RECIPE_MX4, bs.OUT_BF16)])
+                                              (bs.RECIPE_MX4, bs.OUT_BF16), (F8, bs.OUT_BF16)])
 def test_block_scaled_fprop_10000_calls_bitwise(recipe, out_dtype):
     case = W.deepgemm_case(DEV, 2048, 2048)
     splits, K, R = case["splits"], case["h"], case["R"]
     E, N = len(splits), 2048
     st = W.splits_tensor(splits, DEV)
-    xq = gpu_quantize(case["x"], splits, recipe, bs.ROWWISE)
+    qrecipe = recipe & ~bs.GEMM_FP8_MFMA
+    xq = gpu_quantize(case["x"], splits, qrecipe, bs.ROWWISE)
     w = W.randn_bf16((E * N, K), torch.Generator(device=DEV).manual_seed(8), DEV)
-    wq = gpu_quantize(w, None, recipe, bs.ROWWISE)
+    wq = gpu_quantize(w, None, qrecipe, bs.ROWWISE)
     out = torch.empty(R, N, dtype=torch.float32 if out_dtype == bs.OUT_F32 else torch.bfloat16, device=DEV)
 
     def run():
