@@ -291,6 +291,139 @@ def fp8_mfma_leg(bs, case, dq, xq, wq, st, R, n, h, K, N, mg, fout, status, stre
     return res, outs
 
 
+def _time_calls(fn, stream, reps):
+    """Mean milliseconds per call over `reps` back-to-back calls (after one warm-up call), with
+    HIP events on the launch stream."""
+    import torch
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def small_configs_leg(bs, W, dev, stream, run_oracle=True):
+    """The other four workloads, each in the launch configuration its parity test uses, timed on
+    the GPU (mean over back-to-back calls) and run through the full CPU oracle (quantize, then
+    the GEMMs) with its wall time and thread count:
+      1 DeepGEMM #365 shape: 4 experts [256,128,128,256] + 256 rows of 3.0, n = h = 256,
+        per-channel recipe, wgrad stored fp32 (launch/HBM bound: microseconds and GB/s)
+      2 TE #3484 shape: one group of 512 rows in a 768-row buffer padded with 3.0, hidden 1024,
+        MXFP8, wgrad accumulated into a zeroed fp32 main_grad
+      3 DeepGEMM #365 shape at n = h = 2048, per-channel, wgrad stored
+      4 MoE, 32 experts, 65,536 Zipf-routed rows (4 empty, padded with random bits), hidden
+        4096, ffn 1536, MXFP8: quantize x (row + col), dy (col), W (row); wgrad stored fp32,
+        fprop fp32 (near the ridge: TFLOP/s)
+    GB/s are algorithmic bytes: bf16 read once, codes and scales written once per layout;
+    GEMM operands read once, outputs written once (main_grad read and written)."""
+    import torch
+
+    import oracle
+
+    out = {}
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def kp_rows(splits):
+        return sum(128 * ((k + 127) // 128) for k in splits)
+
+    def wgrad_case(name, case, recipe, accumulate, reps):
+        splits, R, n, h = case["splits"], case["R"], case["n"], case["h"]
+        T, E, kp = sum(splits), len(splits), kp_rows(splits)
+        st = W.splits_tensor(splits, dev)
+        dq = bs.alloc_quantized(R, n, E, recipe, bs.COLWISE, dev)
+        xq = bs.alloc_quantized(R, h, E, recipe, bs.COLWISE, dev)
+        mg = case["main_grad"].clone() if accumulate else torch.empty(E, n, h, dtype=torch.float32, device=dev)
+        sbytes = 4 / 128 if recipe == bs.RECIPE_PC else 1 / 32
+        legs = {
+            "quantize_dy": (lambda: bs.grouped_quantize(case["dy"], st, recipe, bs.COLWISE, dq, status=status),
+                            2.0 * T * n + kp * n * (1 + sbytes)),
+            "quantize_x": (lambda: bs.grouped_quantize(case["x"], st, recipe, bs.COLWISE, xq, status=status),
+                           2.0 * T * h + kp * h * (1 + sbytes)),
+            "wgrad": (lambda: bs.grouped_gemm_wgrad(dq, n, xq, h, st, R, recipe, mg, accumulate=accumulate,
+                                                    status=status),
+                      (n + h) * kp * (1 + sbytes) + 4.0 * n * h * E * (2 if accumulate else 1)),
+        }
+        res = {}
+        for leg, (fn, nbytes) in legs.items():
+            ms = _time_calls(fn, stream, reps)
+            res[leg] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms / 1e3) / 1e9, 1)}
+        res["wgrad"]["TFLOP/s"] = round(2.0 * n * h * T / (res["wgrad"]["us"] / 1e6) / 1e12, 2)
+        if run_oracle:
+            t0 = time.perf_counter()
+            odq = oracle.grouped_quantize(W.bf16_bits(case["dy"]), splits, recipe, oracle.COLWISE)
+            oxq = oracle.grouped_quantize(W.bf16_bits(case["x"]), splits, recipe, oracle.COLWISE)
+            oracle.grouped_wgrad(odq["col_q"], odq["col_s"], n, oxq["col_q"], oxq["col_s"], h, splits, R, recipe)
+            res["oracle_s"] = round(time.perf_counter() - t0, 3)
+            res["oracle_threads"] = oracle.num_threads()
+        out[name] = res
+        del dq, xq, mg
+
+    log("config 1 (DeepGEMM #365 shape, 256 channels, padded)")
+    wgrad_case("1_deepgemm_256_padded", W.deepgemm_case(dev, 256, 256, R=1024, pad_fill=3.0), bs.RECIPE_PC,
+               False, 200)
+    log("config 2 (TE #3484 shape, one group, padded with 3.0)")
+    wgrad_case("2_te3484_single_group", W.te_single_group_case(dev, R=768, pad_fill=3.0), bs.RECIPE_MX, True, 200)
+    log("config 3 (DeepGEMM #365 shape, 2048 channels)")
+    wgrad_case("3_deepgemm_2048", W.deepgemm_case(dev, 2048, 2048), bs.RECIPE_PC, False, 100)
+
+    log("config 4 (32 experts, Zipf routing)")
+    case = W.moe32_zipf(dev)
+    splits, R, T = case["splits"], case["R"], case["T"]
+    n, h, K, N = case["n"], case["h"], case["K"], case["N"]
+    E, kp = len(splits), kp_rows(splits)
+    st = W.splits_tensor(splits, dev)
+    xq = bs.alloc_quantized(R, h, E, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, dev)
+    dq = bs.alloc_quantized(R, n, E, bs.RECIPE_MX, bs.COLWISE, dev)
+    wq = bs.alloc_quantized(E * N, K, 1, bs.RECIPE_MX, bs.ROWWISE, dev)
+    dw = torch.empty(E, n, h, dtype=torch.float32, device=dev)
+    fo = torch.empty(R, N, dtype=torch.float32, device=dev)
+    w2 = case["W"].view(E * N, K)
+    legs = {
+        "quantize_x": (lambda: bs.grouped_quantize(case["x"], st, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, xq,
+                                                   status=status),
+                       2.0 * T * h + (T + kp) * h * (1 + 1 / 32)),
+        "quantize_dy": (lambda: bs.grouped_quantize(case["dy"], st, bs.RECIPE_MX, bs.COLWISE, dq, status=status),
+                        2.0 * T * n + kp * n * (1 + 1 / 32)),
+        "quantize_w": (lambda: bs.grouped_quantize(w2, None, bs.RECIPE_MX, bs.ROWWISE, wq), E * N * K * (3 + 1 / 32)),
+        "wgrad": (lambda: bs.grouped_gemm_wgrad(dq, n, xq, h, st, R, bs.RECIPE_MX, dw, status=status),
+                  (n + h) * kp * (1 + 1 / 32) + 4.0 * n * h * E),
+        "fprop": (lambda: bs.grouped_gemm_fprop(xq, K, wq, N, st, R, fo, bs.OUT_F32, status=status),
+                  T * K * (1 + 1 / 32) + E * N * K * (1 + 1 / 32) + 4.0 * T * N),
+    }
+    res = {}
+    for leg, (fn, nbytes) in legs.items():
+        ms = _time_calls(fn, stream, 20)
+        res[leg] = {"us": round(ms * 1e3, 1), "GB/s": round(nbytes / (ms / 1e3) / 1e9, 1)}
+    flop = 2.0 * n * h * T
+    for leg in ("wgrad", "fprop"):
+        r = flop / (res[leg]["us"] / 1e6) / 1e12
+        res[leg].update({"TFLOP/s": round(r, 1), "frac_of_fp8_peak": round(r / PEAK_FP8_MFMA_TFLOPS, 4)})
+    if run_oracle:
+        log("config 4: full CPU oracle (quantize, wgrad, fprop)")
+        t0 = time.perf_counter()
+        ox = oracle.grouped_quantize(W.bf16_bits(case["x"]), splits, oracle.RECIPE_MX, oracle.COLWISE | oracle.ROWWISE)
+        ody = oracle.grouped_quantize(W.bf16_bits(case["dy"]), splits, oracle.RECIPE_MX, oracle.COLWISE)
+        ow = oracle.grouped_quantize(W.bf16_bits(w2), None, oracle.RECIPE_MX, oracle.ROWWISE)
+        t1 = time.perf_counter()
+        oracle.grouped_wgrad(ody["col_q"], ody["col_s"], n, ox["col_q"], ox["col_s"], h, splits, R, oracle.RECIPE_MX)
+        t2 = time.perf_counter()
+        oracle.grouped_fprop(ox["row_q"], ox["row_s"], ow["row_q"], ow["row_s"], N, splits)
+        t3 = time.perf_counter()
+        res["oracle_s"] = round(t3 - t0, 3)
+        res["oracle_breakdown_s"] = {"quantize": round(t1 - t0, 3), "wgrad": round(t2 - t1, 3),
+                                     "fprop": round(t3 - t2, 3)}
+        res["oracle_wgrad_TFLOP/s"] = round(flop / (t2 - t1) / 1e12, 4)
+        res["oracle_threads"] = oracle.num_threads()
+    out["4_moe32_zipf"] = res
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    return out
+
+
 def moe32_step_bench(args):
     """The same step on the 32-expert layer (65,536 routed rows, Zipf counts with 4 empty
     experts, hidden 4096, ffn 1536, padded capacity with garbage rows): quantize x (row+col),
@@ -387,6 +520,9 @@ def main():
     ap.add_argument("--cpu-channels", type=int, default=2048, help="dy channels per sampled expert")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay leg")
     ap.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4 leg")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other four workloads")
+    ap.add_argument("--no-config-oracle", action="store_true",
+                    help="time the other four workloads on the GPU only, without their full CPU oracle")
     ap.add_argument("--calibrate-copy-gb", type=float, default=0.0,
                     help="after the timed region, run one device copy of this many GB (for counter "
                          "calibration against a kernel of known traffic)")
@@ -736,6 +872,10 @@ def main():
         f8["rel_err_vs_oracle"] = {k: float(f"{v:.3e}") for k, v in rel.items()}
         f8["rel_err_sample"] = f"wgrad store mode, experts {sorted(refs)}, the CPU-baseline channels; max over experts"
     del f8_outs
+    if not args.no_configs:
+        del xq, dq, wq, fout, case, mg
+        torch.cuda.empty_cache()
+        out["configs"] = small_configs_leg(bs, W, dev, stream, run_oracle=not args.no_config_oracle)
     print(json.dumps(out), flush=True)
 
 
