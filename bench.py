@@ -61,7 +61,7 @@ def log(msg):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.hpp", "tile_addr.hpp", "tile_sched.hpp"):
+    for f in ("gemm.hip", "common.hpp", "group_layout.hpp", "tile_addr.hpp", "tile_sched.hpp"):
         with open(os.path.join(ROOT, "block_scaled_fp8_grouped_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

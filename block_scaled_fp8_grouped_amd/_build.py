@@ -16,7 +16,7 @@ SOURCES = ["bsfp8.cpp", "quantize.hip", "gemm.hip"]
 # the MFMA-only throughput probe, a library of its own (measurement, not the path)
 PEAK_LIB_PATH = os.path.join(HERE, "libbsfp8_peak.so")
 PEAK_SOURCES = ["mfma_peak.hip"]
-HEADERS = ["common.hpp"]
+HEADERS = ["common.hpp", "group_layout.hpp", "tile_addr.hpp", "tile_sched.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "../../include/bsfp8.h"
+#include "group_layout.hpp"
 
 namespace bsfp8 {
 int launch_grouped_quantize(const void* in, int64_t R, int64_t C, const int32_t* splits, int E, int recipe,
@@ -57,7 +58,7 @@ extern "C" {
 
 int64_t bsfp8_colwise_rows_bound(int64_t capacity_rows, int32_t num_groups) {
   if (capacity_rows < 0 || !valid_groups(num_groups)) return 0;
-  return 128 * ((capacity_rows + 127 * (int64_t)num_groups) / 128);
+  return bsfp8::col_rows_bound(capacity_rows, num_groups);
 }
 
 size_t bsfp8_colwise_data_bytes(int64_t capacity_rows, int64_t cols, int32_t num_groups, int recipe) {

@@ -14,6 +14,7 @@
 #include <stdint.h>
 
 #include "../../include/bsfp8.h"
+#include "group_layout.hpp"
 
 namespace bsfp8 {
 
@@ -155,7 +156,7 @@ __device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_
     const int64_t v = e < E ? (int64_t)splits[e] : 0;
     if (v < 0) bad |= BSFP8_STATUS_NEGATIVE_SPLIT;
     k[i] = v < 0 ? 0 : v;
-    kp[i] = ((k[i] + 127) >> 7) << 7;
+    kp[i] = col_padded_rows(k[i]);
     tl[i] = tile_rows > 0 ? (k[i] + tile_rows - 1) / tile_rows : 0;
     sk += k[i];
     skp += kp[i];

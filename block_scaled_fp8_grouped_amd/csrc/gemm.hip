@@ -42,6 +42,7 @@
 // Rows past a group's live rows lie outside the buffer range of the tile's loads, so they read
 // as zeros (nothing beyond the live rows is fetched), and their results are not stored.
 #include "common.hpp"
+#include "group_layout.hpp"
 #include "tile_addr.hpp"
 #include "tile_sched.hpp"
 
@@ -208,21 +209,23 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
       }
       return;
     }
-    lda = ldb = gi.kp / EPB;
-    kext = gi.kp / EPB;
-    a_data = args.a_q + args.M * gi.p / EPB;
-    b_data = args.b_q + args.N * gi.p / EPB;
+    // the group's slice of the colwise buffers (group_layout.hpp): M (resp. N) channel rows of
+    // Kp codes each, scales block-major with M (N) entries per block
+    lda = ldb = col_row_bytes(gi.kp, EPB);
+    kext = col_row_bytes(gi.kp, EPB);
+    a_data = args.a_q + col_group_bytes(args.M, gi.p, EPB);
+    b_data = args.b_q + col_group_bytes(args.N, gi.p, EPB);
     a_valid = args.M;
     b_valid = args.N;
     if constexpr (PC) {
-      a_sc = (const uint8_t*)((const float*)args.a_s + args.M * gi.p / 128);
-      b_sc = (const uint8_t*)((const float*)args.b_s + args.N * gi.p / 128);
+      a_sc = (const uint8_t*)((const float*)args.a_s + col_pc_scale_group(args.M, gi.p));
+      b_sc = (const uint8_t*)((const float*)args.b_s + col_pc_scale_group(args.N, gi.p));
     } else {
-      a_sc = (const uint8_t*)args.a_s + args.M * gi.p / 32;
-      b_sc = (const uint8_t*)args.b_s + args.N * gi.p / 32;
+      a_sc = (const uint8_t*)args.a_s + col_e8m0_group(args.M, gi.p);
+      b_sc = (const uint8_t*)args.b_s + col_e8m0_group(args.N, gi.p);
     }
-    a_sld = args.M;
-    b_sld = args.N;
+    a_sld = col_e8m0_block_stride(args.M);
+    b_sld = col_e8m0_block_stride(args.N);
   } else {
     lda = args.K;
     ldb = args.b_ld;
@@ -878,14 +881,16 @@ int launch_grouped_gemm_fprop(const uint8_t* x_q, const uint8_t* x_s, int64_t R,
 int launch_grouped_gemm_dgrad(const uint8_t* dy_q, const uint8_t* dy_s, int64_t R, int64_t n, const uint8_t* w_q,
                               const void* w_s, int64_t k, const int32_t* splits, int E, int recipe, void* out,
                               int out_dtype, uint32_t* status, hipStream_t stream) {
-  // W colwise: group e's rows are its k output channels, each np = 128 * ceil(n / 128) elements
-  // (n along the contraction, pad lanes 0), data at element k * np * e; E8M0 (e, b, c) at
-  // k * np * e / 32 + b * k + c
+  // W colwise (group_layout.hpp with split sizes n, ..., n): group e's rows are its k output
+  // channels of np = Kp(n) codes each (n along the contraction, pad lanes 0) and it starts at
+  // packed row P_e = e * np, so the per-group strides are those of P = np
   const bool f4 = recipe == BSFP8_RECIPE_MXFP4_1X32_E8M0;
   const int fmt = f4 ? kFmtF4 : (recipe & BSFP8_GEMM_FP8_MFMA) ? kFmtF8 : kFmtBf16;
-  const int64_t np = (n + 127) / 128 * 128, epb = f4 ? 2 : 1;
-  return launch_mgrouped(fmt, dy_q, dy_s, R, n / epb, w_q, (const uint8_t*)w_s, k, np / epb, k * np / epb, k * np / 32,
-                         k, splits, E, out, out_dtype, status, stream);
+  const int epb = f4 ? 2 : 1;
+  const int64_t np = col_padded_rows(n);
+  return launch_mgrouped(fmt, dy_q, dy_s, R, n / epb, w_q, (const uint8_t*)w_s, k, col_row_bytes(np, epb),
+                         col_group_bytes(k, np, epb), col_e8m0_group(k, np), col_e8m0_block_stride(k), splits, E, out,
+                         out_dtype, status, stream);
 }
 
 }  // namespace bsfp8

@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "group_layout.hpp"
 
 namespace bsfp8 {
 
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
       g.p += g.kp;
       if (++g.e >= E) return false;
       g.k = splits[g.e];  // validated by the scan: 0 <= k, sum <= capacity
-      g.kp = (g.k + 127) / 128 * 128;
+      g.kp = col_padded_rows(g.k);
     }
     q.jblk = rt - g.tile;
     q.row0 = g.off + kQRows * q.jblk;
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
             q0[i] = (int)e2m1x8(a[0] * s0, a[1] * s0, a[2] * s0, a[3] * s0, a[4] * s0, a[5] * s0, a[6] * s0, a[7] * s0);
             q1[i] = (int)e2m1x8(b[0] * s1, b[1] * s1, b[2] * s1, b[3] * s1, b[4] * s1, b[5] * s1, b[6] * s1, b[7] * s1);
           }
-          uint8_t* dst = col_q + (C * P + oc * kp) / 2 + kQRows / 2 * jblk + 16 * wave;
+          uint8_t* dst = col_q + col_elem(C, P, kp, oc, kQRows * jblk + 32 * wave) / 2;
           *(v4i*)dst = q0;
           *(v4i*)(dst + kp / 2) = q1;
         } else {
@@ -308,13 +309,13 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
             q0[i >> 2][i & 3] = (int)e4m3x4(y0[4 * i] * s0, y0[4 * i + 1] * s0, y0[4 * i + 2] * s0, y0[4 * i + 3] * s0);
             q1[i >> 2][i & 3] = (int)e4m3x4(y1[4 * i] * s1, y1[4 * i + 1] * s1, y1[4 * i + 2] * s1, y1[4 * i + 3] * s1);
           }
-          uint8_t* dst = col_q + C * P + oc * kp + kQRows * jblk + 32 * wave;
+          uint8_t* dst = col_q + col_elem(C, P, kp, oc, kQRows * jblk + 32 * wave);
           *(v4i*)dst = q0[0];
           *(v4i*)(dst + 16) = q0[1];
           *(v4i*)(dst + kp) = q1[0];
           *(v4i*)(dst + kp + 16) = q1[1];
         }
-        *(uint16_t*)((uint8_t*)col_s + C * P / 32 + (4 * jblk + wave) * C + oc) = (uint16_t)sbits;
+        *(uint16_t*)((uint8_t*)col_s + col_e8m0(C, P, 4 * jblk + wave, oc)) = (uint16_t)sbits;
       }
     } else if constexpr (COL) {
       // ---- colwise: wave -> 32 tokens, lane -> channel pair ----
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
           float2 sv;
           sv.x = sf0;
           sv.y = sf1;
-          *(float2*)((float*)col_s + C * P / 128 + jblk * C + c0 + c) = sv;
+          *(float2*)((float*)col_s + col_pc_scale(C, P, jblk, c0 + c)) = sv;
         }
       }
       if constexpr (RECIPE == BSFP8_RECIPE_MXFP4_1X32_E8M0) {
@@ -373,10 +374,10 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
                               bf16_hi(wi[4]) * s1, bf16_hi(wi[5]) * s1, bf16_hi(wi[6]) * s1, bf16_hi(wi[7]) * s1);
         }
         if (c0 + c < C) {
-          uint8_t* dst = col_q + (C * P + (c0 + c) * kp) / 2 + kQRows / 2 * jblk + 16 * wave;
+          uint8_t* dst = col_q + col_elem(C, P, kp, c0 + c, kQRows * jblk + 32 * wave) / 2;
           *(v4i*)dst = q0;
           *(v4i*)(dst + kp / 2) = q1;
-          *(uint16_t*)((uint8_t*)col_s + C * P / 32 + (4 * jblk + wave) * C + c0 + c) = (uint16_t)sbits;
+          *(uint16_t*)((uint8_t*)col_s + col_e8m0(C, P, 4 * jblk + wave, c0 + c)) = (uint16_t)sbits;
         }
       } else {
         v4i q0[2], q1[2];
@@ -390,13 +391,13 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
           q1[i >> 2][i & 3] = (int)hi;
         }
         if (c0 + c < C) {
-          uint8_t* dst = col_q + C * P + (c0 + c) * kp + kQRows * jblk + 32 * wave;
+          uint8_t* dst = col_q + col_elem(C, P, kp, c0 + c, kQRows * jblk + 32 * wave);
           *(v4i*)dst = q0[0];
           *(v4i*)(dst + 16) = q0[1];
           *(v4i*)(dst + kp) = q1[0];
           *(v4i*)(dst + kp + 16) = q1[1];
           if constexpr (RECIPE == BSFP8_RECIPE_MX_1X32_E8M0) {
-            *(uint16_t*)((uint8_t*)col_s + C * P / 32 + (4 * jblk + wave) * C + c0 + c) = (uint16_t)sbits;
+            *(uint16_t*)((uint8_t*)col_s + col_e8m0(C, P, 4 * jblk + wave, c0 + c)) = (uint16_t)sbits;
           }
         }
       }

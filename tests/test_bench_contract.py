@@ -39,7 +39,7 @@ def test_kernel_source_hash_covers_the_gemm_sources(tmp_path, monkeypatch):
     # the hash follows the GEMM kernel's source text
     csrc = tmp_path / "block_scaled_fp8_grouped_amd" / "csrc"
     csrc.mkdir(parents=True)
-    for name in ("gemm.hip", "common.hpp", "tile_addr.hpp", "tile_sched.hpp"):
+    for name in ("gemm.hip", "common.hpp", "group_layout.hpp", "tile_addr.hpp", "tile_sched.hpp"):
         src = os.path.join(ROOT, "block_scaled_fp8_grouped_amd", "csrc", name)
         (csrc / name).write_bytes(open(src, "rb").read())
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
