@@ -130,25 +130,38 @@ struct GroupInfo {
 template <int NT>
 struct GroupScanSmem {
   int64_t wave_tot[NT / 64][3];
+  int64_t wave_aux[NT / 64][2];  // per wave: largest size, live groups
   int32_t tile_prefix[kMaxGroups + 1];
   int64_t info[4];
+  int32_t sel;
   uint32_t flags;
 };
 
+// Size skew at which the weight-gradient GEMM takes its groups largest first: the largest group
+// holds more than kSkewRatio times the mean size of the non-empty groups.  Each group's tiles
+// run for as many K steps as it has padded rows, so with a skewed split the largest groups
+// decide the kernel's end; started first, they finish beside the rest (longest-processing-time
+// order).  Near-uniform splits keep index order.  Ranking is done for at most kRankMaxGroups
+// groups (every workgroup ranks the sizes itself).
+constexpr int kSkewRatio = 2;
+constexpr int kRankMaxGroups = 256;
+
 // Scans split_sizes[0..E) across the workgroup.  tile_rows > 0 makes each group own
 // ceil(k_e / tile_rows) tiles, and the workgroup's linear tile `tile_index` is mapped to its
-// group (binary search over the tile prefix).  tile_rows == 0 selects group `group_index`.
+// group (binary search over the tile prefix).  tile_rows == 0 selects group `group_index`, or,
+// with `by_size` and a skewed split (kSkewRatio), the group of size rank `group_index`: groups
+// ordered by decreasing size, equal sizes by index.  The rank depends on split_sizes only.
 // Returns the validation bits (BSFP8_STATUS_*); GroupInfo.e is -1 when the tile is beyond the
 // last group's tiles or when the sizes are invalid.
 template <int NT>
 __device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_t capacity,
                                int tile_rows, int64_t tile_index, int group_index,
-                               GroupScanSmem<NT>& sm, GroupInfo& gi) {
+                               GroupScanSmem<NT>& sm, GroupInfo& gi, bool by_size = false) {
   constexpr int kItems = (kMaxGroups + NT - 1) / NT;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   int64_t k[kItems], kp[kItems], tl[kItems];
-  int64_t sk = 0, skp = 0, stl = 0;
+  int64_t sk = 0, skp = 0, stl = 0, kmax = 0, nlive = 0;
   uint32_t bad = 0;
 #pragma unroll
   for (int i = 0; i < kItems; ++i) {
@@ -161,6 +174,17 @@ __device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_
     sk += k[i];
     skp += kp[i];
     stl += tl[i];
+    kmax = k[i] > kmax ? k[i] : kmax;
+    nlive += k[i] > 0;
+  }
+  const bool rank = by_size && tile_rows == 0 && E <= kRankMaxGroups;
+  if (rank) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const int64_t m = __shfl_xor(kmax, d, 64), c = __shfl_xor(nlive, d, 64);
+      kmax = m > kmax ? m : kmax;
+      nlive += c;
+    }
   }
   // exclusive prefix of the per-thread sums across the workgroup
   const int64_t ik = wave_inclusive_scan(sk), ikp = wave_inclusive_scan(skp), itl = wave_inclusive_scan(stl);
@@ -169,6 +193,17 @@ __device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_
     sm.wave_tot[wave][0] = ik;
     sm.wave_tot[wave][1] = ikp;
     sm.wave_tot[wave][2] = itl;
+  }
+  if (rank) {
+    if (lane == 0) {
+      sm.wave_aux[wave][0] = kmax;
+      sm.wave_aux[wave][1] = nlive;
+    }
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int e = tid * kItems + i;
+      if (e < E) sm.tile_prefix[e] = (int32_t)k[i];  // the sizes, for the ranking below
+    }
   }
   __syncthreads();
   if (bad) atomicOr(&sm.flags, bad);
@@ -232,6 +267,41 @@ __device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_
     __syncthreads();
     gi.e = lo;
     gi.tile = sm.tile_prefix[lo];
+  } else if (rank) {
+    int64_t big = 0, live = 0;
+    for (int w = 0; w < NT / 64; ++w) {
+      big = sm.wave_aux[w][0] > big ? sm.wave_aux[w][0] : big;
+      live += sm.wave_aux[w][1];
+    }
+    if (big * live > (int64_t)kSkewRatio * tot) {
+      // skewed: the group of size rank group_index publishes its extents
+      int64_t ok2 = bk, okp2 = bkp;
+#pragma unroll
+      for (int i = 0; i < kItems; ++i) {
+        const int e = tid * kItems + i;
+        if (e < E) {
+          int r = 0;
+          for (int f = 0; f < E; ++f) {
+            const int32_t kf = sm.tile_prefix[f];
+            r += (kf > (int32_t)k[i]) || (kf == (int32_t)k[i] && f < e);
+          }
+          if (r == group_index) {
+            sm.info[0] = k[i];
+            sm.info[1] = ok2;
+            sm.info[2] = kp[i];
+            sm.info[3] = okp2;
+            sm.sel = e;
+          }
+        }
+        ok2 += k[i];
+        okp2 += kp[i];
+      }
+      __syncthreads();
+      gi.e = sm.sel;
+    } else {
+      gi.e = group_index;
+    }
+    gi.tile = 0;
   } else {
     gi.e = group_index;
     gi.tile = 0;

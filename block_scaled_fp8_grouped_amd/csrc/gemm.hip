@@ -180,10 +180,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   const int64_t L = xcd_logical(blockIdx.x);
   if (L >= args.tiles) return;
   if constexpr (MODE == kModeWgrad) {
+    // e is the group's place in the order: its index, or its size rank when the split is
+    // skewed (largest groups first; see group_scan)
     wgrad_tile(L, args.tiles_m, args.tiles_n, &e, &tm, &tn);
-    const uint32_t flags = group_scan<NT>(args.splits, args.E, args.R, 0, 0, e, gsm, gi);
+    const uint32_t flags = group_scan<NT>(args.splits, args.E, args.R, 0, 0, e, gsm, gi, true);
     report_status(args.status, flags);
     if (gi.e < 0) return;
+    e = gi.e;
   } else {
     int64_t mt;
     fprop_tile(L, args.tiles_n, &mt, &tn);

@@ -2,7 +2,8 @@
 //
 // The hardware hands workgroup b to XCD b % 8, and each XCD takes its workgroups in increasing
 // b.  xcd_logical() renumbers the launch so that the logical tiles go to the XCDs in runs of
-// 32 (one per CU of an XCD), run r to XCD r % 8: the 32 workgroups running together on one XCD
+// 32 (one per CU of an XCD), eight runs per round, one to each XCD (snake order over the
+// rounds, below): the 32 workgroups running together on one XCD
 // then read the same few A and B panels at the same K positions through that XCD's L2, and
 // every XCD gets the same share of the tiles (also when the tile count is only an upper bound
 // and the spare tiles at its end exit at once).  The logical order packs tiles that share
@@ -29,11 +30,16 @@ BSFP8_HD int64_t xcd_launch_size(int64_t tiles) {
   return (tiles + round - 1) / round * round;
 }
 
-// Logical tile of workgroup b (launch of xcd_launch_size() workgroups): XCD b % 8 takes its
-// j-th workgroup (j = b / 8) from run (j / 32) * 8 + b % 8, position j % 32.
+// Logical tile of workgroup b (launch of xcd_launch_size() workgroups): XCD x = b % 8 takes
+// its j-th workgroup (j = b / 8) from run 8 q + (q even ? x : 7 - x) of round q = j / 32, at
+// position j % 32.  The snake over the rounds balances the XCDs' totals when the runs get
+// shorter along the order (the weight-gradient order puts the largest groups first when the
+// split is skewed): XCD x takes the x-th longest run of one round and the (7-x)-th of the next.
+// Within an XCD the hardware hands the next workgroup to whichever CU frees first.
 BSFP8_HD int64_t xcd_logical(int64_t b) {
-  const int64_t x = b % kXcds, j = b / kXcds;
-  return ((j / kCusPerXcd) * kXcds + x) * kCusPerXcd + j % kCusPerXcd;
+  const int64_t x = b % kXcds, j = b / kXcds, q = j / kCusPerXcd;
+  const int64_t r = q * kXcds + ((q & 1) ? kXcds - 1 - x : x);
+  return r * kCusPerXcd + j % kCusPerXcd;
 }
 
 // Columns per block of the wgrad order for a TM-row tile grid.

@@ -1,8 +1,8 @@
 // Host check of the XCD-aware tile order (csrc/tile_sched.hpp), run by tests/test_tile_addr.py:
 // over a launch of xcd_launch_size() workgroups every tile is produced exactly once, spare
 // workgroups map past the tile count, workgroup 0 gets tile 0, each XCD walks whole runs of 32
-// consecutive logical tiles in increasing order, and the XCDs' shares of the real tiles differ
-// by at most one run.
+// consecutive logical tiles in increasing order (one run per round of 8, in snake order), and
+// the XCDs' shares of the real tiles differ by at most one run.
 #include <cstdint>
 #include <cstdio>
 #include <vector>
@@ -55,8 +55,8 @@ static void check_fprop(int64_t MT, int TN) {
 }
 
 int main() {
-  // xcd_logical is a bijection of [0, B); XCD x takes runs x, x + 8, ... in order; for any
-  // tile count the real tiles per XCD differ by at most one run
+  // xcd_logical is a bijection of [0, B); XCD x takes one run per round (x, then 15 - x, ...)
+  // in increasing order; for any tile count the real tiles per XCD differ by at most one run
   for (int64_t tiles : {1, 31, 32, 255, 256, 257, 1000, 27328, 33792}) {
     const int64_t B = xcd_launch_size(tiles);
     if (B % 256 != 0 || B < tiles || B - tiles >= 256) ++g_fail;
@@ -67,7 +67,9 @@ int main() {
       if (L < 0 || L >= B) { ++g_fail; continue; }
       seen[(size_t)L]++;
       const int x = (int)(b % kXcds);
-      if ((L / kCusPerXcd) % kXcds != x) ++g_fail;  // run r belongs to XCD r % 8
+      // run r of round q = r / 8 belongs to XCD r % 8 (q even) or 7 - r % 8 (q odd): snake order
+      const int64_t run = L / kCusPerXcd, q = run / kXcds;
+      if (((q & 1) ? kXcds - 1 - run % kXcds : run % kXcds) != x) ++g_fail;
       if (L <= prev[x]) ++g_fail;                     // each XCD walks increasing tiles
       prev[x] = L;
       if (L < tiles) real[x]++;
