@@ -180,8 +180,8 @@ __global__ __launch_bounds__(64) void mfma_dot_kernel(const uint8_t* __restrict_
         const int kk = k0 + 8 * h;
         const v2i a = *(const v2i*)(a_q + (int64_t)r * k + kk), b = *(const v2i*)(b_q + (int64_t)r * k + kk);
         if constexpr (KIND == BSFP8_DOT_FP8_LEGACY) {
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b), acc,
-                                                           0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b),
+                                                           acc, 0, 0, 0);
         } else {
           const float fa = __uint_as_float(max((uint32_t)a_s[(kk / 32) * 32 + r] << 23, 0x00400000u));
           const float fb = __uint_as_float(max((uint32_t)b_s[(kk / 32) * 32 + r] << 23, 0x00400000u));

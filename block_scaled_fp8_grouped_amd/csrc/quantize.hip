@@ -33,7 +33,14 @@ namespace bsfp8 {
 constexpr int kQThreads = 256;
 constexpr int kQRows = 128;
 constexpr int kQCols = 128;
-constexpr int kQTilesPerWG = 8;  // consecutive 128-row tiles one workgroup walks
+constexpr int kQTilesPerWG = 8;  // most consecutive 128-row tiles one workgroup walks
+// Tiles per workgroup for a launch of `tiles` 128 x 128 tiles: up to kQTilesPerWG on large
+// inputs (one group scan and one prologue per run of tiles), fewer on small ones so that the
+// launch still spreads over the chip (at least ~1024 workgroups when the input has them).
+static inline int quantize_tiles_per_wg(int64_t tiles) {
+  const int64_t t = tiles / 1024;
+  return (int)(t < 1 ? 1 : t > kQTilesPerWG ? kQTilesPerWG : t);
+}
 
 // Where one 128-row tile of the token buffer lives.
 struct QTile {
@@ -120,7 +127,7 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
     const uint16_t* __restrict__ in, int64_t R, int64_t C, const int32_t* __restrict__ splits, int E,
     float zero_amax_scale, uint8_t* __restrict__ row_q, uint8_t* __restrict__ row_s,
     uint8_t* __restrict__ col_q, void* __restrict__ col_s, const float* noop_flag, uint32_t* status,
-    ActArgs act) {
+    ActArgs act, int tpw) {
   static_assert(ACT == 0 || RECIPE != BSFP8_RECIPE_PER_CHANNEL_128_F32, "the fused activation takes MX recipes");
   // a set flag turns the whole call into a no-op: the outputs (and the status word) keep what
   // they hold, which lets a captured graph skip re-quantizing a cached weight
@@ -134,10 +141,10 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  // workgroup -> (run of kQTilesPerWG row tiles, 128-channel tile), channel tiles fastest: the
+  // workgroup -> (run of tpw row tiles, 128-channel tile), channel tiles fastest: the
   // workgroups in flight together read neighbouring pieces of the same rows
   const int64_t ctiles = (C + kQCols - 1) / kQCols;
-  const int64_t rt0 = (int64_t)blockIdx.x / ctiles * kQTilesPerWG, ctile = (int64_t)blockIdx.x % ctiles;
+  const int64_t rt0 = (int64_t)blockIdx.x / ctiles * tpw, ctile = (int64_t)blockIdx.x % ctiles;
   const int64_t c0 = ctile * kQCols;
   const int ncols = (int)((C - c0) < kQCols ? (C - c0) : kQCols);  // a multiple of 32
   // The GLU gradient pairs its outputs: tile columns [0, 64) are da at input columns
@@ -255,7 +262,7 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
   QTile cur;
   if (!place(rt0, cur)) return;
   load_tile(cur);
-  for (int t = 0; t < kQTilesPerWG; ++t) {
+  for (int t = 0; t < tpw; ++t) {
     if constexpr (ACT != 0) {
       commit_act();
     } else {
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(kQThreads) void grouped_quantize_kernel(
     __syncthreads();
     // the next tile's loads are in flight while this one is quantized
     QTile nxt;
-    const bool more = t + 1 < kQTilesPerWG && place(rt0 + t + 1, nxt);
+    const bool more = t + 1 < tpw && place(rt0 + t + 1, nxt);
     if (more) load_tile(nxt);
     const int64_t row0 = cur.row0, P = cur.p, kp = cur.kp, jblk = cur.jblk;
     const int nlive = cur.nlive;
@@ -468,36 +475,38 @@ static inline int64_t quantize_row_tiles(int64_t R, int E, bool grouped) {
 int launch_grouped_quantize(const void* in, int64_t R, int64_t C, const int32_t* splits, int E, int recipe,
                             int which, float zas, uint8_t* row_q, uint8_t* row_s, uint8_t* col_q, void* col_s,
                             const float* noop_flag, uint32_t* status, hipStream_t stream) {
-  const int64_t gx = (quantize_row_tiles(R, E, splits != nullptr) + kQTilesPerWG - 1) / kQTilesPerWG;
-  const int64_t gy = (C + kQCols - 1) / kQCols;
+  const int64_t rtiles = quantize_row_tiles(R, E, splits != nullptr), gy = (C + kQCols - 1) / kQCols;
+  const int tpw = quantize_tiles_per_wg(rtiles * gy);
+  const int64_t gx = (rtiles + tpw - 1) / tpw;
   if (gx <= 0 || gy <= 0) return BSFP8_OK;
   if (gx * gy > 0x7fffffff) return BSFP8_ERR_SHAPE;
   dim3 grid((unsigned)(gx * gy)), block(kQThreads);
   const uint16_t* x = (const uint16_t*)in;
   const bool row = (which & BSFP8_ROWWISE) != 0, col = (which & BSFP8_COLWISE) != 0;
+  const ActArgs none{nullptr, nullptr, 0};
   if (recipe == BSFP8_RECIPE_MX_1X32_E8M0) {
     if (row && col)
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MX_1X32_E8M0, true, true>), grid, block, 0, stream, x,
-                         R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{nullptr, nullptr, 0});
+                         R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, none, tpw);
     else if (row)
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MX_1X32_E8M0, true, false>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{nullptr, nullptr, 0});
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, none, tpw);
     else
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MX_1X32_E8M0, false, true>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{nullptr, nullptr, 0});
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, none, tpw);
   } else if (recipe == BSFP8_RECIPE_MXFP4_1X32_E8M0) {
     if (row && col)
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MXFP4_1X32_E8M0, true, true>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{nullptr, nullptr, 0});
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, none, tpw);
     else if (row)
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MXFP4_1X32_E8M0, true, false>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{nullptr, nullptr, 0});
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, none, tpw);
     else
       hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_MXFP4_1X32_E8M0, false, true>), grid, block, 0, stream,
-                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{nullptr, nullptr, 0});
+                         x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, none, tpw);
   } else {
     hipLaunchKernelGGL((grouped_quantize_kernel<BSFP8_RECIPE_PER_CHANNEL_128_F32, false, true>), grid, block, 0,
-                       stream, x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, ActArgs{nullptr, nullptr, 0});
+                       stream, x, R, C, splits, E, zas, row_q, row_s, col_q, col_s, noop_flag, status, none, tpw);
   }
   return hipGetLastError() == hipSuccess ? BSFP8_OK : BSFP8_ERR_LAUNCH;
 }
@@ -505,16 +514,16 @@ int launch_grouped_quantize(const void* in, int64_t R, int64_t C, const int32_t*
 template <int RECIPE, int ACT>
 static void launch_act(dim3 grid, dim3 block, hipStream_t stream, bool row, bool col, const uint16_t* x, int64_t R,
                        int64_t C, const int32_t* splits, int E, uint8_t* row_q, uint8_t* row_s, uint8_t* col_q,
-                       void* col_s, uint32_t* status, ActArgs a) {
+                       void* col_s, uint32_t* status, ActArgs a, int tpw) {
   if (row && col)
     hipLaunchKernelGGL((grouped_quantize_kernel<RECIPE, true, true, ACT>), grid, block, 0, stream, x, R, C, splits, E,
-                       0.0f, row_q, row_s, col_q, col_s, nullptr, status, a);
+                       0.0f, row_q, row_s, col_q, col_s, nullptr, status, a, tpw);
   else if (row)
     hipLaunchKernelGGL((grouped_quantize_kernel<RECIPE, true, false, ACT>), grid, block, 0, stream, x, R, C, splits, E,
-                       0.0f, row_q, row_s, col_q, col_s, nullptr, status, a);
+                       0.0f, row_q, row_s, col_q, col_s, nullptr, status, a, tpw);
   else
     hipLaunchKernelGGL((grouped_quantize_kernel<RECIPE, false, true, ACT>), grid, block, 0, stream, x, R, C, splits, E,
-                       0.0f, row_q, row_s, col_q, col_s, nullptr, status, a);
+                       0.0f, row_q, row_s, col_q, col_s, nullptr, status, a, tpw);
 }
 
 int launch_grouped_act_quantize(int act, const void* h, const float* probs, const void* dy, int64_t R, int64_t cols,
@@ -522,8 +531,9 @@ int launch_grouped_act_quantize(int act, const void* h, const float* probs, cons
                                 uint8_t* col_q, void* col_s, uint32_t* status, hipStream_t stream) {
   // output columns: cols, or 2 cols for the GLU gradient (da | db)
   const int64_t C = act == BSFP8_ACT_SWIGLU_GRAD ? 2 * cols : cols;
-  const int64_t gx = (quantize_row_tiles(R, E, true) + kQTilesPerWG - 1) / kQTilesPerWG;
-  const int64_t gy = (C + kQCols - 1) / kQCols;
+  const int64_t rtiles = quantize_row_tiles(R, E, true), gy = (C + kQCols - 1) / kQCols;
+  const int tpw = quantize_tiles_per_wg(rtiles * gy);
+  const int64_t gx = (rtiles + tpw - 1) / tpw;
   if (gx <= 0 || gy <= 0) return BSFP8_OK;
   if (gx * gy > 0x7fffffff) return BSFP8_ERR_SHAPE;
   dim3 grid((unsigned)(gx * gy)), block(kQThreads);
@@ -534,16 +544,20 @@ int launch_grouped_act_quantize(int act, const void* h, const float* probs, cons
     constexpr int RC = decltype(recipe_tag)::value;
     switch (act) {
       case BSFP8_ACT_SRELU:
-        launch_act<RC, 1>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q, col_s, status, a);
+        launch_act<RC, 1>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q, col_s, status, a,
+                          tpw);
         break;
       case BSFP8_ACT_SRELU_GRAD:
-        launch_act<RC, 2>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q, col_s, status, a);
+        launch_act<RC, 2>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q, col_s, status, a,
+                          tpw);
         break;
       case BSFP8_ACT_SWIGLU:
-        launch_act<RC, 3>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q, col_s, status, a);
+        launch_act<RC, 3>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q, col_s, status, a,
+                          tpw);
         break;
       default:
-        launch_act<RC, 4>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q, col_s, status, a);
+        launch_act<RC, 4>(grid, block, stream, row, col, x, R, C, splits, E, row_q, row_s, col_q, col_s, status, a,
+                          tpw);
     }
   };
   if (recipe == BSFP8_RECIPE_MX_1X32_E8M0)
