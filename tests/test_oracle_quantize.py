@@ -1,10 +1,11 @@
 """Pins of the oracle's grouped quantize (both recipes, both layouts) against independent routes.
 
-* Per-channel 128-row recipe: restated with torch CPU ops from the DeepGEMM #365 reproducer's
-  cast (fp32 amax, divide by 448, zero -> sf_val, clamp at 1e-30, multiply by the fp32
-  reciprocal, torch's e4m3 conversion) on the reproducer's shapes, where every expert count
-  is a multiple of 128 and the oracle's colwise layout must equal that page's per-expert
-  K-major pack (each expert's rows transposed and flattened, experts back to back).
+* Per-channel 128-row recipe: the recipe's definition (DeepGEMM #365, "Non-deterministic
+  numerical problem of k_grouped_fp8_gemm_nt_contiguous", reproducer: fp32 amax, divide by
+  448, zero -> sf_val, clamp at 1e-30, multiply by the fp32 reciprocal, e4m3 conversion; each
+  expert's tokens packed K-major, experts back to back) written out as an explicit loop over
+  experts and 128-token blocks in numpy, on that page's shapes, where every expert count is a
+  multiple of 128.
 * MXFP8 1x32: a torch route that takes the exponent from frexp and converts with torch, and
   unpacks the group layout with torch reshapes, on ragged groups (counts not multiples of 32,
   empty groups) — this pins offsets, per-group block restarts and pad lanes.
@@ -57,23 +58,34 @@ def _torch_rowwise_mx(x, T):
     return q.numpy(), (e + 127).to(torch.uint8).t().contiguous().numpy()  # scales [C/32, T]
 
 
-def _torch_per_channel(x_live, sf_val):
-    """Per-channel cast restated with torch: blocks of 128 rows over the live buffer."""
-    T, C = x_live.shape
-    v = x_live.view(T // 128, 128, C)
-    amax = v.abs().float().amax(dim=1)
-    sf = amax / 448.0
-    sf = torch.where(sf == 0, torch.full_like(sf, sf_val), sf).clamp_min(1e-30)
-    q = (v * (1.0 / sf).unsqueeze(1)).to(torch.float8_e4m3fn).view(torch.uint8).view(T, C)
-    return q, sf
-
-
-def _kmajor_pack(q, splits):
-    parts, off = [], 0
+def _per_channel_expected(x_live, splits, sf_val):
+    """The per-channel 128-row recipe written out group by group and block by block, in numpy
+    fp32: for each expert, each 128-token block and every channel, the block's amax, the scale
+    fp32(amax / 448) (sf_val where that is zero, never below 1e-30), and the codes of
+    v * fp32(1 / scale) by torch's e4m3 conversion; each expert's codes laid out channel by
+    channel (its tokens contiguous), experts back to back, scales [block][channel] per expert."""
+    x = x_live.float().numpy()
+    C = x.shape[1]
+    codes, scales, off = [], [], 0
     for k in splits:
-        parts.append(q[off:off + k].t().reshape(-1))
+        assert k % 128 == 0
+        q_e = np.zeros((C, k), np.uint8)
+        s_e = np.zeros((k // 128, C), np.float32)
+        for b in range(k // 128):
+            rows = x[off + 128 * b: off + 128 * (b + 1)]           # [128][C]
+            amax = np.abs(rows).max(axis=0).astype(np.float32)
+            sf = (amax / np.float32(448.0)).astype(np.float32)
+            sf = np.where(sf == 0, np.float32(sf_val), sf).astype(np.float32)
+            sf = np.maximum(sf, np.float32(1e-30))
+            r = (np.float32(1.0) / sf).astype(np.float32)
+            v = (rows * r[None, :]).astype(np.float32)
+            q = torch.from_numpy(np.ascontiguousarray(v)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            q_e[:, 128 * b: 128 * (b + 1)] = q.T
+            s_e[b] = sf
+        codes.append(q_e.reshape(-1))
+        scales.append(s_e.reshape(-1))
         off += k
-    return torch.cat(parts).numpy()
+    return np.concatenate(codes), np.concatenate(scales)
 
 
 @pytest.mark.parametrize("n,sf_val", [(256, 1e-30), (2048, 1e-30), (256, 1.0), (256, 1e-4)])
@@ -84,9 +96,9 @@ def test_per_channel_matches_page_recipe(n, sf_val):
         buf = case[name]
         got = oracle.grouped_quantize(W.bf16_bits(buf), case["splits"], oracle.RECIPE_PC, oracle.COLWISE,
                                       zero_amax_scale=sf_val)
-        q, sf = _torch_per_channel(buf[:T], sf_val)
-        assert np.array_equal(got["col_q"], _kmajor_pack(q, case["splits"])), name
-        assert np.array_equal(got["col_s"].view(np.uint32), sf.numpy().reshape(-1).view(np.uint32)), name
+        q, sf = _per_channel_expected(buf[:T], case["splits"], sf_val)
+        assert np.array_equal(got["col_q"], q), name
+        assert np.array_equal(got["col_s"].view(np.uint32), sf.view(np.uint32)), name
     # the zeroed dy channel of the 128-token experts gets sf_val (clamped at 1e-30)
     got = oracle.grouped_quantize(W.bf16_bits(case["dy"]), case["splits"], oracle.RECIPE_PC, oracle.COLWISE,
                                   zero_amax_scale=sf_val)
@@ -181,13 +193,13 @@ def test_group_independence():
 @pytest.mark.parametrize("sf_val", [0.0, 1e-40, 1e-30])
 def test_per_channel_clamp_on_tiny_amax(sf_val):
     """Blocks whose amax / 448 underflows 1e-30, and a zero-amax replacement below 1e-30, are
-    both clamped to 1e-30 (the reproducer's clamp_min); checked against the torch restatement."""
+    both clamped to 1e-30 (the reproducer's clamp_min); checked against the written-out recipe."""
     rng = np.random.default_rng(2)
     x = torch.from_numpy(rng.standard_normal((256, 64)).astype(np.float32) * 1e-29).to(torch.bfloat16)
     x[:, 3] = 0.0          # zero channel -> sf_val, then the clamp
     x[128:, 5] *= 1e-8     # amax/448 far below 1e-30
     got = oracle.grouped_quantize(W.bf16_bits(x), [256], oracle.RECIPE_PC, oracle.COLWISE, zero_amax_scale=sf_val)
-    q, sf = _torch_per_channel(x, sf_val)
-    assert np.array_equal(got["col_q"], _kmajor_pack(q, [256]))
-    assert np.array_equal(got["col_s"].view(np.uint32), sf.numpy().reshape(-1).view(np.uint32))
+    q, sf = _per_channel_expected(x, [256], sf_val)
+    assert np.array_equal(got["col_q"], q)
+    assert np.array_equal(got["col_s"].view(np.uint32), sf.view(np.uint32))
     assert got["col_s"].reshape(2, 64)[1, 5] == np.float32(1e-30)
