@@ -191,6 +191,39 @@ def mfma_probe(dev, stream, iters=150000):
     return res
 
 
+def lds_dma_probe(dev, stream):
+    """Global -> LDS DMA throughput (the probe library's bsfp8_lds_dma_probe): one workgroup of
+    8 waves per CU, each wave moving 8 KB per round by 16-byte-per-lane LDS DMA, waiting, and
+    meeting the workgroup at a barrier -- the way the GEMMs stage their tiles.  Sources of 64 KB
+    per workgroup (2 MB per XCD: they stay in L2) and of 32 MB per workgroup (8 GB: streamed
+    from HBM).  Mean of 3 launches after a warm-up launch, in GB/s per CU and in total."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "block_scaled_fp8_grouped_amd", "libbsfp8_peak.so")
+    lib = ctypes.CDLL(path)
+    lib.bsfp8_lds_dma_probe.restype = ctypes.c_int
+    lib.bsfp8_lds_dma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    res = {}
+    for name, span, rounds in (("l2_resident", 64 << 10, 2000), ("hbm", 32 << 20, 400)):
+        src = torch.ones(blocks * span, dtype=torch.uint8, device=dev)
+        out = torch.empty(blocks * 512, dtype=torch.int32, device=dev)
+
+        def launch():
+            rc = lib.bsfp8_lds_dma_probe(src.data_ptr(), span, 0, blocks, 8, rounds, out.data_ptr(),
+                                         ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"lds dma probe: error {rc}")
+        ms = _time_calls(launch, stream, 3)
+        nbytes = blocks * 8 * 8192.0 * rounds
+        res[name] = {"GB/s_per_CU": round(nbytes / blocks / (ms / 1e3) / 1e9, 1),
+                     "TB/s": round(nbytes / (ms / 1e3) / 1e12, 2), "us_per_64KB_round": round(ms * 1e3 / rounds, 3)}
+        del src, out
+    return res
+
+
 def graph_leg(graph_step, flag, stream):
     """Capture one step in a HIP graph; mean replay time with the weight quantize running (flag 0)
     and skipped on the device (flag 1)."""
@@ -843,6 +876,10 @@ def main():
     out["mfma_probe"] = dict(probe, note="MFMA-only kernels, no memory traffic in the loop: what the "
                                          "matrix cores sustain on this GPU")
     out["roofline"]["frac_of_probe_bf16"] = round(achieved / probe["bf16_random_TFLOP/s"], 4)
+    log("LDS DMA probe")
+    out["lds_dma_probe"] = dict(lds_dma_probe(dev, stream),
+                                note="global -> LDS DMA as the GEMMs stage tiles: one 8-wave workgroup per CU, "
+                                     "64 KB per round; the MXFP8 GEMMs move 66 KB per CU per K step")
     out["fp8_mfma"]["wgrad_frac_of_fp8_probe"] = round(out["fp8_mfma"]["wgrad_TFLOP/s"] / probe["fp8_random_TFLOP/s"], 4)
     if mx4 is not None:
         out["mxfp4"]["wgrad_frac_of_fp4_probe"] = round(T4 / (mx4["wgrad"] / 1e3) / 1e12

@@ -18,6 +18,7 @@
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int int4v __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -194,6 +195,48 @@ __global__ __launch_bounds__(64) void mfma_dot_kernel(const uint8_t* __restrict_
   }
 }
 
+// Global -> LDS DMA throughput: workgroup b streams its source region (src + b * span, or src
+// itself when `shared`) into LDS, each wave 8 KB per round as 8 buffer_load_dwordx4 ... lds of
+// 64 lanes x 16 bytes into its own 8 KB of LDS, then waits for them and meets the other waves
+// at a barrier; round r of wave w takes the region's bytes from offset
+// (r * waves * 8 KB + w * 8 KB + u * 1 KB) mod span, instruction u.  After the last round every
+// lane XORs the 8 dwords-x4 it moved in that round (read back from LDS) into out[b * 64 * waves
+// + t], so the caller can check that the DMA delivered the bytes it names.
+__device__ __forceinline__ int4v rsrc4(const void* base, uint32_t num_records) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return int4v{__builtin_amdgcn_readfirstlane((int)(uint32_t)a), __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff)),
+               __builtin_amdgcn_readfirstlane((int)num_records), 0x00020000};
+}
+
+__global__ __launch_bounds__(512) void lds_dma_kernel(const uint8_t* __restrict__ src, uint32_t span, int shared,
+                                                      int rounds, uint32_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t sm[8 * 8192];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, nw = blockDim.x >> 6;
+  const uint8_t* base = src + (shared ? 0 : (uint64_t)blockIdx.x * span);
+  const int4v rs = rsrc4(base, span);
+  const uint32_t lds0 =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(sm + w * 8192));
+  const uint32_t per_round = (uint32_t)nw * 8192u;
+  for (int r = 0; r < rounds; ++r) {
+    const uint32_t off = (uint32_t)r * per_round + (uint32_t)w * 8192u + (uint32_t)lane * 16u;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t o = (off + (uint32_t)u * 1024u) % span;
+      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(o), "s"(rs), "{m0}"(lds0 + u * 1024u)
+                   : "memory");
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  uint32_t x = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int4v v = *(const int4v*)(sm + w * 8192 + u * 1024 + lane * 16);
+    x ^= (uint32_t)(v[0] ^ v[1] ^ v[2] ^ v[3]);
+  }
+  out[(uint64_t)blockIdx.x * blockDim.x + t] = x;
+}
+
 double mfma_flops(int kind) {
   switch (kind) {
     case BSFP8_PEAK_BF16: return 2.0 * 32 * 32 * 16;
@@ -257,6 +300,16 @@ extern "C" int bsfp8_mfma_dot_probe(int kind, const uint8_t* a_q, const uint8_t*
     default:
       hipLaunchKernelGGL(mfma_dot_kernel<BSFP8_DOT_FP8_LEGACY>, dim3(1), dim3(64), 0, s, a_q, a_s, b_q, b_s, kk, out);
   }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+extern "C" int bsfp8_lds_dma_probe(const uint8_t* src, int64_t span, int shared, int64_t blocks, int waves,
+                                   int64_t rounds, uint32_t* out, void* stream) {
+  if (src == nullptr || out == nullptr) return -1;
+  if (span < 8192 || span > (int64_t(1) << 31) || span % 1024 != 0) return -3;
+  if (blocks < 1 || blocks > 4096 || waves < 1 || waves > 8 || rounds < 1 || rounds > 100000) return -3;
+  hipLaunchKernelGGL(lds_dma_kernel, dim3((unsigned)blocks), dim3(64 * waves), 0, (hipStream_t)stream, src,
+                     (uint32_t)span, shared ? 1 : 0, (int)rounds, out);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

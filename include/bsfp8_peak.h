@@ -1,7 +1,7 @@
 /*
  * bsfp8_peak.h — probes for MI355X (gfx950), built as libbsfp8_peak.so: the MFMA-only
- * throughput probe, the matrix-instruction precision probe, and the exhaustive check of the
- * reciprocal the fused SwiGLU uses.
+ * throughput probe, the matrix-instruction precision probe, the global -> LDS DMA throughput
+ * probe, and the exhaustive check of the reciprocal the fused SwiGLU uses.
  *
  * Not part of the quantize / GEMM path.  The grouped-GEMM throughput is quoted as a fraction of
  * the matrix-core peak; the published dense peaks assume the full engine clock, which a chip
@@ -72,6 +72,24 @@ int bsfp8_mfma_peak_probe(int kind, const uint32_t* pool, float* out, int64_t bl
  */
 int bsfp8_mfma_dot_probe(int kind, const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
                          int64_t k, float* out, void* stream);
+
+/*
+ * Global -> LDS DMA throughput probe: the path the grouped GEMMs stage their operand tiles by
+ * (buffer_load_dwordx4 with the lds flag, 16 bytes per lane).  `blocks` workgroups of `waves`
+ * waves; workgroup b streams its source region (src + b * span bytes, or src itself for every
+ * workgroup when `shared` is nonzero) into LDS, each wave 8 KB per round (8 instructions of
+ * 1 KB into its own 8 KB of LDS), waits for its loads, then meets the workgroup at a barrier.
+ * Round r of wave w moves the bytes at offsets (r * waves * 8192 + w * 8192 + u * 1024 + 16 l)
+ * mod span (instruction u, lane l), each 16 bytes long.  With span * blocks below the L2 the
+ * sources stay in it; far above it they stream from HBM.  out (uint32 [blocks * 64 * waves]):
+ * thread t = 64 w + l of workgroup b writes, at b * 64 * waves + t, the XOR of the 8 x 4 words
+ * it moved in the last round, as read back from LDS.
+ * Constraints: span a multiple of 1024 in [8192, 2^31]; the source spans blocks * span bytes
+ * (span if shared); 1 <= blocks <= 4096, 1 <= waves <= 8, 1 <= rounds <= 100000.  Returns 0, or
+ * -1 NULL pointer, -3 an argument out of range, -4 the launch failed.  The caller times it.
+ */
+int bsfp8_lds_dma_probe(const uint8_t* src, int64_t span, int shared, int64_t blocks, int waves, int64_t rounds,
+                        uint32_t* out, void* stream);
 
 /* Rate of the real-time counter of `device` in kHz (HIP's wall-clock rate), or -1. */
 int bsfp8_wall_clock_khz(int device);

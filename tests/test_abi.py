@@ -50,8 +50,8 @@ def _peak_lib():
 def test_probe_library_exports_and_rejects_before_launch():
     L = _peak_lib()
     names = _declared(os.path.join(ROOT, "include", "bsfp8_peak.h"))
-    assert names == ["bsfp8_mfma_dot_probe", "bsfp8_mfma_peak_flops", "bsfp8_mfma_peak_probe", "bsfp8_recip_check",
-                     "bsfp8_wall_clock_khz"]
+    assert names == ["bsfp8_lds_dma_probe", "bsfp8_mfma_dot_probe", "bsfp8_mfma_peak_flops", "bsfp8_mfma_peak_probe",
+                     "bsfp8_recip_check", "bsfp8_wall_clock_khz"]
     for n in names:
         assert hasattr(L, n), n
     def probe(kind, pool, out, blocks, iters):
@@ -81,6 +81,16 @@ def test_probe_library_exports_and_rejects_before_launch():
     assert dot(kind=0) == -2 and dot(kind=5) == -2
     assert dot(k=64) == -3 and dot(k=192) == -3 and dot(k=65536 + 128) == -3
     assert dot(aq=P + 16) == -5 and dot(bq=P + 8) == -5
+    L.bsfp8_lds_dma_probe.restype = ctypes.c_int
+    L.bsfp8_lds_dma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+
+    def dma(src=P, span=65536, shared=0, blocks=256, waves=8, rounds=10, out=P):
+        return L.bsfp8_lds_dma_probe(src, span, shared, blocks, waves, rounds, out, None)
+    assert dma(src=None) == -1 and dma(out=None) == -1
+    assert dma(span=4096) == -3 and dma(span=65536 + 512) == -3 and dma(span=(1 << 31) + 1024) == -3
+    assert dma(blocks=0) == -3 and dma(blocks=4097) == -3 and dma(waves=0) == -3 and dma(waves=9) == -3
+    assert dma(rounds=0) == -3 and dma(rounds=100001) == -3
 
 
 def test_binding_constants_match_header():

@@ -82,3 +82,37 @@ def test_recip_equals_ieee_division_on_its_domain():
             assert n == 0, f"first mismatch {int(first.item()) & 0xFFFFFFFF:#x}"
         else:
             assert n > 0  # the check does see a difference where there is one
+
+
+def test_lds_dma_probe_moves_the_named_bytes():
+    """The global -> LDS DMA probe (bench.py's operand-delivery reference) moves exactly the bytes
+    its header names: each lane's XOR of the 8 x 16 bytes of its last round, read back from LDS,
+    equals the XOR of those source bytes computed on the host (private and shared sources)."""
+    import numpy as np
+    L = _lib()
+    L.bsfp8_lds_dma_probe.restype = ctypes.c_int
+    L.bsfp8_lds_dma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    blocks, waves, rounds, span = 6, 8, 5, 24 * 1024
+    g = torch.Generator(device=DEV).manual_seed(11)
+    src = torch.randint(0, 256, (blocks * span,), dtype=torch.uint8, device=DEV, generator=g)
+    host = src.cpu().numpy().view(np.uint32)
+    for shared in (0, 1):
+        flush(f"lds dma probe shared={shared}")
+        out = torch.zeros(blocks * 64 * waves, dtype=torch.int32, device=DEV)
+        assert L.bsfp8_lds_dma_probe(src.data_ptr(), span, shared, blocks, waves, rounds, out.data_ptr(), s) == 0
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint32)
+        r = rounds - 1
+        exp = np.zeros_like(got)
+        for b in range(blocks):
+            base = 0 if shared else b * span
+            for t in range(64 * waves):
+                w, l = divmod(t, 64)
+                x = np.uint32(0)
+                for u in range(8):
+                    o = (r * waves * 8192 + w * 8192 + u * 1024 + 16 * l) % span
+                    x ^= np.bitwise_xor.reduce(host[(base + o) // 4:(base + o) // 4 + 4])
+                exp[b * 64 * waves + t] = x
+        assert np.array_equal(got, exp)
