@@ -275,9 +275,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   for (int u = 0; u < S::A_INS; ++u) a_off[u] = tile_dma_voffset(wave * S::A_INS + u, lane, (uint32_t)lda, 0);
 #pragma unroll
   for (int u = 0; u < S::B_INS; ++u) b_off[u] = tile_dma_voffset(wave * S::B_INS + u, lane, (uint32_t)ldb, 0);
-  auto issue = [&](int kk, uint8_t* __restrict__ base) {
+  // parts [p0, p1) of the step's loads: part 0 the fprop A scales, parts u < A_INS the A data
+  // DMAs, then B_INS of B data, then the scale DMAs
+  auto issue = [&](int kk, uint8_t* __restrict__ base, int p0 = 0, int p1 = 1 << 20) {
     const uint32_t k0 = (uint32_t)kk * BK;
-    if constexpr (MODE == kModeFprop) {
+    if (MODE == kModeFprop && p0 == 0) {
       // A scales first: waiting for these register loads (in settle) then does not wait for
       // the DMAs behind them.  Thread t -> block t / (NT / SBLK) of this K step, rows
       // FA_ROWS * (t % (NT / SBLK)) and the next FA_ROWS - 1 (t / (NT / SBLK) = wave / (NW / SBLK),
@@ -307,16 +309,19 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
     }
 #pragma unroll
     for (int u = 0; u < S::A_INS; ++u) {
+      if (u < p0 || u >= p1) continue;
       const int g = wave * S::A_INS + u;
       if constexpr (SC) asm_dma16(a_rw, lds_of(base + S::A_OFF + g * 1024), a_off[u] + k0);
       else buffer_dma16(a_rs, base + S::A_OFF + g * 1024, a_off[u] + k0);
     }
 #pragma unroll
     for (int u = 0; u < S::B_INS; ++u) {
+      if (S::A_INS + u < p0 || S::A_INS + u >= p1) continue;
       const int g = wave * S::B_INS + u;
       if constexpr (SC) asm_dma16(b_rw, lds_of(base + S::B_OFF + g * 1024), b_off[u] + k0);
       else buffer_dma16(b_rs, base + S::B_OFF + g * 1024, b_off[u] + k0);
     }
+    if (S::A_INS + S::B_INS < p0 || S::A_INS + S::B_INS >= p1) return;
     if constexpr (PC) {
       // one fp32 per row: BM + BN dwords, 64 per instruction
       constexpr int S_INS = (BM + BN) / 64;
@@ -486,9 +491,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
           bs[j][1] = ((const float*)(cur + S::SBF_OFF))[(2 * s + 1) * BN + row];
         }
       }
-      // the next step's loads go out once this half's reads are issued: issued before the first
-      // read of `cur`, the compiler would make every read of the step wait for them
-      if (s == 0 && kk + 1 < nk) issue(kk + 1, nxt);
+      // the next step's loads go out after this half's reads are issued (issued before the first
+      // read of `cur`, the compiler would make every read of the step wait for them), spread in
+      // four parts over this half's MFMA groups, below: issued together, all of every wave's
+      // loads queue at once behind the texture unit and hold back the MFMAs (spread, wgrad and
+      // fprop run 2-3% faster; spread over both halves, 5% slower: the last ones land too late)
       // widen and multiply: 4 bf16 MFMAs (K = 16 each) per fragment pair
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -504,6 +511,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
             if constexpr (PC) part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[i], bw[j], part[i][j], 0, 0, 0);
             else acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[i], bw[j], acc[i][j], 0, 0, 0);
           }
+        if (s == 0 && kk + 1 < nk) {
+          constexpr int NP = S::A_INS + S::B_INS + 1;
+          issue(kk + 1, nxt, t * NP / 4, t == 3 ? (1 << 20) : (t + 1) * NP / 4);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     if constexpr (PC) {
@@ -588,14 +600,23 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
     // software pipeline over the 4 groups: group g + 1's reads go out beside group g's MFMAs;
     // the scheduling fences keep each phase's reads from being hoisted further up (two groups'
     // fragments fit beside the accumulators, four do not)
+    // wgrad spreads the next step's loads in three parts over the first three groups (2% faster,
+    // as in the bf16 step above); the forward issues them together (spread, its A-scale
+    // registers no longer fit beside the fragments and spill)
+    constexpr int NP = S::A_INS + S::B_INS + 1;
+    constexpr int P1 = MODE == kModeWgrad ? NP / 3 : NP, P2 = MODE == kModeWgrad ? 2 * NP / 3 : NP;
     rd(0, 0);
-    issue(kk + 1, nxt);
+    issue(kk + 1, nxt, 0, P1);
     __builtin_amdgcn_sched_barrier(0);
     rd(1, 1);
     mm(0);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (P1 < NP) issue(kk + 1, nxt, P1, P2);
+    __builtin_amdgcn_sched_barrier(0);
     rd(2, 0);
     mm(1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (P2 < NP) issue(kk + 1, nxt, P2);
     __builtin_amdgcn_sched_barrier(0);
     rd(3, 1);
     mm(0);
