@@ -102,6 +102,38 @@ def _ptr(t):
     return t.data_ptr()
 
 
+_U8 = (torch.uint8,)
+_BF16 = (torch.bfloat16, torch.int16)  # bf16 data, or its bits viewed as int16
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+_F32_BITS = (torch.float32, torch.int32)
+
+
+def _dev(t, what, dtypes):
+    """Pointer of an argument that the kernels read or write: a contiguous device tensor of one
+    of ``dtypes`` (checked in that order, so a wrong type is reported before a wrong device), a
+    raw device address (int, not checked), or None.  A host tensor would hand the GPU a host
+    pointer, and a tensor of another element type would be read with the wrong layout (an int64
+    split_sizes tensor reads as sizes k_0, 0, k_1, 0, ...)."""
+    if t is None or not isinstance(t, torch.Tensor):
+        return _ptr(t)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{what}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: a {t.device.type} tensor; the library takes device memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: not contiguous")
+    return t.data_ptr()
+
+
+def _quant(q, key, what, dtypes=_U8):
+    return _dev(q.get(key), f"{what}[{key!r}]", dtypes)
+
+
+def _col_s_types(recipe):
+    return _F32 if (recipe & ~GEMM_FP8_MFMA) == RECIPE_PC else _U8
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -169,9 +201,12 @@ def grouped_quantize(x, split_sizes, recipe, which, out, zero_amax_scale=1e-30, 
     else:
         R, C = capacity_rows, cols
     E = 0 if split_sizes is None else int(split_sizes.numel())
-    rc = lib().bsfp8_grouped_quantize(_ptr(x), R, C, _ptr(split_sizes), E, recipe, which, float(zero_amax_scale),
-                                      _ptr(out.get("row_q")), _ptr(out.get("row_s")), _ptr(out.get("col_q")),
-                                      _ptr(out.get("col_s")), _ptr(noop_flag), _ptr(status), _stream(stream))
+    rc = lib().bsfp8_grouped_quantize(_dev(x, "x", _BF16), R, C, _dev(split_sizes, "split_sizes", _I32), E, recipe,
+                                      which, float(zero_amax_scale), _quant(out, "row_q", "out"),
+                                      _quant(out, "row_s", "out"), _quant(out, "col_q", "out"),
+                                      _quant(out, "col_s", "out", _col_s_types(recipe)),
+                                      _dev(noop_flag, "noop_flag", _F32), _dev(status, "status", _I32),
+                                      _stream(stream))
     _check(rc, "grouped_quantize")
     return out
 
@@ -189,10 +224,11 @@ def grouped_act_quantize(activation, h, split_sizes, recipe, which, out, probs=N
             raise ValueError("grouped_act_quantize: a GLU input has an even number of columns")
         C //= 2
     E = int(split_sizes.numel())
-    rc = lib().bsfp8_grouped_act_quantize(activation, _ptr(h), _ptr(probs), _ptr(dy), R, C, _ptr(split_sizes), E,
-                                          recipe, which, _ptr(out.get("row_q")), _ptr(out.get("row_s")),
-                                          _ptr(out.get("col_q")), _ptr(out.get("col_s")), _ptr(status),
-                                          _stream(stream))
+    rc = lib().bsfp8_grouped_act_quantize(activation, _dev(h, "h", _BF16), _dev(probs, "probs", _F32),
+                                          _dev(dy, "dy", _BF16), R, C, _dev(split_sizes, "split_sizes", _I32), E,
+                                          recipe, which, _quant(out, "row_q", "out"), _quant(out, "row_s", "out"),
+                                          _quant(out, "col_q", "out"), _quant(out, "col_s", "out"),
+                                          _dev(status, "status", _I32), _stream(stream))
     _check(rc, "grouped_act_quantize")
     return out
 
@@ -203,9 +239,12 @@ def grouped_gemm_wgrad(dy_q, n, x_q, h, split_sizes, capacity_rows, recipe, out,
     fp32 [E, n, h] (overwritten, or accumulated into with ``accumulate``).  recipe: the data
     recipe, or RECIPE_MX | GEMM_FP8_MFMA for the MXFP8 operands on the scaled fp8 MFMA."""
     E = int(split_sizes.numel())
-    rc = lib().bsfp8_grouped_gemm_wgrad(_ptr(dy_q["col_q"]), _ptr(dy_q["col_s"]), n, _ptr(x_q["col_q"]),
-                                        _ptr(x_q["col_s"]), h, _ptr(split_sizes), E, capacity_rows, recipe,
-                                        _ptr(out), 1 if accumulate else 0, _ptr(status), _stream(stream))
+    cs = _col_s_types(recipe)
+    rc = lib().bsfp8_grouped_gemm_wgrad(_quant(dy_q, "col_q", "dy_q"), _quant(dy_q, "col_s", "dy_q", cs), n,
+                                        _quant(x_q, "col_q", "x_q"), _quant(x_q, "col_s", "x_q", cs), h,
+                                        _dev(split_sizes, "split_sizes", _I32), E, capacity_rows, recipe,
+                                        _dev(out, "out", _F32_BITS), 1 if accumulate else 0,
+                                        _dev(status, "status", _I32), _stream(stream))
     _check(rc, "grouped_gemm_wgrad")
     return out
 
@@ -217,9 +256,11 @@ def grouped_gemm_fprop(x_q, k, w_q, n, split_sizes, capacity_rows, out, out_dtyp
     operands on the scaled fp8 MFMA); out is [R, n] fp32 or bf16 (rows past
     sum(split_sizes) untouched)."""
     E = int(split_sizes.numel())
-    rc = lib().bsfp8_grouped_gemm_fprop(_ptr(x_q["row_q"]), _ptr(x_q["row_s"]), capacity_rows, k,
-                                        _ptr(w_q["row_q"]), _ptr(w_q["row_s"]), n, _ptr(split_sizes), E, recipe,
-                                        _ptr(out), out_dtype, _ptr(status), _stream(stream))
+    rc = lib().bsfp8_grouped_gemm_fprop(_quant(x_q, "row_q", "x_q"), _quant(x_q, "row_s", "x_q"), capacity_rows, k,
+                                        _quant(w_q, "row_q", "w_q"), _quant(w_q, "row_s", "w_q"), n,
+                                        _dev(split_sizes, "split_sizes", _I32), E, recipe,
+                                        _dev(out, "out", _F32_BITS if out_dtype == OUT_F32 else _BF16), out_dtype,
+                                        _dev(status, "status", _I32), _stream(stream))
     _check(rc, "grouped_gemm_fprop")
     return out
 
@@ -231,8 +272,10 @@ def grouped_gemm_dgrad(dy_q, n, w_q, k, split_sizes, capacity_rows, out, out_dty
     expert); out is [R, k] fp32 or bf16: out[off_e + t] = dy[off_e + t] @ W_e (rows past
     sum(split_sizes) untouched)."""
     E = int(split_sizes.numel())
-    rc = lib().bsfp8_grouped_gemm_dgrad(_ptr(dy_q["row_q"]), _ptr(dy_q["row_s"]), capacity_rows, n,
-                                        _ptr(w_q["col_q"]), _ptr(w_q["col_s"]), k, _ptr(split_sizes), E, recipe,
-                                        _ptr(out), out_dtype, _ptr(status), _stream(stream))
+    rc = lib().bsfp8_grouped_gemm_dgrad(_quant(dy_q, "row_q", "dy_q"), _quant(dy_q, "row_s", "dy_q"), capacity_rows,
+                                        n, _quant(w_q, "col_q", "w_q"), _quant(w_q, "col_s", "w_q"), k,
+                                        _dev(split_sizes, "split_sizes", _I32), E, recipe,
+                                        _dev(out, "out", _F32_BITS if out_dtype == OUT_F32 else _BF16), out_dtype,
+                                        _dev(status, "status", _I32), _stream(stream))
     _check(rc, "grouped_gemm_dgrad")
     return out
