@@ -148,14 +148,16 @@ constexpr int kRankMaxGroups = 256;
 
 // Scans split_sizes[0..E) across the workgroup.  tile_rows > 0 makes each group own
 // ceil(k_e / tile_rows) tiles, and the workgroup's linear tile `tile_index` is mapped to its
-// group (binary search over the tile prefix).  tile_rows == 0 selects group `group_index`, or,
-// with `by_size` and a skewed split (kSkewRatio), the group of size rank `group_index`: groups
-// ordered by decreasing size, equal sizes by index.  The rank depends on split_sizes only.
-// Returns the validation bits (BSFP8_STATUS_*); GroupInfo.e is -1 when the tile is beyond the
-// last group's tiles or when the sizes are invalid.
-template <int NT>
+// group (binary search over the tile prefix).  tile_rows == 0 selects group g = pick(skewed)
+// (pick is called with the same argument by every thread and must return the same value;
+// g < 0: no group), where, with `by_size` and a skewed split (kSkewRatio), skewed is true and g
+// is a size rank: groups ordered by decreasing size, equal sizes by index.  The rank and the
+// skew depend on split_sizes only.  Returns the validation bits (BSFP8_STATUS_*); GroupInfo.e
+// is -1 when there is no group to select (a tile beyond the last group's tiles, g < 0) or when
+// the sizes are invalid.
+template <int NT, class Pick>
 __device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_t capacity,
-                               int tile_rows, int64_t tile_index, int group_index,
+                               int tile_rows, int64_t tile_index, Pick pick,
                                GroupScanSmem<NT>& sm, GroupInfo& gi, bool by_size = false) {
   constexpr int kItems = (kMaxGroups + NT - 1) / NT;
   const int tid = threadIdx.x;
@@ -178,6 +180,8 @@ __device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_
     nlive += k[i] > 0;
   }
   const bool rank = by_size && tile_rows == 0 && E <= kRankMaxGroups;
+  // without ranking the selection is known now and is published by the prefix pass below
+  const int group_index = tile_rows == 0 && !rank ? pick(false) : -1;
   if (rank) {
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
@@ -273,36 +277,39 @@ __device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_
       big = sm.wave_aux[w][0] > big ? sm.wave_aux[w][0] : big;
       live += sm.wave_aux[w][1];
     }
-    if (big * live > (int64_t)kSkewRatio * tot) {
-      // skewed: the group of size rank group_index publishes its extents
-      int64_t ok2 = bk, okp2 = bkp;
+    const bool skewed = big * live > (int64_t)kSkewRatio * tot;
+    const int g = pick(skewed);
+    if (g < 0) return 0;
+    // the selected group (skewed: the one of size rank g; else group g) publishes its extents
+    int64_t ok2 = bk, okp2 = bkp;
 #pragma unroll
-      for (int i = 0; i < kItems; ++i) {
-        const int e = tid * kItems + i;
-        if (e < E) {
-          int r = 0;
+    for (int i = 0; i < kItems; ++i) {
+      const int e = tid * kItems + i;
+      if (e < E) {
+        int r = e;
+        if (skewed) {
+          r = 0;
           for (int f = 0; f < E; ++f) {
             const int32_t kf = sm.tile_prefix[f];
             r += (kf > (int32_t)k[i]) || (kf == (int32_t)k[i] && f < e);
           }
-          if (r == group_index) {
-            sm.info[0] = k[i];
-            sm.info[1] = ok2;
-            sm.info[2] = kp[i];
-            sm.info[3] = okp2;
-            sm.sel = e;
-          }
         }
-        ok2 += k[i];
-        okp2 += kp[i];
+        if (r == g) {
+          sm.info[0] = k[i];
+          sm.info[1] = ok2;
+          sm.info[2] = kp[i];
+          sm.info[3] = okp2;
+          sm.sel = e;
+        }
       }
-      __syncthreads();
-      gi.e = sm.sel;
-    } else {
-      gi.e = group_index;
+      ok2 += k[i];
+      okp2 += kp[i];
     }
+    __syncthreads();
+    gi.e = sm.sel;
     gi.tile = 0;
   } else {
+    if (group_index < 0) return 0;
     gi.e = group_index;
     gi.tile = 0;
   }
@@ -311,6 +318,15 @@ __device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_
   gi.kp = sm.info[2];
   gi.p = sm.info[3];
   return 0;
+}
+
+// group_scan selecting a fixed group index (ignored when tile_rows > 0).
+template <int NT>
+__device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_t capacity,
+                               int tile_rows, int64_t tile_index, int group_index,
+                               GroupScanSmem<NT>& sm, GroupInfo& gi, bool by_size = false) {
+  return group_scan<NT>(splits, E, capacity, tile_rows, tile_index, [group_index](bool) { return group_index; }, sm,
+                        gi, by_size);
 }
 
 // OR the validation bits into the caller's status word (one thread of workgroup 0 only).

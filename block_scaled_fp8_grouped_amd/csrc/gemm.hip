@@ -177,17 +177,25 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   int e, tm, tn;
   // workgroup -> logical tile in the XCD-aware order; workgroup 0 always has tile 0 and is
   // the one that reports the status bits
-  const int64_t L = xcd_logical(blockIdx.x);
-  if (L >= args.tiles) return;
   if constexpr (MODE == kModeWgrad) {
-    // e is the group's place in the order: its index, or its size rank when the split is
-    // skewed (largest groups first; see group_scan)
-    wgrad_tile(L, args.tiles_m, args.tiles_n, &e, &tm, &tn);
-    const uint32_t flags = group_scan<NT>(args.splits, args.E, args.R, 0, 0, e, gsm, gi, true);
+    // e is the group's place in the order: its index, or, when the split is skewed, its size
+    // rank (largest groups first; see group_scan), the tiles then dealt to the XCDs in short
+    // runs (kSkewRun).  The scan decides the skew before the tile is placed.
+    const uint32_t flags = group_scan<NT>(
+        args.splits, args.E, args.R, 0, 0,
+        [&](bool skewed) {
+          const int64_t L = xcd_logical(blockIdx.x, skewed ? kSkewRun : kCusPerXcd);
+          if (L >= args.tiles) return -1;
+          wgrad_tile(L, args.tiles_m, args.tiles_n, &e, &tm, &tn);
+          return e;
+        },
+        gsm, gi, true);
     report_status(args.status, flags);
     if (gi.e < 0) return;
     e = gi.e;
   } else {
+    const int64_t L = xcd_logical(blockIdx.x);
+    if (L >= args.tiles) return;
     int64_t mt;
     fprop_tile(L, args.tiles_n, &mt, &tn);
     const uint32_t flags = group_scan<NT>(args.splits, args.E, args.R, BM, mt, 0, gsm, gi);

@@ -6,8 +6,10 @@
 // rounds, below): the 32 workgroups running together on one XCD
 // then read the same few A and B panels at the same K positions through that XCD's L2, and
 // every XCD gets the same share of the tiles (also when the tile count is only an upper bound
-// and the spare tiles at its end exit at once).  The logical order packs tiles that share
-// operand panels into those runs:
+// and the spare tiles at its end exit at once).  Shorter runs (kSkewRun) trade that sharing for
+// balance when the tiles' lengths differ widely: the weight gradient over a skewed split uses
+// them, so that the longest group's tiles spread over all eight XCDs instead of filling a few.
+// The logical order packs tiles that share operand panels into those runs:
 //   wgrad: per group, blocks of `gn` tile columns; inside a block, tile rows then columns
 //          (TM x gn tiles with gn = 32 / TM share all A panels and gn B panels).
 //   fprop: runs of `gm` m-tiles (rows of the groups' tokens) crossing the TN weight tiles in
@@ -23,6 +25,7 @@ namespace bsfp8 {
 
 constexpr int kXcds = 8;
 constexpr int kCusPerXcd = 32;
+constexpr int kSkewRun = 4;  // run length for a skewed weight-gradient split
 
 // Launch size for `tiles` logical tiles: a whole number of rounds of 8 runs of 32.
 BSFP8_HD int64_t xcd_launch_size(int64_t tiles) {
@@ -30,16 +33,17 @@ BSFP8_HD int64_t xcd_launch_size(int64_t tiles) {
   return (tiles + round - 1) / round * round;
 }
 
-// Logical tile of workgroup b (launch of xcd_launch_size() workgroups): XCD x = b % 8 takes
-// its j-th workgroup (j = b / 8) from run 8 q + (q even ? x : 7 - x) of round q = j / 32, at
-// position j % 32.  The snake over the rounds balances the XCDs' totals when the runs get
-// shorter along the order (the weight-gradient order puts the largest groups first when the
-// split is skewed): XCD x takes the x-th longest run of one round and the (7-x)-th of the next.
-// Within an XCD the hardware hands the next workgroup to whichever CU frees first.
-BSFP8_HD int64_t xcd_logical(int64_t b) {
-  const int64_t x = b % kXcds, j = b / kXcds, q = j / kCusPerXcd;
+// Logical tile of workgroup b (launch of xcd_launch_size() workgroups) for runs of `run` tiles
+// (a divisor of 32): XCD x = b % 8 takes its j-th workgroup (j = b / 8) from run
+// 8 q + (q even ? x : 7 - x) of round q = j / run, at position j % run.  The snake over the
+// rounds balances the XCDs' totals when the runs get shorter along the order (the
+// weight-gradient order puts the largest groups first when the split is skewed): XCD x takes
+// the x-th longest run of one round and the (7-x)-th of the next.  Within an XCD the hardware
+// hands the next workgroup to whichever CU frees first.
+BSFP8_HD int64_t xcd_logical(int64_t b, int run = kCusPerXcd) {
+  const int64_t x = b % kXcds, j = b / kXcds, q = j / run;
   const int64_t r = q * kXcds + ((q & 1) ? kXcds - 1 - x : x);
-  return r * kCusPerXcd + j % kCusPerXcd;
+  return r * run + j % run;
 }
 
 // Columns per block of the wgrad order for a TM-row tile grid.
