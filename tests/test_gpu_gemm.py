@@ -109,6 +109,24 @@ def test_wgrad_accumulate_parity_and_empty_untouched(recipe):
     check_wgrad(dy, x, splits, recipe, accumulate=True, mg=mg, label=f"acc r{recipe}")
 
 
+@pytest.mark.parametrize("recipe", [bs.RECIPE_MX, bs.RECIPE_PC])
+def test_wgrad_skewed_split_many_tiles(recipe):
+    """A skewed split (largest group above twice the mean non-empty size) over more tiles than
+    one round of 256 workgroups: the kernel takes its groups largest first and deals the tiles
+    to the XCDs in short runs; every expert is checked against the oracle."""
+    rng = np.random.default_rng(11)
+    splits = [int(c) for c in W.zipf_counts(rng, 40, 36, 7000)]
+    live = [k for k in splits if k > 0]
+    assert max(live) * len(live) > 2 * sum(live), splits  # the kernel's skew condition
+    n, h = 512, 1024
+    tiles = len(splits) * (n // 256) * (h // 256) if recipe == bs.RECIPE_MX else len(splits) * (n // 128) * (h // 128)
+    assert tiles > 256
+    flush(f"wgrad skewed recipe={recipe} splits={splits}")
+    R = sum(splits) + 77
+    dy, x = _operands(R, n, h, splits, seed=12)
+    check_wgrad(dy, x, splits, recipe, label=f"skewed r{recipe}")
+
+
 def test_wgrad_zero_channel_gives_zero_row():
     """DeepGEMM #365 structure: one all-zero dy channel in each 128-token expert."""
     case = W.deepgemm_case(DEV, 256, 256, R=1024)
