@@ -115,15 +115,6 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 // is the fp32 subnormal 2^-127 (0x00400000, below every byte << 23 for byte >= 1).
 __device__ __forceinline__ float e8m0_value(uint32_t byte) { return __uint_as_float(max(byte << 23, 0x00400000u)); }
 
-// Orders a wave's LDS writes before its later LDS reads from other lanes of the same wave (the
-// fence keeps the compiler from moving LDS accesses across; the wait drains the wave's LDS queue).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Eight e4m3 codes (two dwords) -> eight bf16 values times `scale`.
 __device__ __forceinline__ v8bf widen8(int d0, int d1, float scale) {
   const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d0, scale, false);
@@ -725,26 +716,20 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   }
 
   // ---------------- epilogue ----------------
-  // Each wave moves its own WM x WN block to HBM, one 32-row fragment row at a time, through a
-  // private LDS buffer, so no wave waits for another: the fragments of the row are written into
-  // a row-major fp32 block (row pitch padded so that the two 32-lane halves of a fragment write,
-  // rows 4 apart, fall in different banks), read back as 16-byte runs of whole rows (WN / 4
-  // lanes per row) and stored.  With accumulation the main_grad loads of the next fragment row
-  // are in flight while this one is moved.  Fragment element r of lane (h, l32) sits at row
-  // 8 (r / 4) + 4 h + r % 4, column l32 of its 32 x 32 fragment.
+  // Each wave stores its own WM x WN block straight from its accumulator registers: element r of
+  // fragment (i, j) of lane (h, l32) is row i*32 + 8(r/4) + 4h + r%4, column j*32 + l32 of the
+  // block, so one store instruction writes two row segments of 32 outputs (whole 128-byte lines
+  // for fp32; the two halves of a bf16 line come from the fragments j and j + 1 and meet in
+  // L2).  No LDS and no wave waits for another.  With accumulation the main_grad values of the
+  // next fragment row are in flight while this one is added and stored.  (Staging each fragment
+  // row through LDS into 16-byte runs of whole rows was as fast on the 128-expert shapes and
+  // 10% slower on the 32-expert Zipf wgrad, whose short tiles make the epilogue a larger share.)
   // Global accesses go through a buffer resource that spans exactly the block's valid rows
   // (from its first column to the end of its last valid row); lanes past the last column get
   // an offset beyond that range.  The hardware drops out-of-range stores and returns zeros for
   // out-of-range loads, so every access is issued unconditionally.
   {
-    constexpr int PITCH = WN + 8;  // fp32 words per LDS row
-    constexpr int LPR = WN / 4;    // lanes per row
-    constexpr int RPI = 64 / LPR;  // rows per instruction
-    constexpr int IPF = 32 / RPI;  // instructions per fragment row
     constexpr int ES = (MODE == kModeFprop && OUT == BSFP8_OUT_BF16) ? 2 : 4;  // output element bytes
-    static_assert(NW * 32 * PITCH * 4 <= 2 * S::STAGE && 64 % LPR == 0, "epilogue buffers");
-    float* buf = (float*)smem + wave * 32 * PITCH;
-    const int c4 = lane % LPR, rl = lane / LPR;
     const int64_t row0 = a_row0 + wm * WM;  // first row of this wave's block within the group
     const int64_t col0 = b_row0 + wn * WN;  // first column of the block
     const int64_t left = (MODE == kModeWgrad ? args.M : (int64_t)gi.k) - row0;
@@ -755,41 +740,44 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((uint8_t*)args.out + org * ES, (short)0, (int)nbytes, 0x00020000);
     // byte offsets below WM * N * ES < 2^31 (host bound on N); a lane past the last column starts
-    // at 2^31, so all its offsets stay at or above 2^31 > nbytes
-    const uint32_t lane_off = (uint32_t)(rl * args.N + 4 * c4) * ES | (col0 + 4 * c4 < args.N ? 0u : 0x80000000u);
-    const uint32_t row_step = (uint32_t)(RPI * args.N * ES), frag_step = (uint32_t)(32 * args.N * ES);
-    auto off = [&](int i, int it) { return lane_off + (uint32_t)i * frag_step + (uint32_t)it * row_step; };
-    v4f mg[2][IPF];
-    auto load_mg = [&](int i, v4f* m) {
+    // at 2^31, so all its offsets stay at or above 2^31 > nbytes (and below 2^32)
+    uint32_t loff[FN];
 #pragma unroll
-      for (int it = 0; it < IPF; ++it)
-        m[it] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off(i, it), 0, 0));
+    for (int j = 0; j < FN; ++j)
+      loff[j] = (uint32_t)((4 * h) * args.N + j * 32 + l32) * (uint32_t)ES |
+                (col0 + j * 32 + l32 < args.N ? 0u : 0x80000000u);
+    auto voff = [&](int i, int j, int r) {
+      return loff[j] + (uint32_t)((i * 32 + 8 * (r >> 2) + (r & 3)) * args.N) * (uint32_t)ES;
     };
-    if constexpr (MODE == kModeWgrad && ACCUM) load_mg(0, mg[0]);
+    auto put = [&](float v, int i, int j, int r) {
+      if constexpr (ES == 4) __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), rs, (int)voff(i, j, r), 0, 0);
+      else __builtin_amdgcn_raw_buffer_store_b16((short)f32_to_bf16_rne(v), rs, (int)voff(i, j, r), 0, 0);
+    };
+    if constexpr (MODE == kModeWgrad && ACCUM) {
+      v16f m[2][FN];
+      auto load = [&](int i, v16f* d) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if constexpr (MODE == kModeWgrad && ACCUM) {
-        if (i + 1 < FM) load_mg(i + 1, mg[(i + 1) & 1]);
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            d[j][r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)voff(i, j, r), 0, 0));
+      };
+      load(0, m[0]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if (i + 1 < FM) load(i + 1, m[(i + 1) & 1]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) put(m[i & 1][j][r] + acc[i][j][r], i, j, r);
       }
+    } else {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) buf[(8 * (r >> 2) + 4 * h + (r & 3)) * PITCH + j * 32 + l32] = acc[i][j][r];
-      wave_lds_sync();
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int it = 0; it < IPF; ++it) {
-        v4f v = *(const v4f*)(buf + (rl + it * RPI) * PITCH + 4 * c4);
-        if constexpr (MODE == kModeWgrad && ACCUM) v = mg[i & 1][it] + v;
-        if constexpr (ES == 4) {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rs, (int)off(i, it), 0, 0);
-        } else {
-          v2i w;
-          w[0] = (int)((uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16));
-          w[1] = (int)((uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16));
-          __builtin_amdgcn_raw_buffer_store_b64(w, rs, (int)off(i, it), 0, 0);
-        }
-      }
-      wave_lds_sync();  // every lane has read the buffer before the next fragment row is written
+          for (int r = 0; r < 16; ++r) put(acc[i][j][r], i, j, r);
     }
   }
 }
