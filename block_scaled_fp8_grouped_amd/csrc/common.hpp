@@ -95,13 +95,11 @@ __device__ __forceinline__ uint32_t e2m1x8(float a0, float a1, float a2, float a
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (inputs are finite sums).
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// fp32 -> bf16 bits, rounded to nearest even by the hardware conversion (v_cvt_pk_bf16_f32, one
+// instruction): on every non-NaN fp32 it equals the integer round-to-nearest-even of the top 16
+// bits, and a NaN stays a NaN (checked over all 2^32 patterns on the GPU: bsfp8_bf16_cvt_check
+// in the probe library).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // ---------------------------------------------------------------------------------------------
 // Group scan

@@ -751,7 +751,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
     };
     auto put = [&](float v, int i, int j, int r) {
       if constexpr (ES == 4) __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), rs, (int)voff(i, j, r), 0, 0);
-      else __builtin_amdgcn_raw_buffer_store_b16((short)f32_to_bf16_rne(v), rs, (int)voff(i, j, r), 0, 0);
+      else __builtin_amdgcn_raw_buffer_store_b16((short)f32_to_bf16(v), rs, (int)voff(i, j, r), 0, 0);
     };
     if constexpr (MODE == kModeWgrad && ACCUM) {
       v16f m[2][FN];

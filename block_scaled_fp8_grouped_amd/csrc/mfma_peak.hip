@@ -2,7 +2,8 @@
 // sustain on this machine with nothing else in the loop, to set the grouped GEMMs against.  The
 // precision probe: one 32 x 32 block-scaled e4m3 dot product through each candidate matrix
 // instruction, which shows why the MXFP8 GEMMs run the bf16 MFMA on widened codes.  And the
-// check of the fast reciprocal that the fused SwiGLU uses against the IEEE division.
+// checks of the fast reciprocal that the fused SwiGLU uses against the IEEE division, and of the
+// GEMMs' hardware fp32 -> bf16 conversion against an integer round-to-nearest-even.
 //
 // Each wave holds its A and B operands in registers (read once from the caller's pool) and
 // issues 4 independent accumulator chains of one instruction per iteration; with 2 workgroups
@@ -92,6 +93,41 @@ __global__ __launch_bounds__(256) void recip_check_kernel(uint32_t lo, uint32_t 
     const uint32_t bits = lo + (uint32_t)j;
     const float d = __uint_as_float(bits);
     if (__float_as_uint(bsfp8::recip_rn(d)) != __float_as_uint(1.0f / d)) {
+      ++local;
+      low = low < bits ? low : bits;
+    }
+  }
+  if (local) {
+    atomicAdd(mism, local);
+    atomicMin(first, low);
+  }
+}
+
+// The GEMMs' fp32 -> bf16 output conversion (the hardware one, bsfp8::f32_to_bf16) against an
+// integer rounding of the fp32 bits written out here: mode 0 round to nearest even (carry
+// 0x7fff plus the kept lowest bit into the top half), mode 1 truncation (a reference that
+// must differ, so the check is seen to catch differences).  A NaN input must give a bf16 NaN;
+// any other input the reference's bits.  64 consecutive patterns per thread from lo;
+// mismatching patterns are counted and the lowest one kept.
+__global__ __launch_bounds__(256) void bf16_cvt_check_kernel(uint32_t lo, uint32_t count, int mode,
+                                                             unsigned long long* mism, uint32_t* first) {
+  const uint64_t base = ((uint64_t)blockIdx.x * 256 + threadIdx.x) * 64;
+  unsigned long long local = 0;
+  uint32_t low = 0xFFFFFFFFu;
+  for (int i = 0; i < 64; ++i) {
+    const uint64_t j = base + i;
+    if (j >= count) break;
+    const uint32_t bits = lo + (uint32_t)j;
+    const uint32_t got = bsfp8::f32_to_bf16(__uint_as_float(bits));
+    const bool nan_in = (bits & 0x7f800000u) == 0x7f800000u && (bits & 0x007fffffu) != 0;
+    bool bad;
+    if (nan_in) {
+      bad = (got & 0x7f80u) != 0x7f80u || (got & 0x007fu) == 0;
+    } else {
+      const uint32_t want = mode == 0 ? (bits + 0x7fffu + ((bits >> 16) & 1u)) >> 16 : bits >> 16;
+      bad = got != (want & 0xffffu);
+    }
+    if (bad) {
       ++local;
       low = low < bits ? low : bits;
     }
@@ -310,6 +346,18 @@ extern "C" int bsfp8_lds_dma_probe(const uint8_t* src, int64_t span, int shared,
   if (blocks < 1 || blocks > 4096 || waves < 1 || waves > 8 || rounds < 1 || rounds > 100000) return -3;
   hipLaunchKernelGGL(lds_dma_kernel, dim3((unsigned)blocks), dim3(64 * waves), 0, (hipStream_t)stream, src,
                      (uint32_t)span, shared ? 1 : 0, (int)rounds, out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+extern "C" int bsfp8_bf16_cvt_check(uint32_t lo_bits, uint32_t hi_bits, int mode, unsigned long long* mismatches,
+                                    uint32_t* first_bits, void* stream) {
+  if (mismatches == nullptr || first_bits == nullptr) return -1;
+  if (mode != 0 && mode != 1) return -2;
+  if (hi_bits <= lo_bits) return -3;
+  const uint32_t count = hi_bits - lo_bits;
+  const uint64_t blocks = ((uint64_t)count + 64 * 256 - 1) / (64 * 256);
+  hipLaunchKernelGGL(bf16_cvt_check_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, lo_bits,
+                     count, mode, mismatches, first_bits);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -1,7 +1,8 @@
 /*
  * bsfp8_peak.h — probes for MI355X (gfx950), built as libbsfp8_peak.so: the MFMA-only
  * throughput probe, the matrix-instruction precision probe, the global -> LDS DMA throughput
- * probe, and the exhaustive check of the reciprocal the fused SwiGLU uses.
+ * probe, and the exhaustive checks of the reciprocal the fused SwiGLU uses and of the GEMMs'
+ * fp32 -> bf16 output conversion.
  *
  * Not part of the quantize / GEMM path.  The grouped-GEMM throughput is quoted as a fraction of
  * the matrix-core peak; the published dense peaks assume the full engine clock, which a chip
@@ -104,6 +105,19 @@ int bsfp8_wall_clock_khz(int device);
  */
 int bsfp8_recip_check(uint32_t lo_bits, uint32_t hi_bits, unsigned long long* mismatches, uint32_t* first_bits,
                       void* stream);
+
+/*
+ * Check of the fp32 -> bf16 conversion that the GEMMs' bf16 outputs go through (the hardware
+ * round-to-nearest-even conversion) for every fp32 bit pattern in [lo_bits, hi_bits): against
+ * an integer round-to-nearest-even of the fp32 bits (mode 0), or against truncation (mode 1, a
+ * reference that differs, to show the check sees differences).  A NaN must give a bf16 NaN.
+ * *mismatches (device uint64, zeroed by the caller) is increased by the number of patterns
+ * that differ; *first_bits (device uint32, set to 0xFFFFFFFF by the caller) is lowered to the
+ * smallest differing pattern.
+ * Returns 0, -1 NULL pointer, -2 unknown mode, -3 empty range, -4 the launch failed.
+ */
+int bsfp8_bf16_cvt_check(uint32_t lo_bits, uint32_t hi_bits, int mode, unsigned long long* mismatches,
+                         uint32_t* first_bits, void* stream);
 
 /* Dense FLOPs one probe launch performs (2 M N K per MFMA), or 0 for an invalid kind. */
 double bsfp8_mfma_peak_flops(int kind, int64_t blocks, int64_t iters);

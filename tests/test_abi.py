@@ -50,7 +50,7 @@ def _peak_lib():
 def test_probe_library_exports_and_rejects_before_launch():
     L = _peak_lib()
     names = _declared(os.path.join(ROOT, "include", "bsfp8_peak.h"))
-    assert names == ["bsfp8_lds_dma_probe", "bsfp8_mfma_dot_probe", "bsfp8_mfma_peak_flops", "bsfp8_mfma_peak_probe",
+    assert names == ["bsfp8_bf16_cvt_check", "bsfp8_lds_dma_probe", "bsfp8_mfma_dot_probe", "bsfp8_mfma_peak_flops", "bsfp8_mfma_peak_probe",
                      "bsfp8_recip_check", "bsfp8_wall_clock_khz"]
     for n in names:
         assert hasattr(L, n), n
@@ -68,6 +68,11 @@ def test_probe_library_exports_and_rejects_before_launch():
     L.bsfp8_recip_check.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     assert L.bsfp8_recip_check(1, 5, None, P, None) == -1 and L.bsfp8_recip_check(1, 5, P, None, None) == -1
     assert L.bsfp8_recip_check(5, 5, P, P, None) == -3 and L.bsfp8_recip_check(6, 5, P, P, None) == -3
+    L.bsfp8_bf16_cvt_check.restype = ctypes.c_int
+    L.bsfp8_bf16_cvt_check.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    assert L.bsfp8_bf16_cvt_check(1, 5, 0, None, P, None) == -1 and L.bsfp8_bf16_cvt_check(1, 5, 0, P, None, None) == -1
+    assert L.bsfp8_bf16_cvt_check(1, 5, 2, P, P, None) == -2 and L.bsfp8_bf16_cvt_check(5, 5, 0, P, P, None) == -3
     L.bsfp8_mfma_dot_probe.restype = ctypes.c_int
     L.bsfp8_mfma_dot_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]

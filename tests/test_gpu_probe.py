@@ -84,6 +84,31 @@ def test_recip_equals_ieee_division_on_its_domain():
             assert n > 0  # the check does see a difference where there is one
 
 
+def test_bf16_output_conversion_is_round_to_nearest_even():
+    """The GEMMs' bf16 outputs go through the hardware fp32 -> bf16 conversion: over all 2^32 fp32
+    patterns it equals an integer round-to-nearest-even of the fp32 bits (NaN stays NaN), and the
+    same check against truncation does report differences."""
+    flush("bf16 conversion check")
+    L = _lib()
+    L.bsfp8_bf16_cvt_check.restype = ctypes.c_int
+    L.bsfp8_bf16_cvt_check.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for mode, ranges in ((0, ((0, 0x80000000), (0x80000000, 0xFFFFFFFF), (0xFFFFFFFE, 0xFFFFFFFF))),
+                         (1, ((0x3F800000, 0x3F810000),))):
+        mism = torch.zeros(1, dtype=torch.int64, device=DEV)
+        first = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        for lo, hi in ranges:
+            assert L.bsfp8_bf16_cvt_check(lo, hi, mode, mism.data_ptr(), first.data_ptr(), s) == 0
+        torch.cuda.synchronize()
+        n = int(mism.item())
+        flush(f"bf16 conversion, mode {mode}: {n} mismatches")
+        if mode == 0:
+            assert n == 0, f"first mismatch {int(first.item()) & 0xFFFFFFFF:#x}"
+        else:
+            assert n > 0  # truncation differs from rounding on about half of the patterns
+
+
 def test_lds_dma_probe_moves_the_named_bytes():
     """The global -> LDS DMA probe (bench.py's operand-delivery reference) moves exactly the bytes
     its header names: each lane's XOR of the 8 x 16 bytes of its last round, read back from LDS,
