@@ -129,8 +129,8 @@ template <int NT>
 struct GroupScanSmem {
   int64_t wave_tot[NT / 64][3];
   int64_t wave_aux[NT / 64][2];  // per wave: largest size, live groups
-  int32_t tile_prefix[kMaxGroups + 1];
-  int64_t info[4];
+  int32_t tile_prefix[kMaxGroups + 1];  // the sizes, for the ranking
+  int64_t info[5];
   int32_t sel;
   uint32_t flags;
 };
@@ -190,7 +190,10 @@ __device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_
   }
   // exclusive prefix of the per-thread sums across the workgroup
   const int64_t ik = wave_inclusive_scan(sk), ikp = wave_inclusive_scan(skp), itl = wave_inclusive_scan(stl);
-  if (tid == 0) sm.flags = 0;
+  if (tid == 0) {
+    sm.flags = 0;
+    sm.sel = -1;
+  }
   if (lane == 63) {
     sm.wave_tot[wave][0] = ik;
     sm.wave_tot[wave][1] = ikp;
@@ -209,7 +212,7 @@ __device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_
   }
   __syncthreads();
   if (bad) atomicOr(&sm.flags, bad);
-  int64_t bk = ik - sk, bkp = ikp - skp, btl = itl - stl, tot = 0, tot_tl = 0;
+  int64_t bk = ik - sk, bkp = ikp - skp, btl = itl - stl, tot = 0;
   for (int w = 0; w < NT / 64; ++w) {
     if (w < wave) {
       bk += sm.wave_tot[w][0];
@@ -217,20 +220,23 @@ __device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_
       btl += sm.wave_tot[w][2];
     }
     tot += sm.wave_tot[w][0];
-    tot_tl += sm.wave_tot[w][2];
   }
-  if (tid == 0 && tile_rows > 0) sm.tile_prefix[E] = (int32_t)tot_tl;
-  // per-entry exclusive prefixes; publish the tile prefix and the selected group's extents
+  // per-entry exclusive prefixes; the selected group publishes its extents: with tiles, the one
+  // whose tile range [otl, otl + tl) holds tile_index (none when it is past the last group's
+  // tiles), else group group_index
   int64_t ok = bk, okp = bkp, otl = btl;
 #pragma unroll
   for (int i = 0; i < kItems; ++i) {
     const int e = tid * kItems + i;
-    if (e < E && tile_rows > 0) sm.tile_prefix[e] = (int32_t)otl;
-    if (tile_rows == 0 && e == group_index && e < E) {
+    const bool sel = tile_rows > 0 ? e < E && tile_index >= otl && tile_index < otl + tl[i]
+                                   : e == group_index && e < E;
+    if (sel) {
       sm.info[0] = k[i];
       sm.info[1] = ok;
       sm.info[2] = kp[i];
       sm.info[3] = okp;
+      sm.info[4] = otl;
+      sm.sel = e;
     }
     ok += k[i];
     okp += kp[i];
@@ -242,33 +248,9 @@ __device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_
   gi.e = -1;
   if (flags) return flags;
   if (tile_rows > 0) {
-    const int64_t total = sm.tile_prefix[E];
-    if (tile_index >= total) return 0;
-    int lo = 0, hi = E;  // tile_prefix[lo] <= tile_index < tile_prefix[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (sm.tile_prefix[mid] <= tile_index) lo = mid; else hi = mid;
-    }
-    // this workgroup's group is lo; its owner thread publishes the extents
-    __syncthreads();
-    {
-      int64_t ok2 = bk, okp2 = bkp;
-#pragma unroll
-      for (int i = 0; i < kItems; ++i) {
-        const int e = tid * kItems + i;
-        if (e == lo) {
-          sm.info[0] = k[i];
-          sm.info[1] = ok2;
-          sm.info[2] = kp[i];
-          sm.info[3] = okp2;
-        }
-        ok2 += k[i];
-        okp2 += kp[i];
-      }
-    }
-    __syncthreads();
-    gi.e = lo;
-    gi.tile = sm.tile_prefix[lo];
+    if (sm.sel < 0) return 0;  // past the last group's tiles
+    gi.e = sm.sel;
+    gi.tile = sm.info[4];
   } else if (rank) {
     int64_t big = 0, live = 0;
     for (int w = 0; w < NT / 64; ++w) {
