@@ -192,7 +192,11 @@ __device__ uint32_t group_scan(const int32_t* __restrict__ splits, int E, int64_
   const int64_t ik = wave_inclusive_scan(sk), ikp = wave_inclusive_scan(skp), itl = wave_inclusive_scan(stl);
   if (tid == 0) {
     sm.flags = 0;
-    sm.sel = -1;
+    // With tiles, no group may own tile_index, so the selection starts unset; a selection by
+    // index or rank always writes it.  Only the tile kernels clear it: in the weight-gradient
+    // kernel the same store left every result bit unchanged but its launches fetched 35 -> 59
+    // GB from beyond L2 (measured A/B on the 128-expert shape; the cause was not found).
+    if (tile_rows > 0) sm.sel = -1;
   }
   if (lane == 63) {
     sm.wave_tot[wave][0] = ik;
