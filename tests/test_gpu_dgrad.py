@@ -72,7 +72,7 @@ def check_dgrad(dy, w, splits, out_dtype, cols_sel=None, experts=None, label="")
 
 
 @pytest.mark.parametrize("out_dtype", [bs.OUT_F32, bs.OUT_BF16])
-@pytest.mark.parametrize("n,k", [(256, 256), (96, 320), (160, 64), (512, 512)])
+@pytest.mark.parametrize("n,k", [(256, 256), (96, 320), (160, 64), (512, 512), (128, 96)])
 @pytest.mark.parametrize("splits", [[0, 1, 31, 32, 33, 127, 128, 129, 256], [300, 0, 45, 1, 200], [600]])
 def test_dgrad_parity(out_dtype, n, k, splits):
     flush(f"dgrad dtype={out_dtype} n={n} k={k} splits={splits}")

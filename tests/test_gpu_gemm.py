@@ -8,7 +8,8 @@
 * padding invariance (TE #3484 expected behaviour): capacity tails of 0.0, 3.0 or random bits
   give results bitwise equal to the unpadded run.
 * device status word: a negative size or sum(k_e) > capacity sets its bit and nothing is written.
-Tiles: n/h/N not multiples of 256 (partial tiles) and K not a multiple of 128 (fprop tail).
+Tiles: n/h/N not multiples of 256 (partial tiles; output widths of 96 leave a wave's second
+32-column fragment past the last column) and K not a multiple of 128 (fprop tail).
 """
 import numpy as np
 import pytest
@@ -88,7 +89,7 @@ def check_wgrad(dy, x, splits, recipe, accumulate=False, mg=None, zas=1e-30, row
 # ------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("recipe", [bs.RECIPE_MX, bs.RECIPE_PC])
-@pytest.mark.parametrize("n,h", [(256, 256), (96, 320), (512, 64)])
+@pytest.mark.parametrize("n,h", [(256, 256), (96, 320), (512, 64), (64, 96)])
 @pytest.mark.parametrize("splits", [[0, 1, 31, 32, 33, 127, 128, 129, 256], [300, 0, 45, 1, 200], [1000]])
 def test_wgrad_store_parity(recipe, n, h, splits):
     flush(f"wgrad store recipe={recipe} n={n} h={h} splits={splits}")
@@ -240,7 +241,7 @@ def check_fprop(x, w, splits, N, out_dtype, cols_sel=None, label=""):
 
 
 @pytest.mark.parametrize("out_dtype", [bs.OUT_F32, bs.OUT_BF16])
-@pytest.mark.parametrize("K,N", [(256, 256), (96, 320), (160, 64), (512, 512)])
+@pytest.mark.parametrize("K,N", [(256, 256), (96, 320), (160, 64), (512, 512), (256, 96)])
 @pytest.mark.parametrize("splits", [[0, 1, 31, 32, 33, 127, 128, 129, 256], [300, 0, 45, 1, 200], [600]])
 def test_fprop_parity(out_dtype, K, N, splits):
     flush(f"fprop dtype={out_dtype} K={K} N={N} splits={splits}")
