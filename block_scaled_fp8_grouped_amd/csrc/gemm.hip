@@ -132,11 +132,13 @@ struct GemmShape {
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int NW = WAVES_M * WAVES_N, NT = NW * 64;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  // LDS stage: A rows, B rows, then scales (MX: [SBLK blocks][rows] E8M0 bytes as they arrive,
-  // and for the widened MXFP8 path the same decoded to fp32 [4 blocks][rows]; PC: one fp32 per row)
+  // LDS stage: A rows, B rows, then scales (the scaled-MFMA paths: [SBLK blocks][rows] E8M0 bytes
+  // as they arrive; the widened MXFP8 path: fp32 [4 blocks][rows], decoded from E8M0 words the
+  // waves load into registers; PC: one fp32 per row)
+  static constexpr bool E8_LDS = !PC && FMT != kFmtBf16;
   static constexpr int A_OFF = 0, B_OFF = BM * BK, SA_OFF = (BM + BN) * BK;
-  static constexpr int SB_OFF = SA_OFF + (PC ? BM * 4 : SBLK * BM);
-  static constexpr int SAF_OFF = SB_OFF + (PC ? BN * 4 : SBLK * BN), SBF_OFF = SAF_OFF + 16 * BM;
+  static constexpr int SB_OFF = SA_OFF + (PC ? BM * 4 : E8_LDS ? SBLK * BM : 0);
+  static constexpr int SAF_OFF = SB_OFF + (PC ? BN * 4 : E8_LDS ? SBLK * BN : 0), SBF_OFF = SAF_OFF + 16 * BM;
   static constexpr int STAGE = (PC || FMT != kFmtBf16) ? SAF_OFF : SBF_OFF + 16 * BN;
   static constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;  // 1 KB DMA instructions per wave
   static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
@@ -270,6 +272,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   constexpr int FA_ROWS = SBLK * BM / NT;  // fprop: A-scale bytes (rows) each thread stages per K step
   uint8_t fa_b[FA_ROWS];                 // fprop: those bytes, held in registers until settle
   uint32_t a_off[S::A_INS], b_off[S::B_INS];
+  // widened MX recipe: this wave's E8M0 scale words of the step whose loads are in flight
+  uint32_t sc_w[(PC || SC) ? 1 : (SBLK * BM / 256 + SBLK * BN / 256) / NW];
 #pragma unroll
   for (int u = 0; u < S::A_INS; ++u) a_off[u] = tile_dma_voffset(wave * S::A_INS + u, lane, (uint32_t)lda, 0);
 #pragma unroll
@@ -356,19 +360,23 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
           const int r4 = scale_dma_row(part, lane, is_a ? a_last : b_last);
           dma4((is_a ? a_sc + a_row0 : b_sc + b_row0) + kbc * (is_a ? a_sld : b_sld) + r4, dst);
         } else if (MODE == kModeFprop && kb * BLK_BYTES >= kext) {
-          *(uint32_t*)(dst + 4 * lane) = 0x7f7f7f7fu;  // past K: unit scales over zero data
+          sc_w[u] = 0x7f7f7f7fu;  // past K: unit scales over zero data
         } else {
-          // valid rows are a multiple of 32 here, so a group of 4 is all valid or all past
+          // valid rows are a multiple of 32 here, so a group of 4 is all valid or all past.  The
+          // word goes to a register: settle() decodes it from there after the step's wait, with
+          // no LDS round trip between that wait and the barrier (1-1.5% on every widened GEMM
+          // against landing the bytes in LDS by DMA and reading them back)
           const int r4 = scale_dma_row(part, lane, is_a ? a_last : b_last);
-          dma4((is_a ? a_sc + a_row0 : b_sc + b_row0) + kb * (is_a ? a_sld : b_sld) + r4, dst);
+          sc_w[u] = *(const uint32_t*)((is_a ? a_sc + a_row0 : b_sc + b_row0) + kb * (is_a ? a_sld : b_sld) + r4);
         }
       }
     }
   };
-  // After the DMA has landed: decode the step's E8M0 scales once into the stage's fp32 area, so
-  // the fragment reads take fp32 scales with no per-read decode.  Each wave decodes the 256
-  // bytes its own scale DMA (or tail store) wrote -- visible to it after its own wait -- and the
-  // fprop A scales come from the register-staged bytes.
+  // After the step's loads have landed: decode its E8M0 scales once into the stage's fp32 area,
+  // so the fragment reads take fp32 scales with no per-read decode.  Each wave decodes the 256
+  // bytes of scale words it loaded into registers (sc_w), and the fprop A scales come from the
+  // register-staged bytes (fa_b).  (The scaled-MFMA paths take the E8M0 bytes from LDS as they
+  // are; their settle() only fixes up a tail step.)
   auto settle = [&](uint8_t* base, int kk) {
     if constexpr (SC) {
       // The scaled MFMA takes the E8M0 bytes as they are.  The fprop A scales, staged in
@@ -420,7 +428,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
         const int per = (is_a ? BM : BN) / 256;
         const int blk = vv / per, part = vv % per;
         const int idx = (is_a ? blk * BM : blk * BN) + part * 256 + 4 * lane;  // first of 4 rows
-        const uint32_t w4 = *(const uint32_t*)(base + (is_a ? S::SA_OFF : S::SB_OFF) + idx);
+        const uint32_t w4 = sc_w[u];
         float* f = (float*)(base + (is_a ? S::SAF_OFF : S::SBF_OFF)) + idx;
         *(v4f*)f = v4f{e8m0_value(w4 & 0xffu), e8m0_value((w4 >> 8) & 0xffu), e8m0_value((w4 >> 16) & 0xffu),
                        e8m0_value(w4 >> 24)};
