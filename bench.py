@@ -33,6 +33,9 @@ Reported (one JSON line on stdout):
               probe library libbsfp8_peak.so): bf16 32x32x16 on random and on all-zero
               operands, scaled fp8 and fp4 32x32x64 on random operands, in TFLOP/s; the
               roofline object sets the wgrad kernel against the bf16 figure too.
+  library_reference  the vendor GEMM library (hipBLASLt through torch) on one expert's dense
+              wgrad shape: its bf16 GEMM's TFLOP/s, and its fp8 GEMM's TFLOP/s and relative
+              error against fp64 on the same fp8 values (context, not part of the path).
   cpu_baseline the CPU oracle (quantize + fp64 wgrad) on one expert and a slice of the dy
               channels, in the same unit, with the number of threads it used.
 """
@@ -189,6 +192,49 @@ def mfma_probe(dev, stream, iters=150000):
         ghz = ((st[:, 2] - st[:, 0]) / (st[:, 3] - st[:, 1]) * wall_khz / 1e6).median().item()
         res[name + "_clock_GHz"] = round(ghz, 3)
     return res
+
+
+def library_reference(dev, stream, M=2048, N=7168, K=8192, reps=20):
+    """The vendor GEMM library (hipBLASLt, through torch) on one expert's dense weight-gradient shape
+    (dy channels x x channels x the mean expert's tokens), unquantized bf16 and OCP e4m3 with
+    per-tensor unit scales: TFLOP/s, and the fp8 product's relative Frobenius error against fp64 on
+    the same fp8 values.  Context for the grouped kernels, not part of the path; skipped (None) if
+    torch's fp8 GEMM is not available."""
+    import torch
+
+    g = torch.Generator(device=dev).manual_seed(7)
+    a = (torch.randn(M, K, device=dev, generator=g) * 0.5).to(torch.bfloat16)
+    b = (torch.randn(K, N, device=dev, generator=g) * 0.5).to(torch.bfloat16)
+    flop = 2.0 * M * N * K
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    c = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+    ms = timed(lambda: torch.matmul(a, b, out=c))
+    out = {"shape_MxNxK": [M, N, K], "bf16_ms": round(ms, 4), "bf16_TFLOP/s": round(flop / (ms / 1e3) / 1e12, 1)}
+    try:
+        a8 = a.to(torch.float8_e4m3fn)
+        b8 = b.t().contiguous().to(torch.float8_e4m3fn).t()  # column-major, as the fp8 GEMM takes it
+        one = torch.tensor(1.0, device=dev)
+        o = torch._scaled_mm(a8, b8, scale_a=one, scale_b=one, out_dtype=torch.float32)
+        ms8 = timed(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one, out_dtype=torch.float32))
+        ref = a8.double() @ b8.double()
+        rel = (torch.linalg.norm(o.double() - ref) / torch.linalg.norm(ref)).item()
+        out.update({"fp8_ms": round(ms8, 4), "fp8_TFLOP/s": round(flop / (ms8 / 1e3) / 1e12, 1),
+                    "fp8_rel_err_vs_fp64": float(f"{rel:.3e}")})
+        del a8, b8, o, ref
+    except (RuntimeError, AttributeError, TypeError) as ex:  # no fp8 GEMM in this torch build
+        out["fp8_error"] = repr(ex)[:160]
+    return out
 
 
 def lds_dma_probe(dev, stream):
@@ -876,6 +922,12 @@ def main():
     out["mfma_probe"] = dict(probe, note="MFMA-only kernels, no memory traffic in the loop: what the "
                                          "matrix cores sustain on this GPU")
     out["roofline"]["frac_of_probe_bf16"] = round(achieved / probe["bf16_random_TFLOP/s"], 4)
+    log("vendor GEMM reference")
+    lib = library_reference(dev, stream)
+    lib["note"] = ("hipBLASLt through torch on one expert's dense wgrad shape, unquantized bf16 and e4m3 "
+                   "with per-tensor scales: the vendor library's own rate, and its fp8 GEMM's error")
+    lib["wgrad_vs_bf16"] = round(achieved / lib["bf16_TFLOP/s"], 3)
+    out["library_reference"] = lib
     log("LDS DMA probe")
     out["lds_dma_probe"] = dict(lds_dma_probe(dev, stream),
                                 note="global -> LDS DMA as the GEMMs stage tiles: one 8-wave workgroup per CU, "

@@ -46,6 +46,10 @@ def test_bench_prints_one_contract_line():
     f8 = d["fp8_mfma"]
     assert f8["wgrad_TFLOP/s"] > 0 and abs(f8["wgrad_frac_of_fp8_peak"] - f8["wgrad_TFLOP/s"] / 5000.0) < 1e-3
     assert f8["rel_err_vs_oracle"]["bf16_widened"] <= 1e-5 < f8["rel_err_vs_oracle"]["fp8_mfma"] <= 5e-5
+    # the vendor library's dense GEMMs on one expert's shape, beside the grouped kernel
+    lib = d["library_reference"]
+    assert lib["bf16_TFLOP/s"] > 0 and abs(lib["wgrad_vs_bf16"] - rf["achieved"] / lib["bf16_TFLOP/s"]) < 2e-3
+    assert "fp8_TFLOP/s" in lib or "fp8_error" in lib
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["cores"] >= 1 and cb["value"] > 0
     assert isinstance(cb["sample"], str) and cb["sample"]
