@@ -3,7 +3,9 @@ traces the blow-ups to a race condition inside the GEMM kernel): the 2048 x 2048
 (one all-zero dy channel in each 128-token expert) called 10,000 times on operands cast once,
 for each zero-channel scale in the page's sweep (1, 1e-4, 1e-8, 1e-30).  Every call must be
 bitwise equal to the first, and no call may show the page's blow-up criterion (an expert's
-output norm above max(100 x its unquantized reference norm, 1))."""
+output norm above max(100 x its unquantized reference norm, 1)).  The same stress runs on the
+pipelined block-scaled kernels, and the launches the benchmark times repeat bit for bit at the
+128-expert MoE size."""
 import numpy as np
 import pytest
 import torch
@@ -131,3 +133,60 @@ def test_block_scaled_fprop_10000_calls_bitwise(recipe, out_dtype):
     label = f"fprop recipe={recipe} out_dtype={out_dtype}"
     flush(label)
     _stress(run, out, label)
+
+
+# The launches the benchmark times, at full size: the 128-expert MoE layer (1,048,576 expert rows,
+# hidden 7168, ffn 2048), MXFP8 wgrad accumulating into a main_grad reset before every call, the
+# bf16 forward and the bf16 data gradient, each called repeatedly and compared bit for bit with
+# the first call (the 128-expert shape runs 28,672 to 118,272 workgroups, over a hundred rounds of
+# the chip, where the small stress shape runs one).
+FULL_CALLS = 30
+
+
+def _repeat(run, out, label, calls=FULL_CALLS):
+    run()
+    torch.cuda.synchronize()
+    first = out.clone()
+    bits = torch.int16 if out.dtype == torch.bfloat16 else torch.int32
+    mismatched = torch.zeros((), dtype=torch.int64, device=DEV)
+    for _ in range(calls):
+        run()
+        mismatched += torch.ne(out.view(bits), first.view(bits)).any().to(torch.int64)
+    torch.cuda.synchronize()
+    assert int(mismatched) == 0, f"{label}: {int(mismatched)} of {calls} calls differ from the first"
+    return first
+
+
+def test_moe128_launches_repeat_bitwise():
+    case = W.moe128_top8(DEV)
+    splits, R, T = case["splits"], case["R"], case["T"]
+    n, h, K, N = case["n"], case["h"], case["K"], case["N"]
+    E = len(splits)
+    st = W.splits_tensor(splits, DEV)
+    xq = bs.alloc_quantized(R, h, E, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, DEV)
+    dq = bs.alloc_quantized(R, n, E, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, DEV)
+    wq = bs.alloc_quantized(E * N, K, 1, bs.RECIPE_MX, bs.ROWWISE, DEV)
+    wc = bs.alloc_quantized(E * N, K, E, bs.RECIPE_MX, bs.COLWISE, DEV)
+    bs.grouped_quantize(case["x"], st, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, xq)
+    bs.grouped_quantize(case["dy"], st, bs.RECIPE_MX, bs.COLWISE | bs.ROWWISE, dq)
+    w2 = case["W"].view(E * N, K)
+    bs.grouped_quantize(w2, None, bs.RECIPE_MX, bs.ROWWISE, wq)
+    bs.grouped_quantize(w2, W.splits_tensor([N] * E, DEV), bs.RECIPE_MX, bs.COLWISE, wc)
+    mg0 = case["main_grad"]
+    del case, w2
+    mg = torch.empty_like(mg0)
+
+    def wgrad():
+        mg.copy_(mg0)
+        bs.grouped_gemm_wgrad(dq, n, xq, h, st, R, bs.RECIPE_MX, mg, accumulate=True)
+
+    flush("moe128 wgrad repeated")
+    _repeat(wgrad, mg, "moe128 wgrad")
+    del mg, mg0
+    y = torch.empty(R, N, dtype=torch.bfloat16, device=DEV)
+    flush("moe128 fprop repeated")
+    _repeat(lambda: bs.grouped_gemm_fprop(xq, K, wq, N, st, R, y, bs.OUT_BF16), y, "moe128 fprop")
+    del y
+    dx = torch.empty(R, K, dtype=torch.bfloat16, device=DEV)
+    flush("moe128 dgrad repeated")
+    _repeat(lambda: bs.grouped_gemm_dgrad(dq, n, wc, K, st, R, dx, bs.OUT_BF16), dx, "moe128 dgrad")
