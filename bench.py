@@ -194,7 +194,7 @@ def mfma_probe(dev, stream, iters=150000):
     return res
 
 
-def library_reference(dev, stream, M=2048, N=7168, K=8192, reps=20):
+def library_reference(dev, stream, M=2048, N=7168, K=8192, reps=50, warm=10):
     """The vendor GEMM library (hipBLASLt, through torch) on one expert's dense weight-gradient shape
     (dy channels x x channels x the mean expert's tokens), unquantized bf16 and OCP e4m3 with
     per-tensor unit scales: TFLOP/s, and the fp8 product's relative Frobenius error against fp64 on
@@ -209,8 +209,9 @@ def library_reference(dev, stream, M=2048, N=7168, K=8192, reps=20):
     bk = (torch.randn(N, K, device=dev, generator=g) * 0.5).to(torch.bfloat16)
     flop = 2.0 * M * N * K
 
-    def timed(fn):
-        fn()
+    def timed(fn):  # after warm-up calls: the library's rate climbs over its first calls
+        for _ in range(warm):
+            fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -220,8 +221,7 @@ def library_reference(dev, stream, M=2048, N=7168, K=8192, reps=20):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    c = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
-    ms = timed(lambda: torch.matmul(a, bk.t(), out=c))
+    ms = timed(lambda: torch.matmul(a, bk.t()))
     out = {"shape_MxNxK": [M, N, K], "bf16_ms": round(ms, 4), "bf16_TFLOP/s": round(flop / (ms / 1e3) / 1e12, 1)}
     try:
         a8 = a.to(torch.float8_e4m3fn)
@@ -474,10 +474,26 @@ def small_configs_leg(bs, W, dev, stream, run_oracle=True):
         "fprop": (lambda: bs.grouped_gemm_fprop(xq, K, wq, N, st, R, fo, bs.OUT_F32, status=status),
                   T * K * (1 + 1 / 32) + E * N * K * (1 + 1 / 32) + 4.0 * T * N),
     }
+    # each kernel in the step, as the headline times its kernels (the five calls in order, 20
+    # steps, HIP events around every call), and the same kernel called 20 times back to back
+    names = list(legs)
+    for _ in range(3):
+        for leg in names:
+            legs[leg][0]()
+    torch.cuda.synchronize()
+    steps = 20
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    for st_ev in ev:
+        st_ev[0].record(stream)
+        for i, leg in enumerate(names):
+            legs[leg][0]()
+            st_ev[i + 1].record(stream)
+    torch.cuda.synchronize()
     res = {}
-    for leg, (fn, nbytes) in legs.items():
-        ms = _time_calls(fn, stream, 20)
-        res[leg] = {"us": round(ms * 1e3, 1), "GB/s": round(nbytes / (ms / 1e3) / 1e9, 1)}
+    for i, leg in enumerate(names):
+        ms = sum(e[i].elapsed_time(e[i + 1]) for e in ev) / steps
+        res[leg] = {"us": round(ms * 1e3, 1), "GB/s": round(legs[leg][1] / (ms / 1e3) / 1e9, 1),
+                    "us_back_to_back": round(_time_calls(legs[leg][0], stream, 20) * 1e3, 1)}
     flop = 2.0 * n * h * T
     for leg in ("wgrad", "fprop"):
         r = flop / (res[leg]["us"] / 1e6) / 1e12
