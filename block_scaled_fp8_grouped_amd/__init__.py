@@ -130,6 +130,26 @@ def _quant(q, key, what, dtypes=_U8):
     return _dev(q.get(key), f"{what}[{key!r}]", dtypes)
 
 
+def _need(t, nbytes, what):
+    """A tensor argument must hold at least the bytes the kernels address for the given sizes and
+    recipe (a buffer quantized with another recipe, or sized for other dims, would be read or
+    written past its end); raw addresses are not checked."""
+    if isinstance(t, torch.Tensor) and nbytes > 0 and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{what}: {t.numel() * t.element_size()} bytes, the call addresses {nbytes}")
+
+
+def _need_quant(q, recipe, rows, cols, num_groups, which, what):
+    """The quantized buffers of ``q`` (a dict from alloc_quantized) against the layouts ``which``
+    of a [rows, cols] operand with ``num_groups`` groups."""
+    r = recipe & ~GEMM_FP8_MFMA
+    if which & ROWWISE:
+        _need(q.get("row_q"), rowwise_data_bytes(rows, cols, r), f"{what}['row_q']")
+        _need(q.get("row_s"), rowwise_scale_bytes(rows, cols), f"{what}['row_s']")
+    if which & COLWISE:
+        _need(q.get("col_q"), colwise_data_bytes(rows, cols, num_groups, r), f"{what}['col_q']")
+        _need(q.get("col_s"), colwise_scale_bytes(rows, cols, num_groups, r), f"{what}['col_s']")
+
+
 def _col_s_types(recipe):
     return _F32 if (recipe & ~GEMM_FP8_MFMA) == RECIPE_PC else _U8
 
@@ -201,12 +221,13 @@ def grouped_quantize(x, split_sizes, recipe, which, out, zero_amax_scale=1e-30, 
     else:
         R, C = capacity_rows, cols
     E = 0 if split_sizes is None else int(split_sizes.numel())
-    rc = lib().bsfp8_grouped_quantize(_dev(x, "x", _BF16), R, C, _dev(split_sizes, "split_sizes", _I32), E, recipe,
-                                      which, float(zero_amax_scale), _quant(out, "row_q", "out"),
-                                      _quant(out, "row_s", "out"), _quant(out, "col_q", "out"),
-                                      _quant(out, "col_s", "out", _col_s_types(recipe)),
-                                      _dev(noop_flag, "noop_flag", _F32), _dev(status, "status", _I32),
-                                      _stream(stream))
+    args = (_dev(x, "x", _BF16), R, C, _dev(split_sizes, "split_sizes", _I32), E, recipe, which,
+            float(zero_amax_scale), _quant(out, "row_q", "out"), _quant(out, "row_s", "out"),
+            _quant(out, "col_q", "out"), _quant(out, "col_s", "out", _col_s_types(recipe)),
+            _dev(noop_flag, "noop_flag", _F32), _dev(status, "status", _I32), _stream(stream))
+    _need(x, R * C * 2, "x")
+    _need_quant(out, recipe, R, C, max(E, 1), which, "out")
+    rc = lib().bsfp8_grouped_quantize(*args)
     _check(rc, "grouped_quantize")
     return out
 
@@ -224,11 +245,12 @@ def grouped_act_quantize(activation, h, split_sizes, recipe, which, out, probs=N
             raise ValueError("grouped_act_quantize: a GLU input has an even number of columns")
         C //= 2
     E = int(split_sizes.numel())
-    rc = lib().bsfp8_grouped_act_quantize(activation, _dev(h, "h", _BF16), _dev(probs, "probs", _F32),
-                                          _dev(dy, "dy", _BF16), R, C, _dev(split_sizes, "split_sizes", _I32), E,
-                                          recipe, which, _quant(out, "row_q", "out"), _quant(out, "row_s", "out"),
-                                          _quant(out, "col_q", "out"), _quant(out, "col_s", "out"),
-                                          _dev(status, "status", _I32), _stream(stream))
+    args = (activation, _dev(h, "h", _BF16), _dev(probs, "probs", _F32), _dev(dy, "dy", _BF16), R, C,
+            _dev(split_sizes, "split_sizes", _I32), E, recipe, which, _quant(out, "row_q", "out"),
+            _quant(out, "row_s", "out"), _quant(out, "col_q", "out"), _quant(out, "col_s", "out"),
+            _dev(status, "status", _I32), _stream(stream))
+    _need_quant(out, recipe, R, 2 * C if activation == ACT_SWIGLU_GRAD else C, E, which, "out")
+    rc = lib().bsfp8_grouped_act_quantize(*args)
     _check(rc, "grouped_act_quantize")
     return out
 
@@ -240,11 +262,13 @@ def grouped_gemm_wgrad(dy_q, n, x_q, h, split_sizes, capacity_rows, recipe, out,
     recipe, or RECIPE_MX | GEMM_FP8_MFMA for the MXFP8 operands on the scaled fp8 MFMA."""
     E = int(split_sizes.numel())
     cs = _col_s_types(recipe)
-    rc = lib().bsfp8_grouped_gemm_wgrad(_quant(dy_q, "col_q", "dy_q"), _quant(dy_q, "col_s", "dy_q", cs), n,
-                                        _quant(x_q, "col_q", "x_q"), _quant(x_q, "col_s", "x_q", cs), h,
-                                        _dev(split_sizes, "split_sizes", _I32), E, capacity_rows, recipe,
-                                        _dev(out, "out", _F32_BITS), 1 if accumulate else 0,
-                                        _dev(status, "status", _I32), _stream(stream))
+    args = (_quant(dy_q, "col_q", "dy_q"), _quant(dy_q, "col_s", "dy_q", cs), n, _quant(x_q, "col_q", "x_q"),
+            _quant(x_q, "col_s", "x_q", cs), h, _dev(split_sizes, "split_sizes", _I32), E, capacity_rows, recipe,
+            _dev(out, "out", _F32_BITS), 1 if accumulate else 0, _dev(status, "status", _I32), _stream(stream))
+    _need_quant(dy_q, recipe, capacity_rows, n, E, COLWISE, "dy_q")
+    _need_quant(x_q, recipe, capacity_rows, h, E, COLWISE, "x_q")
+    _need(out, E * n * h * 4, "out")
+    rc = lib().bsfp8_grouped_gemm_wgrad(*args)
     _check(rc, "grouped_gemm_wgrad")
     return out
 
@@ -256,11 +280,14 @@ def grouped_gemm_fprop(x_q, k, w_q, n, split_sizes, capacity_rows, out, out_dtyp
     operands on the scaled fp8 MFMA); out is [R, n] fp32 or bf16 (rows past
     sum(split_sizes) untouched)."""
     E = int(split_sizes.numel())
-    rc = lib().bsfp8_grouped_gemm_fprop(_quant(x_q, "row_q", "x_q"), _quant(x_q, "row_s", "x_q"), capacity_rows, k,
-                                        _quant(w_q, "row_q", "w_q"), _quant(w_q, "row_s", "w_q"), n,
-                                        _dev(split_sizes, "split_sizes", _I32), E, recipe,
-                                        _dev(out, "out", _F32_BITS if out_dtype == OUT_F32 else _BF16), out_dtype,
-                                        _dev(status, "status", _I32), _stream(stream))
+    args = (_quant(x_q, "row_q", "x_q"), _quant(x_q, "row_s", "x_q"), capacity_rows, k, _quant(w_q, "row_q", "w_q"),
+            _quant(w_q, "row_s", "w_q"), n, _dev(split_sizes, "split_sizes", _I32), E, recipe,
+            _dev(out, "out", _F32_BITS if out_dtype == OUT_F32 else _BF16), out_dtype,
+            _dev(status, "status", _I32), _stream(stream))
+    _need_quant(x_q, recipe, capacity_rows, k, E, ROWWISE, "x_q")
+    _need_quant(w_q, recipe, E * n, k, 1, ROWWISE, "w_q")
+    _need(out, capacity_rows * n * (4 if out_dtype == OUT_F32 else 2), "out")
+    rc = lib().bsfp8_grouped_gemm_fprop(*args)
     _check(rc, "grouped_gemm_fprop")
     return out
 
@@ -272,10 +299,17 @@ def grouped_gemm_dgrad(dy_q, n, w_q, k, split_sizes, capacity_rows, out, out_dty
     expert); out is [R, k] fp32 or bf16: out[off_e + t] = dy[off_e + t] @ W_e (rows past
     sum(split_sizes) untouched)."""
     E = int(split_sizes.numel())
-    rc = lib().bsfp8_grouped_gemm_dgrad(_quant(dy_q, "row_q", "dy_q"), _quant(dy_q, "row_s", "dy_q"), capacity_rows,
-                                        n, _quant(w_q, "col_q", "w_q"), _quant(w_q, "col_s", "w_q"), k,
-                                        _dev(split_sizes, "split_sizes", _I32), E, recipe,
-                                        _dev(out, "out", _F32_BITS if out_dtype == OUT_F32 else _BF16), out_dtype,
-                                        _dev(status, "status", _I32), _stream(stream))
+    args = (_quant(dy_q, "row_q", "dy_q"), _quant(dy_q, "row_s", "dy_q"), capacity_rows, n,
+            _quant(w_q, "col_q", "w_q"), _quant(w_q, "col_s", "w_q"), k, _dev(split_sizes, "split_sizes", _I32), E,
+            recipe, _dev(out, "out", _F32_BITS if out_dtype == OUT_F32 else _BF16), out_dtype,
+            _dev(status, "status", _I32), _stream(stream))
+    _need_quant(dy_q, recipe, capacity_rows, n, E, ROWWISE, "dy_q")
+    # the weight [E*n, k] quantized colwise with split sizes n: E groups of 128 * ceil(n / 128) rows
+    np_ = 128 * ((n + 127) // 128)
+    per = 2 if (recipe & ~GEMM_FP8_MFMA) == RECIPE_MX4 else 1
+    _need(w_q.get("col_q"), k * E * np_ // per, "w_q['col_q']")
+    _need(w_q.get("col_s"), k * E * np_ // 32, "w_q['col_s']")
+    _need(out, capacity_rows * k * (4 if out_dtype == OUT_F32 else 2), "out")
+    rc = lib().bsfp8_grouped_gemm_dgrad(*args)
     _check(rc, "grouped_gemm_dgrad")
     return out
