@@ -139,8 +139,12 @@ def _need(t, nbytes, what):
 
 
 def _need_quant(q, recipe, rows, cols, num_groups, which, what):
-    """The quantized buffers of ``q`` (a dict from alloc_quantized) against the layouts ``which``
-    of a [rows, cols] operand with ``num_groups`` groups."""
+    """The quantized buffers of ``q`` against the layouts ``which`` of a [rows, cols] operand with
+    ``num_groups`` groups: at least the size queries' bytes (alloc_quantized's sizes; a colwise
+    buffer holds up to that bound, depending on the device split sizes).  With no rows nothing is
+    addressed."""
+    if rows == 0:
+        return
     r = recipe & ~GEMM_FP8_MFMA
     if which & ROWWISE:
         _need(q.get("row_q"), rowwise_data_bytes(rows, cols, r), f"{what}['row_q']")

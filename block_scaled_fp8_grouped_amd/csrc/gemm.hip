@@ -83,8 +83,8 @@ __device__ __forceinline__ void buffer_dma16(__amdgpu_buffer_rsrc_t rs, uint8_t*
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
-// The MXFP4 loop issues its DMAs as inline assembly (M0 = the wave-uniform LDS byte address,
-// one wait state between setting M0 and its use).  Issued through the builtins, the compiler
+// The scaled-MFMA loops (MXFP4, MXFP8 on the fp8 MFMA) issue their DMAs as inline assembly (M0 =
+// the wave-uniform LDS byte address, one wait state between setting M0 and its use).  Issued through the builtins, the compiler
 // cannot tell the DMA into the next LDS stage from the reads of the current one and makes the
 // step's later fragment reads wait for it, which leaves the DMA no time to hide behind; the
 // kernel waits for its DMAs itself (s_waitcnt vmcnt(0) before a stage is read), and any wait
@@ -92,8 +92,8 @@ __device__ __forceinline__ void buffer_dma16(__amdgpu_buffer_rsrc_t rs, uint8_t*
 __device__ __forceinline__ void asm_dma16(v4i rsrc, uint32_t lds, uint32_t voff) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
-__device__ __forceinline__ void asm_dma4(const void* g, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "{m0}"(lds) : "memory");
+__device__ __forceinline__ void asm_dma16g(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
 }
 // The four words of a raw buffer resource (base, stride 0, num_records bytes, the flags word
 // passed to __builtin_amdgcn_make_buffer_rsrc elsewhere), wave-uniform.
@@ -259,13 +259,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
       (void*)(a_data + a_row0 * lda), (short)0, (int)tile_range(a_valid - a_row0, lda), 0x00020000);
   const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(b_data + b_row0 * ldb), (short)0, (int)tile_range(b_valid - b_row0, ldb), 0x00020000);
-  // LDS byte address of a place in smem (MXFP4's assembly DMAs take it in M0)
+  // LDS byte address of a place in smem (the assembly DMAs take it in M0)
   const uint32_t smem_lds =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem);
   auto lds_of = [&](const uint8_t* p) { return smem_lds + (uint32_t)(p - smem); };
-  auto dma4 = [&](const void* g, uint8_t* l) {
-    if constexpr (SC) asm_dma4(g, lds_of(l));
-    else __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+  auto dma4 = [&](const void* g, uint8_t* l) {  // the per-channel recipe's fp32 scales
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
   };
   const v4i a_rw = rsrc_words(a_data + a_row0 * lda, (uint32_t)tile_range(a_valid - a_row0, lda));
   const v4i b_rw = rsrc_words(b_data + b_row0 * ldb, (uint32_t)tile_range(b_valid - b_row0, ldb));
@@ -339,8 +338,29 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
           dma4((const float*)b_sc + (int64_t)kk * b_sld + b_row0 + min(row - BM, b_last), base + S::SA_OFF + v * 256);
         }
       }
+    } else if constexpr (SC) {
+      // E8M0 block rows [blk][row], 16 bytes per lane: one instruction moves four whole 256-row
+      // blocks (1 KB, contiguous in LDS), a quarter of the instructions 4-byte loads take (1-3%
+      // on every scaled GEMM).  wgrad loads the A and B blocks, the m-grouped kernels the B
+      // (weight) blocks; their token rows' A scales go through registers (part 0 above).  The
+      // waves take the instructions in turn and waves past their number repeat one, writing the
+      // same bytes to the same place: no branch in the step.  A lane past the tile's valid rows
+      // reloads the last valid 16 bytes (valid rows are a multiple of 32), and a block past kext
+      // reloads the last valid block: every source byte lies in the group's scale rows, and the
+      // finite scales of a block past kext multiply the chunks settle() zeroes.
+      static_assert(BM == 256 && BN == 256, "16-byte scale loader shape");
+      constexpr int NA = MODE == kModeWgrad ? SBLK * BM / 1024 : 0, NI = NA + SBLK * BN / 1024;
+      const int v = wave % NI;
+      const bool is_a = v < NA;
+      const int vv = is_a ? v : v - NA;
+      const int blk = 4 * vv + (lane >> 4);
+      const int r = scale_dma16_row(lane, is_a ? a_last : b_last);
+      const int64_t kb = (int64_t)kk * SBLK + blk;
+      const int64_t kbc = kb < nblk ? kb : nblk - 1;
+      const uint8_t* src = (is_a ? a_sc + a_row0 : b_sc + b_row0) + kbc * (is_a ? a_sld : b_sld) + r;
+      asm_dma16g(src, lds_of(base + (is_a ? S::SA_OFF : S::SB_OFF) + 4 * vv * 256));
     } else {
-      // E8M0 block rows [blk][row]: 4 rows of 4 bytes per lane, 256 bytes per instruction
+      // the widened path: E8M0 block rows [blk][row], 4 rows of 4 bytes per lane into registers
       constexpr int SA_INS = SBLK * BM / 256, SB_INS = SBLK * BN / 256;
       static_assert((SA_INS + SB_INS) % NW == 0, "MX scale loader shape");
 #pragma unroll
@@ -351,14 +371,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
         const int per = (is_a ? BM : BN) / 256;
         const int blk = vv / per, part = vv % per;
         const int64_t kb = (int64_t)kk * SBLK + blk;
-        uint8_t* dst = base + (is_a ? S::SA_OFF + blk * BM : S::SB_OFF + blk * BN) + part * 256;
         if (MODE == kModeFprop && is_a) {
           // rows of a group start anywhere: single-byte loads per thread instead (above)
-        } else if (SC) {
-          // no branch: a block past kext loads the last valid one; settle() puts unit scales there
-          const int64_t kbc = kb < nblk ? kb : nblk - 1;
-          const int r4 = scale_dma_row(part, lane, is_a ? a_last : b_last);
-          dma4((is_a ? a_sc + a_row0 : b_sc + b_row0) + kbc * (is_a ? a_sld : b_sld) + r4, dst);
         } else if (MODE == kModeFprop && kb * BLK_BYTES >= kext) {
           sc_w[u] = 0x7f7f7f7fu;  // past K: unit scales over zero data
         } else {
@@ -376,13 +390,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
   // so the fragment reads take fp32 scales with no per-read decode.  Each wave decodes the 256
   // bytes of scale words it loaded into registers (sc_w), and the fprop A scales come from the
   // register-staged bytes (fa_b).  (The scaled-MFMA paths take the E8M0 bytes from LDS as they
-  // are; their settle() only fixes up a tail step.)
+  // are; their settle() only places the fprop A scales and fixes up a tail step.)
   auto settle = [&](uint8_t* base, int kk) {
     if constexpr (SC) {
       // The scaled MFMA takes the E8M0 bytes as they are.  The fprop A scales, staged in
-      // registers, are written to their [blk][row] place, and blocks past kext (a tail step)
-      // get unit scales over their zero data, in the 256-byte pieces this wave's DMA filled.
-      constexpr int SA_INS = SBLK * BM / 256, SB_INS = SBLK * BN / 256, PER = (SA_INS + SB_INS) / NW;
+      // registers, are written to their [blk][row] place (unit scales for blocks past kext).
       if constexpr (MODE == kModeFprop) {
         const int blk = wave / (NW / SBLK);
         const bool valid = ((int64_t)kk * SBLK + blk) * BLK_BYTES < kext;
@@ -390,19 +402,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
 #pragma unroll
         for (int i = 0; i < FA_ROWS; ++i) f[i] = valid ? fa_b[i] : (uint8_t)0x7f;
       }
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int v = wave * PER + u;
-        const bool is_a = v < SA_INS;
-        if (MODE == kModeFprop && is_a) continue;
-        const int vv = is_a ? v : v - SA_INS;
-        const int per = (is_a ? BM : BN) / 256;
-        const int blk = vv / per, part = vv % per;
-        if (((int64_t)kk * SBLK + blk) * BLK_BYTES >= kext)
-          *(uint32_t*)(base + (is_a ? S::SA_OFF + blk * BM : S::SB_OFF + blk * BN) + part * 256 + 4 * lane) =
-              0x7f7f7f7fu;
-      }
-      // a tail step: the 16-byte chunks this wave's data DMA put past kext (bytes of the next
+      // The scale blocks the DMA loaded past kext hold the last valid block's finite scales
+      // (several waves may load the same bytes, so no wave rewrites them); they multiply the
+      // chunks zeroed here.  A tail step: the 16-byte chunks this wave's data DMA put past kext (bytes of the next
       // row, or zeros past the operand) become zeros, so the step needs no masking
       const int64_t k0 = (int64_t)kk * BK;
       if (k0 + BK > kext) {

@@ -47,4 +47,12 @@ BSFP8_HD int scale_dma_row(int part, int lane, int last) {
   return r4 + 3 <= last ? r4 : last - 3;
 }
 
+// First of the 16 E8M0 scale rows one 16-byte DMA lane moves (the scaled-MFMA paths: 16 lanes per
+// 256-row block): rows 16 * (lane % 16) .. + 15, pulled back so that all 16 are valid (`last` + 1,
+// the tile's valid rows counted from its first, is a multiple of 32 and >= 32).
+BSFP8_HD int scale_dma16_row(int lane, int last) {
+  const int r = 16 * (lane & 15);
+  return r + 15 <= last ? r : last + 1 - 16;
+}
+
 }  // namespace bsfp8

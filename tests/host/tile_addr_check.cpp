@@ -84,6 +84,24 @@ static void check_operand(const char* what, int BM, int NW, int64_t valid, int64
           }
         }
       }
+      // 16 rows per lane (the scaled-MFMA paths): in range, 16-aligned, and every valid row of the
+      // tile's 256 delivered by some lane
+      if (BM == 256) {
+        std::vector<int> got(256, 0);
+        for (int lane = 0; lane < 16; ++lane) {
+          const int r = scale_dma16_row(lane, last);
+          ++g_checked;
+          if (r < 0 || r % 16 != 0 || r + 15 > last) {
+            if (g_fail++ < 10) std::printf("%s: 16-byte scale rows %d..%d past last %d\n", what, r, r + 15, last);
+            continue;
+          }
+          for (int i = 0; i < 16 && r + i < 256; ++i) got[r + i] = 1;
+        }
+        for (int i = 0; i < 256 && i <= last; ++i)
+          if (!got[i]) {
+            if (g_fail++ < 10) std::printf("%s: scale row %d not loaded (last %d)\n", what, i, last);
+          }
+      }
     }
   }
 }
