@@ -372,6 +372,22 @@ def fp8_mfma_leg(bs, case, dq, xq, wq, st, R, n, h, K, N, mg, fout, status, stre
     return res, outs
 
 
+def _call_stats(fn, stream, reps):
+    """Per-call milliseconds of `reps` back-to-back calls (after one warm-up call), from HIP events
+    recorded between the calls on the launch stream: (mean, median, min)."""
+    import torch
+    fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+    mid = ts[reps // 2] if reps % 2 else (ts[reps // 2 - 1] + ts[reps // 2]) / 2
+    return ev[0].elapsed_time(ev[reps]) / reps, mid, ts[0]
+
+
 def _time_calls(fn, stream, reps):
     """Mean milliseconds per call over `reps` back-to-back calls (after one warm-up call), with
     HIP events on the launch stream."""
@@ -429,8 +445,9 @@ def small_configs_leg(bs, W, dev, stream, run_oracle=True):
         }
         res = {}
         for leg, (fn, nbytes) in legs.items():
-            ms = _time_calls(fn, stream, reps)
-            res[leg] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms / 1e3) / 1e9, 1)}
+            ms, med, mn = _call_stats(fn, stream, reps)
+            res[leg] = {"us": round(ms * 1e3, 2), "us_median": round(med * 1e3, 2), "us_min": round(mn * 1e3, 2),
+                        "GB/s": round(nbytes / (ms / 1e3) / 1e9, 1)}
         res["wgrad"]["TFLOP/s"] = round(2.0 * n * h * T / (res["wgrad"]["us"] / 1e6) / 1e12, 2)
         if run_oracle:
             t0 = time.perf_counter()
@@ -491,8 +508,10 @@ def small_configs_leg(bs, W, dev, stream, run_oracle=True):
     torch.cuda.synchronize()
     res = {}
     for i, leg in enumerate(names):
-        ms = sum(e[i].elapsed_time(e[i + 1]) for e in ev) / steps
-        res[leg] = {"us": round(ms * 1e3, 1), "GB/s": round(legs[leg][1] / (ms / 1e3) / 1e9, 1),
+        ts = sorted(e[i].elapsed_time(e[i + 1]) for e in ev)
+        ms = sum(ts) / steps
+        res[leg] = {"us": round(ms * 1e3, 1), "us_median": round((ts[steps // 2 - 1] + ts[steps // 2]) / 2 * 1e3, 1),
+                    "us_min": round(ts[0] * 1e3, 1), "GB/s": round(legs[leg][1] / (ms / 1e3) / 1e9, 1),
                     "us_back_to_back": round(_time_calls(legs[leg][0], stream, 20) * 1e3, 1)}
     flop = 2.0 * n * h * T
     for leg in ("wgrad", "fprop"):
