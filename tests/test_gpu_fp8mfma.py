@@ -85,7 +85,9 @@ def _wgrad(dy, x, splits, accumulate=False, mg=None):
     return out, dq, xq
 
 
-def check_wgrad_f8(dy, x, splits, accumulate=False, mg=None, label=""):
+def check_wgrad_f8(dy, x, splits, accumulate=False, mg=None, label="", rows_sel=None):
+    """``rows_sel``: the output rows (dy channels) held to the oracle and to the bound (all if
+    None); empty experts are checked in full either way."""
     R, n = dy.shape
     h = x.shape[1]
     out, dq, xq = _wgrad(dy, x, splits, accumulate, mg)
@@ -93,10 +95,11 @@ def check_wgrad_f8(dy, x, splits, accumulate=False, mg=None, label=""):
     o_x = oracle.grouped_quantize(W.bf16_bits(x), splits, oracle.RECIPE_MX, oracle.COLWISE)
     assert_quant_matches(dq, o_dy, splits, R, bs.COLWISE, label + " dy")
     assert_quant_matches(xq, o_x, splits, R, bs.COLWISE, label + " x")
+    sel = np.arange(n, dtype=np.int32) if rows_sel is None else np.asarray(rows_sel, np.int32)
     ref = oracle.grouped_wgrad(o_dy["col_q"], o_dy["col_s"], n, o_x["col_q"], o_x["col_s"], h, splits, R,
-                               oracle.RECIPE_MX)
-    got = out.cpu().numpy().astype(np.float64)
-    mg_h = None if mg is None else mg.cpu().numpy().astype(np.float64)
+                               oracle.RECIPE_MX, rows_sel=sel)
+    got = out.cpu().numpy()[:, sel, :].astype(np.float64)
+    mg_h = None if mg is None else mg.cpu().numpy()[:, sel, :].astype(np.float64)
     for e, k in enumerate(splits):
         if k == 0:
             if accumulate:
@@ -104,7 +107,7 @@ def check_wgrad_f8(dy, x, splits, accumulate=False, mg=None, label=""):
             else:
                 assert (out[e] == 0).all(), f"{label} empty expert {e} not zero"
             continue
-        tol = _mfma_tol(_deq_colwise(o_dy["col_q"], o_dy["col_s"], n, splits, e),
+        tol = _mfma_tol(_deq_colwise(o_dy["col_q"], o_dy["col_s"], n, splits, e)[sel],
                         _deq_colwise(o_x["col_q"], o_x["col_s"], h, splits, e))
         if accumulate:
             exact = mg_h[e] + ref[e]
@@ -162,6 +165,43 @@ def test_wgrad_zero_channel_and_padding_bitwise():
         assert torch.equal(got.view(torch.int32), out.view(torch.int32)), f"padding {fill} changed the result"
 
 
+def test_wgrad_skewed_split_many_tiles():
+    """Zipf split sizes over 40 experts (largest group above twice the mean non-empty size) and
+    more 256x256 tiles than one round of 256 workgroups: the largest-first group order and the
+    short per-XCD runs on the scaled path.  Tile-edge rows and 40 random rows of every expert
+    are held to the bound."""
+    rng = np.random.default_rng(11)
+    splits = [int(c) for c in W.zipf_counts(rng, 40, 36, 7000)]
+    live = [k for k in splits if k > 0]
+    assert max(live) * len(live) > 2 * sum(live), splits  # the kernel's skew condition
+    n, h = 512, 1024
+    assert len(splits) * (n // 256) * (h // 256) > 256
+    flush(f"fp8-mfma wgrad skewed splits={splits}")
+    R = sum(splits) + 77
+    dy, x = _operands(R, n, h, splits, seed=13)
+    edges = [0, 127, 128, 255, 256, 383, 384, 511]
+    sel = np.union1d(edges, np.random.default_rng(14).choice(n, size=40, replace=False))
+    check_wgrad_f8(dy, x, splits, label="f8 skewed", rows_sel=sel)
+
+
+def test_wgrad_and_fprop_max_groups():
+    """num_groups at the 1024 maximum on the scaled path: empty, one-row and 128-row groups
+    mixed, garbage padding; wgrad store and accumulate, and the m-grouped forward."""
+    E = bs.MAX_GROUPS
+    rng = np.random.default_rng(1024)
+    splits = [int(v) for v in rng.choice([0, 1, 2, 31, 33, 64, 128, 129], size=E)]
+    n = h = 64
+    R = sum(splits) + 40
+    flush(f"fp8-mfma max groups E={E} T={sum(splits)}")
+    dy, x = _operands(R, n, h, splits, seed=7)
+    check_wgrad_f8(dy, x, splits, label=f"f8 E={E}")
+    mg = torch.randn(E, n, h, dtype=torch.float32, device=DEV, generator=torch.Generator(device=DEV).manual_seed(9))
+    check_wgrad_f8(dy, x, splits, accumulate=True, mg=mg, label=f"f8 E={E} acc")
+    N = 64
+    w = W.randn_bf16((E * N, h), torch.Generator(device=DEV).manual_seed(8), DEV)
+    _check_fprop(x, w, splits, N, bs.OUT_F32, f"f8 E={E} fprop")
+
+
 def _fprop(x, w, splits, N, out_dtype):
     R, K = x.shape
     st = W.splits_tensor(splits, DEV)
@@ -185,6 +225,10 @@ def test_fprop(out_dtype, K, N, splits):
     g = torch.Generator(device=DEV).manual_seed(K + N)
     x = W.randn_bf16((R, K), g, DEV)
     w = W.randn_bf16((E * N, K), g, DEV)
+    _check_fprop(x, w, splits, N, out_dtype, "fprop")
+
+
+def _check_fprop(x, w, splits, N, out_dtype, label):
     out = _fprop(x, w, splits, N, out_dtype)
     o_x = oracle.grouped_quantize(W.bf16_bits(x), splits, oracle.RECIPE_MX, oracle.ROWWISE)
     o_w = oracle.grouped_quantize(W.bf16_bits(w), None, oracle.RECIPE_MX, oracle.ROWWISE)
@@ -200,7 +244,7 @@ def test_fprop(out_dtype, K, N, splits):
             tol = _mfma_tol(A[off:off + k], B[e * N:(e + 1) * N])
             if out_dtype == bs.OUT_BF16:
                 tol = tol + bf16_ulp(bf16_round(ref[off:off + k]))
-            _check_close(got[off:off + k], ref[off:off + k], tol, f"fprop expert {e}")
+            _check_close(got[off:off + k], ref[off:off + k], tol, f"{label} expert {e}")
             if out_dtype == bs.OUT_F32:
                 assert rel_err(got[off:off + k], ref[off:off + k]) <= REL_F8
         off += k

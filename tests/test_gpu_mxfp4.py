@@ -155,6 +155,43 @@ def test_mx4_wgrad_padding_bitwise_invariant(fill):
     assert torch.equal(base.view(torch.int32), padded.view(torch.int32))
 
 
+def test_mx4_wgrad_skewed_split_many_tiles():
+    """Zipf split sizes over 40 experts (largest group above twice the mean non-empty size) and
+    more 256x256 tiles than one round of 256 workgroups: the largest-first group order and the
+    short per-XCD runs on the fp4 path.  Tile-edge rows and 40 random rows of every expert are
+    held to the oracle."""
+    rng = np.random.default_rng(11)
+    splits = [int(c) for c in W.zipf_counts(rng, 40, 36, 7000)]
+    live = [k for k in splits if k > 0]
+    assert max(live) * len(live) > 2 * sum(live), splits  # the kernel's skew condition
+    n, h = 512, 1024
+    assert len(splits) * (n // 256) * (h // 256) > 256
+    flush(f"mx4 wgrad skewed splits={splits}")
+    R = sum(splits) + 77
+    dy, x = _wgrad_case(R, n, h, splits, seed=13)
+    edges = [0, 127, 128, 255, 256, 383, 384, 511]
+    sel = np.union1d(edges, np.random.default_rng(14).choice(n, size=40, replace=False))
+    _check_wgrad(dy, x, splits, label="mx4 skewed", rows_sel=sel)
+
+
+def test_mx4_wgrad_and_fprop_max_groups():
+    """num_groups at the 1024 maximum on the fp4 path: empty, one-row and 128-row groups mixed,
+    garbage padding; wgrad store and accumulate, and the m-grouped forward."""
+    E = bs.MAX_GROUPS
+    rng = np.random.default_rng(1024)
+    splits = [int(v) for v in rng.choice([0, 1, 2, 31, 33, 64, 128, 129], size=E)]
+    n = h = 64
+    R = sum(splits) + 40
+    flush(f"mx4 max groups E={E} T={sum(splits)}")
+    dy, x = _wgrad_case(R, n, h, splits, seed=7)
+    _check_wgrad(dy, x, splits, label=f"mx4 E={E}")
+    mg = torch.randn(E, n, h, device=DEV, generator=torch.Generator(device=DEV).manual_seed(9))
+    _check_wgrad(dy, x, splits, accumulate=True, mg=mg, label=f"mx4 E={E} acc")
+    N = 64
+    w = W.randn_bf16((E * N, h), torch.Generator(device=DEV).manual_seed(8), DEV)
+    _check_fprop(x, w, splits, N, bs.OUT_F32, f"mx4 E={E} fprop")
+
+
 # ------------------------------------------------------------------------------------------
 # fprop and dgrad
 # ------------------------------------------------------------------------------------------
@@ -184,6 +221,11 @@ def test_mx4_fprop_parity(out_dtype, K, N, splits):
     g = torch.Generator(device=DEV).manual_seed(K + N)
     x = _garbage_pad(W.randn_bf16((R, K), g, DEV), T, K)
     w = W.randn_bf16((len(splits) * N, K), g, DEV)
+    _check_fprop(x, w, splits, N, out_dtype, f"mx4 fprop K={K} N={N}")
+
+
+def _check_fprop(x, w, splits, N, out_dtype, label):
+    R, K = x.shape
     st = W.splits_tensor(splits, DEV)
     xq = gpu_quantize(x, splits, MX4, bs.ROWWISE)
     wq = gpu_quantize(w, None, MX4, bs.ROWWISE)
@@ -197,7 +239,7 @@ def test_mx4_fprop_parity(out_dtype, K, N, splits):
     assert_quant_matches(wq, o_w, None, w.shape[0], bs.ROWWISE, "w")
     ref = oracle.grouped_fprop(o_x["row_q"], o_x["row_s"], o_w["row_q"], o_w["row_s"], N, splits,
                                recipe=oracle.RECIPE_MX4)
-    _check_rows(out.float().cpu().numpy().astype(np.float64), ref, splits, out_dtype, f"mx4 fprop K={K} N={N}")
+    _check_rows(out.float().cpu().numpy().astype(np.float64), ref, splits, out_dtype, label)
 
 
 @pytest.mark.parametrize("out_dtype", [bs.OUT_F32, bs.OUT_BF16])
