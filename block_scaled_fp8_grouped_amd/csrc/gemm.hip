@@ -368,8 +368,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
         const int v = wave * ((SA_INS + SB_INS) / NW) + u;
         const bool is_a = v < SA_INS;
         const int vv = is_a ? v : v - SA_INS;
-        const int per = (is_a ? BM : BN) / 256;
-        const int blk = vv / per, part = vv % per;
+        // the 256 bytes [vv * 256, +256) of the [blk][rows] block rows: 4 rows per lane (a
+        // 128-row tile: lanes 0-31 one block, lanes 32-63 the next)
+        const int rows = is_a ? BM : BN, flat = vv * 256 + 4 * lane;
+        const int blk = flat / rows, row = flat % rows;
         const int64_t kb = (int64_t)kk * SBLK + blk;
         if (MODE == kModeFprop && is_a) {
           // rows of a group start anywhere: single-byte loads per thread instead (above)
@@ -380,7 +382,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
           // word goes to a register: settle() decodes it from there after the step's wait, with
           // no LDS round trip between that wait and the barrier (1-1.5% on every widened GEMM
           // against landing the bytes in LDS by DMA and reading them back)
-          const int r4 = scale_dma_row(part, lane, is_a ? a_last : b_last);
+          const int r4 = scale_dma_row(0, row >> 2, is_a ? a_last : b_last);
           sc_w[u] = *(const uint32_t*)((is_a ? a_sc + a_row0 : b_sc + b_row0) + kb * (is_a ? a_sld : b_sld) + r4);
         }
       }
@@ -427,9 +429,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
         const bool is_a = v < SA_INS;
         if (MODE == kModeFprop && is_a) continue;
         const int vv = is_a ? v : v - SA_INS;
-        const int per = (is_a ? BM : BN) / 256;
-        const int blk = vv / per, part = vv % per;
-        const int idx = (is_a ? blk * BM : blk * BN) + part * 256 + 4 * lane;  // first of 4 rows
+        const int idx = vv * 256 + 4 * lane;  // first of the lane's 4 rows in [blk][rows]
         const uint32_t w4 = sc_w[u];
         float* f = (float*)(base + (is_a ? S::SAF_OFF : S::SBF_OFF)) + idx;
         *(v4f*)f = v4f{e8m0_value(w4 & 0xffu), e8m0_value((w4 >> 8) & 0xffu), e8m0_value((w4 >> 16) & 0xffu),
@@ -804,6 +804,10 @@ static int launch(const GemmArgs& a, dim3 grid, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? BSFP8_OK : BSFP8_ERR_LAUNCH;
 }
 
+// Weight-gradient launches with fewer 256 x 256 tiles than this (half the CUs) take 128 x 128
+// tiles on the widened MXFP8 path.
+constexpr int64_t kSmallWgradTiles = 128;
+
 int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, const uint8_t* x_q, const void* x_s,
                               int64_t h, const int32_t* splits, int E, int64_t R, int recipe, float* out,
                               int accumulate, uint32_t* status, hipStream_t stream) {
@@ -821,6 +825,21 @@ int launch_grouped_gemm_wgrad(const uint8_t* dy_q, const void* dy_s, int64_t n, 
   a.status = status;
   const bool f8 = (recipe & BSFP8_GEMM_FP8_MFMA) != 0;  // MXFP8 on the scaled fp8 MFMA
   recipe &= ~BSFP8_GEMM_FP8_MFMA;
+  if (recipe == BSFP8_RECIPE_MX_1X32_E8M0 && !f8 &&
+      (int64_t)E * ((n + 255) / 256) * ((h + 255) / 256) < kSmallWgradTiles) {
+    // A launch too small to give every CU a 256 x 256 tile (the single-group shape of TE #3484's
+    // reproducer has 16) takes 128 x 128 tiles of 4 waves instead: four times the workgroups,
+    // two per CU.  Every output sees the same MFMA chain (the same K steps, halves and
+    // instructions, at the same place in its 32 x 32 fragment), so the results are the 256 x 256
+    // kernel's bit for bit.
+    constexpr int BM = 128, BN = 128;
+    a.tiles_m = (int)((n + BM - 1) / BM);
+    a.tiles_n = (int)((h + BN - 1) / BN);
+    a.tiles = (int64_t)E * a.tiles_m * a.tiles_n;
+    dim3 grid((unsigned)xcd_launch_size(a.tiles));
+    return accumulate ? launch<kModeWgrad, false, kFmtBf16, BM, BN, 64, 64, true, 0>(a, grid, stream)
+                      : launch<kModeWgrad, false, kFmtBf16, BM, BN, 64, 64, false, 0>(a, grid, stream);
+  }
   if (recipe == BSFP8_RECIPE_MX_1X32_E8M0 || recipe == BSFP8_RECIPE_MXFP4_1X32_E8M0) {
     constexpr int BM = 256, BN = 256;
     a.tiles_m = (int)((n + BM - 1) / BM);

@@ -73,14 +73,17 @@ static void check_operand(const char* what, int BM, int NW, int64_t valid, int64
             if (g_fail++ < 10) std::printf("%s: row %d chunk %d delivered %d times\n", what, r, c, seen[(size_t)r * 8 + c]);
           }
     }
-    // E8M0 scale rows: 4 per lane, 256 per instruction
+    // E8M0 scale rows of the widened path: 4 per lane, the 256 bytes [256 v, +256) of the
+    // [block][BM rows] area per instruction v (a 128-row tile: two blocks per instruction); a
+    // valid row comes from its own place, a row past `last` from valid rows
     if (valid % 32 == 0) {
-      for (int part = 0; part < BM / 256 || part == 0; ++part) {
-        if (BM < 256) break;
+      for (int v = 0; v < 4 * BM / 256; ++v) {
         for (int lane = 0; lane < 64; ++lane) {
-          const int r4 = scale_dma_row(part, lane, last);
-          if (r4 < 0 || r4 % 4 != 0 || r4 + 3 > last) {
-            if (g_fail++ < 10) std::printf("%s: scale rows %d..%d past last %d\n", what, r4, r4 + 3, last);
+          const int flat = v * 256 + 4 * lane, row = flat % BM;
+          const int r4 = scale_dma_row(0, row >> 2, last);
+          ++g_checked;
+          if (r4 < 0 || r4 % 4 != 0 || r4 + 3 > last || (row <= last && r4 != row)) {
+            if (g_fail++ < 10) std::printf("%s: scale rows %d..%d for row %d (last %d)\n", what, r4, r4 + 3, row, last);
           }
         }
       }
@@ -112,6 +115,9 @@ int main() {
   const int64_t kps[] = {128, 256, 384, 8704, 19200};
   for (int64_t c : cols)
     for (int64_t kp : kps) check_operand("wgrad-mx", 256, 8, c, kp, kp);
+  // wgrad MX on a launch of few tiles: 128 x 128 tiles, 4 waves
+  for (int64_t c : cols)
+    for (int64_t kp : kps) check_operand("wgrad-mx128", 128, 4, c, kp, kp);
   // wgrad per-channel: 128 x 128 tiles, 4 waves
   for (int64_t c : cols)
     for (int64_t kp : kps) check_operand("wgrad-pc", 128, 4, c, kp, kp);
