@@ -4,7 +4,7 @@ traces the blow-ups to a race condition inside the GEMM kernel): the 2048 x 2048
 for each zero-channel scale in the page's sweep (1, 1e-4, 1e-8, 1e-30).  Every call must be
 bitwise equal to the first, and no call may show the page's blow-up criterion (an expert's
 output norm above max(100 x its unquantized reference norm, 1)).  The same stress runs on the
-pipelined block-scaled kernels, and the launches the benchmark times repeat bit for bit at the
+pipelined block-scaled kernels and on the 128 x 128 weight-gradient kernel of small launches, and the launches the benchmark times repeat bit for bit at the
 128-expert MoE size."""
 import numpy as np
 import pytest
@@ -111,6 +111,39 @@ def test_block_scaled_wgrad_10000_calls_bitwise(recipe, accumulate):
     # the zeroed channel gives an exact zero row (store) or leaves main_grad's row as it was
     for e in (1, 2):
         assert torch.equal(first[e, 0], mg0[e, 0] if accumulate else torch.zeros_like(first[e, 0]))
+
+
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_small_launch_wgrad_10000_calls_bitwise(accumulate):
+    # TE #3484's single-group shape (1024 x 1024 over 512 tokens, padded to 768 rows with 3.0):
+    # 16 tiles of 256 x 256, so the widened MXFP8 weight gradient takes its 128 x 128 kernel
+    # (4 waves, two workgroups per CU)
+    n = h = 1024
+    live, R = 512, 768
+    g = torch.Generator(device=DEV).manual_seed(1)
+    x = torch.full((R, h), 3.0, dtype=torch.bfloat16, device=DEV)
+    dy = torch.full((R, n), 3.0, dtype=torch.bfloat16, device=DEV)
+    x[:live] = W.randn_bf16((live, h), g, DEV)
+    dy[:live] = W.randn_bf16((live, n), g, DEV)
+    dy[:live, 0] = 0.0
+    splits = [live]
+    st = W.splits_tensor(splits, DEV)
+    dq = gpu_quantize(dy, splits, bs.RECIPE_MX, bs.COLWISE)
+    xq = gpu_quantize(x, splits, bs.RECIPE_MX, bs.COLWISE)
+    out = torch.empty(1, n, h, dtype=torch.float32, device=DEV)
+    mg0 = torch.randn(1, n, h, generator=torch.Generator(device=DEV).manual_seed(7), device=DEV)
+
+    def run():
+        if accumulate:
+            out.copy_(mg0)
+        else:
+            out.fill_(float("nan"))
+        bs.grouped_gemm_wgrad(dq, n, xq, h, st, R, bs.RECIPE_MX, out, accumulate=accumulate)
+
+    label = f"small-launch wgrad accumulate={accumulate}"
+    flush(label)
+    first = _stress(run, out, label)
+    assert torch.equal(first[0, 0], mg0[0, 0] if accumulate else torch.zeros_like(first[0, 0]))
 
 
 @pytest.mark.parametrize("recipe,out_dtype", [(bs.RECIPE_MX, bs.OUT_F32), (bs.RECIPE_MX, bs.OUT_BF16),
