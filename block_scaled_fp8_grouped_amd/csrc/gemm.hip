@@ -370,8 +370,18 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
         const int vv = is_a ? v : v - SA_INS;
         // the 256 bytes [vv * 256, +256) of the [blk][rows] block rows: 4 rows per lane (a
         // 128-row tile: lanes 0-31 one block, lanes 32-63 the next)
-        const int rows = is_a ? BM : BN, flat = vv * 256 + 4 * lane;
-        const int blk = flat / rows, row = flat % rows;
+        int blk, part, plane;  // scale rows part * 256 + 4 * plane ..
+        if constexpr (BM >= 256 && BN >= 256) {
+          const int per = (is_a ? BM : BN) / 256;
+          blk = vv / per;
+          part = vv % per;
+          plane = lane;
+        } else {
+          const int rows = is_a ? BM : BN, flat = vv * 256 + 4 * lane;
+          blk = flat / rows;
+          part = 0;
+          plane = (flat % rows) >> 2;
+        }
         const int64_t kb = (int64_t)kk * SBLK + blk;
         if (MODE == kModeFprop && is_a) {
           // rows of a group start anywhere: single-byte loads per thread instead (above)
@@ -382,7 +392,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
           // word goes to a register: settle() decodes it from there after the step's wait, with
           // no LDS round trip between that wait and the barrier (1-1.5% on every widened GEMM
           // against landing the bytes in LDS by DMA and reading them back)
-          const int r4 = scale_dma_row(0, row >> 2, is_a ? a_last : b_last);
+          const int r4 = scale_dma_row(part, plane, is_a ? a_last : b_last);
           sc_w[u] = *(const uint32_t*)((is_a ? a_sc + a_row0 : b_sc + b_row0) + kb * (is_a ? a_sld : b_sld) + r4);
         }
       }
@@ -429,7 +439,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void grouped_gemm_kerne
         const bool is_a = v < SA_INS;
         if (MODE == kModeFprop && is_a) continue;
         const int vv = is_a ? v : v - SA_INS;
-        const int idx = vv * 256 + 4 * lane;  // first of the lane's 4 rows in [blk][rows]
+        int idx;  // first of the lane's 4 rows in [blk][rows]
+        if constexpr (BM >= 256 && BN >= 256) {
+          const int per = (is_a ? BM : BN) / 256;
+          idx = (is_a ? (vv / per) * BM : (vv / per) * BN) + (vv % per) * 256 + 4 * lane;
+        } else {
+          idx = vv * 256 + 4 * lane;
+        }
         const uint32_t w4 = sc_w[u];
         float* f = (float*)(base + (is_a ? S::SAF_OFF : S::SBF_OFF)) + idx;
         *(v4f*)f = v4f{e8m0_value(w4 & 0xffu), e8m0_value((w4 >> 8) & 0xffu), e8m0_value((w4 >> 16) & 0xffu),
